@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""RelayAttention decode-attention benchmark on one MI355X.
+
+One step = one relay_attn_decode call (sys_attn + ctx_attn + relay_fuse) over one
+batch of the Llama2-7B-shaped decode-attention layer: batch 32, 32 MHA heads,
+head_dim 128, bf16 in / fp32 accumulation, system prompt 2048 tokens, per-request
+contexts uniform in [16, 512] (paged, block 16, shuffled block tables), synthetic
+seeded inputs.  Inputs are resident in HBM before timing starts.  Each real layer
+has its own KV cache, so the timed loop rotates over several copies of the inputs
+whose total exceeds the 256 MB Infinity Cache; a step therefore reads its K/V from
+HBM, not from the last-level cache.
+
+Prints one JSON line:
+  value          query-tokens/s/layer (T_q / step time)
+  roofline       dominant kernel: algorithmic bytes / HIP-event duration vs 8 TB/s
+  cpu_baseline   the fp64 oracle on the host cores over a bounded sample
+  sweep          query-tokens/s and HBM fraction vs system length (Llama-30B shape)
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+MALL_BYTES = 256 * 2**20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload config 1..5 (default 2)")
+    ap.add_argument("--sweep-index", type=int, default=0, help="config-3 system-length index")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="budget of the oracle sample in CPU-seconds (wall time x threads)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------------------
+# algorithmic work (what the method must move / compute, not implementation overhead)
+
+
+def work_of(w):
+    s = w.spec
+    E = 2 if s.dtype == "bf16" else 4
+    d, Hq, Hkv = s.head_dim, s.num_q_heads, s.num_kv_heads
+    Tq, B = w.total_q, s.batch
+    sum_ctx = int(w.ctx_lens.sum())
+    mb = w.max_blocks_per_seq
+    rows = Tq * Hq
+    kv_sys = 2 * Hkv * d * E * s.sys_len
+    kv_ctx = 2 * Hkv * d * E * sum_ctx
+    q_bytes = rows * d * E
+    part_row = rows * (d + 1) * 4          # one fp32 output row + LSE per query row
+    tables = 4 * B * (mb + 2) + (4 * (B + 1) if int(w.q_lens.max()) > 1 else 0)
+    vis = 0
+    for b in range(B):
+        n, c = int(w.q_lens[b]), int(w.ctx_lens[b])
+        vis += sum(c - n + t + 1 for t in range(n))
+    return {
+        "step_bytes": kv_sys + kv_ctx + rows * d * (E + 4) + tables,
+        "step_flops": 4 * Hq * d * (Tq * s.sys_len + vis),
+        "sys_attn": kv_sys + q_bytes + part_row,
+        "ctx_attn": kv_ctx + q_bytes + tables + part_row,
+        "relay_fuse": 2 * part_row + rows * d * 4,
+        "sys_flops": 4 * Hq * d * Tq * s.sys_len,
+        "ctx_flops": 4 * Hq * d * vis,
+    }
+
+
+# ---------------------------------------------------------------------------------------
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self, torch):
+        path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        self.hip = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def clone_set(torch, t):
+    return {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+
+
+def measure(torch, relay, w, steps, warmup, per_kernel=True):
+    """Times `steps` decode steps rotating over input copies; returns a dict."""
+    t0 = relay.to_device(w, "cuda")
+    work = work_of(w)
+    n_sets = max(2, math.ceil(3 * MALL_BYTES / max(work["step_bytes"], 1)))
+    n_sets = min(n_sets, 16)
+    sets = [t0] + [clone_set(torch, t0) for _ in range(n_sets - 1)]
+    dims = relay.dims_of(t0)
+    ws = relay.workspace(dims, t0["sys_len"], "cuda")
+    outs = [torch.empty(t0["q"].shape, dtype=torch.float32, device="cuda") for _ in range(n_sets)]
+    for i in range(warmup):
+        relay.decode_workload(sets[i % n_sets], workspace_buf=ws, out=outs[i % n_sets])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        relay.decode_workload(sets[i % n_sets], workspace_buf=ws, out=outs[i % n_sets])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    res = {"ms_per_step": ms, "n_sets": n_sets, "work": work, "plan": relay.relay_get_plan(dims, t0["sys_len"])}
+    if per_kernel:
+        he = HipEvents(torch)
+        evs = he.create(4 * steps)
+        for i in range(steps):
+            relay.relay_attn_decode_timed(sets[i % n_sets], outs[i % n_sets], ws, evs[4 * i:4 * i + 4])
+        torch.cuda.synchronize()
+        acc = {"sys_attn": 0.0, "ctx_attn": 0.0, "relay_fuse": 0.0}
+        for i in range(steps):
+            e = evs[4 * i:4 * i + 4]
+            acc["sys_attn"] += he.elapsed_ms(e[0], e[1])
+            acc["ctx_attn"] += he.elapsed_ms(e[1], e[2])
+            acc["relay_fuse"] += he.elapsed_ms(e[2], e[3])
+        he.destroy(evs)
+        res["kernel_us"] = {k: 1000.0 * v / steps for k, v in acc.items()}
+    del sets, outs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, budget_cpu_s):
+    """The oracle (unchanged) on the host cores, request by request through the
+    workload (cycling), until about budget_cpu_s CPU-seconds have been spent."""
+    import oracle
+    import numpy as np
+
+    P = oracle.Problem(w)
+    Hq = w.spec.num_q_heads
+    cores = oracle.num_threads()
+    budget_wall = budget_cpu_s / max(cores, 1)
+    tokens, elapsed, n = 0, 0.0, 0
+    start = time.perf_counter()
+    while elapsed < budget_wall:
+        b = n % w.spec.batch
+        lo, hi = int(w.cu_q_lens[b]), int(w.cu_q_lens[b + 1])
+        P.attention(np.arange(lo * Hq, hi * Hq, dtype=np.int64))
+        tokens += hi - lo
+        n += 1
+        elapsed = time.perf_counter() - start
+    return {"value": round(tokens / elapsed, 3), "unit": "query-tokens/s/layer", "cores": cores,
+            "kind": "oracle",
+            "sample": f"exact fp64 causal attention (all {Hq} heads) for {n} requests taken in order, "
+                      f"cycling over the {w.spec.batch} requests of the same workload: {tokens} query "
+                      f"tokens in {elapsed:.2f} s wall on {cores} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              "(the decode-attention path runs on a single MI355X; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from shared_prompt_kv_amd import relay, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    relay.load_library()
+    spec = workloads.config_spec(args.config, args.sweep_index)
+    w = workloads.generate(spec)
+    r = measure(torch, relay, w, args.steps, args.warmup)
+    work = r["work"]
+    ms = r["ms_per_step"]
+    value = w.total_q / (ms * 1e-3)
+    kus = r["kernel_us"]
+    dom = max(kus, key=kus.get)
+    achieved = work[dom] / (kus[dom] * 1e-6) / 1e9
+    step_hbm_frac = work["step_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)
+    peak_flops = (BF16_PEAK_TFLOPS if spec.dtype == "bf16" else FP32_PEAK_TFLOPS) * 1e12
+    step_mfma_frac = work["step_flops"] / (ms * 1e-3) / peak_flops
+    line = {
+        "metric": "decode-attn query-tokens/s/layer + % HBM roofline vs system-prompt length",
+        "value": round(value, 1),
+        "unit": "query-tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": spec.batch, "num_q_heads": spec.num_q_heads,
+                   "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
+                   "sys_len": spec.sys_len, "total_q": w.total_q, "sum_ctx_len": int(w.ctx_lens.sum()),
+                   "ctx_len_range": [int(w.ctx_lens.min()), int(w.ctx_lens.max())],
+                   "parallelism": "single-gpu", "input_copies_rotated": r["n_sets"]},
+        "step_hbm_roofline_frac": round(step_hbm_frac, 4),
+        "step_mfma_roofline_frac": round(step_mfma_frac, 5),
+        "step_bytes_alg": work["step_bytes"],
+        "kernel_us": {k: round(v, 3) for k, v in kus.items()},
+        "plan": r["plan"],
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "bytes_alg_per_launch": work[dom], "traffic": None},
+    }
+    if not args.no_sweep and args.config == 2:
+        sweep = []
+        for i, Ls in enumerate(workloads.CONFIG3_SYS_LENS):
+            ws_ = workloads.generate(workloads.config_spec(3, i))
+            rr = measure(torch, relay, ws_, min(args.steps, 50), min(args.warmup, 10), per_kernel=True)
+            m = rr["ms_per_step"]
+            sweep.append({"sys_len": Ls, "qtok_s": round(ws_.total_q / (m * 1e-3), 1),
+                          "us_per_step": round(1000 * m, 2),
+                          "hbm_frac": round(rr["work"]["step_bytes"] / (m * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                          "kernel_us": {k: round(v, 2) for k, v in rr["kernel_us"].items()}})
+            del ws_
+        line["sweep"] = {"workload": "llama30b_mha (batch 32, 52 heads, ctx 128)", "points": sweep}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

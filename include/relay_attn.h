@@ -1,0 +1,223 @@
+/*
+ * relay_attn.h - C ABI of librelay_attn.so: RelayAttention decode-time attention
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * RelayAttention (RelayAttention paper, abstract; atyun.com article, section
+ * "RelayAttention"; linnk.ai summary, section "Abstract") computes causal decode
+ * attention over a long system prompt shared by every request plus each request's
+ * own context in three steps:
+ *
+ *   1. system attention  - every query row of the batch attends to the shared
+ *      system KV cache alone; the cache is read from HBM once for the whole batch
+ *      by stacking all query rows into one matrix-matrix product;
+ *   2. context attention - each request attends to its own paged context KV alone;
+ *   3. relay fusion      - the final output is a convex combination of the two
+ *      intermediate outputs.  The pages name only "convex combination"; the weights
+ *      here are alpha_sys = e^LSE_sys / (e^LSE_sys + e^LSE_ctx), alpha_ctx =
+ *      1 - alpha_sys, the only convex weights for which the result equals exact
+ *      causal attention over [system; context].
+ *
+ * The system KV cache is separate from the context cache and filled before
+ * serving; context positions follow the system prompt (atyun.com article, section
+ * "RelayAttention").  The kernels take post-RoPE Q and K, so absolute positions
+ * never enter; only the causal index inside the context does.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ * ---------------------------------------------------------------------------
+ *  - All array arguments are DEVICE pointers (HIP device memory of the current
+ *    device) unless marked "host".  Arrays are dense, row-major, with no padding
+ *    beyond what the layouts below state.  Every pointer must be 16-byte aligned.
+ *  - The caller owns every buffer.  The library allocates no device memory, keeps
+ *    no pointer after a call returns, never synchronises the device and enqueues
+ *    work only on `stream` (a hipStream_t; NULL = the legacy default stream).
+ *    Results are valid once the stream's work has completed.
+ *  - Return value: RELAY_OK (0) or a negative RELAY_ERR_* code.  Argument errors
+ *    are detected on the host before anything is enqueued.  relay_last_error()
+ *    returns a thread-local message describing the most recent failure.
+ *  - Data-dependent preconditions (block ids in range, 1 <= n_b <= c_b <= the
+ *    stated maxima) are the caller's; relay_validate() checks them on host copies.
+ *    Kernels clamp indices so that violating them cannot read or write out of
+ *    bounds, but the numbers are then unspecified.
+ *  - Thread safety: no global mutable state; concurrent calls on different
+ *    streams with disjoint outputs and workspaces are safe.
+ *
+ * Notation: B requests; request b has n_b new query tokens (T_q = sum n_b) and a
+ * context of c_b tokens that INCLUDES its n_b new tokens (their K/V are already in
+ * the pages).  Query token t of request b (0 <= t < n_b) sits at context position
+ * p = c_b - n_b + t and sees context keys 0..p and all system keys.  H_q query
+ * heads, H_kv KV heads, g = H_q / H_kv; query head h uses KV head h / g.  d is the
+ * head dimension, E the element size of in_dtype, L_s the system length.
+ *
+ * Layouts (E-byte elements unless stated):
+ *   q            [T_q, H_q, d]               tokens of request b are rows
+ *                                            cu_q_lens[b] .. cu_q_lens[b+1]-1
+ *   sys_k        [H_kv, L_s, d]              system keys, key-major
+ *   sys_v        [H_kv, ceil(L_s/16), d, 16] system values in 16-key tiles,
+ *                                            dimension-major inside a tile (the
+ *                                            tail tile's padding is ignored)
+ *   ctx_k_pages  [num_blocks, H_kv, 16, d]   paged context keys, 16 tokens a page
+ *   ctx_v_pages  [num_blocks, H_kv, d, 16]   paged context values, dimension-major
+ *                                            inside a page
+ *   block_tables int32 [B, max_blocks_per_seq]  context token j of request b is in
+ *                                            page block_tables[b][j/16], slot j%16;
+ *                                            entries past ceil(c_b/16) are unused
+ *   ctx_lens     int32 [B]                   c_b
+ *   cu_q_lens    int32 [B+1] prefix sums of n_b (cu_q_lens[0] = 0), or NULL when
+ *                every request has exactly one query token (then T_q = B)
+ *   out          [T_q, H_q, d] of out_dtype
+ *   LSE arrays   float32 [T_q, H_q], natural log of sum_j exp(scale * q.k_j);
+ *                -inf marks an empty key set
+ *   O partials   float32 [T_q, H_q, d]
+ * Values are stored dimension-major (d before the 16 keys of a tile/page) so that
+ * the keys a matrix-core lane reduces over are contiguous in memory.
+ */
+#ifndef RELAY_ATTN_H
+#define RELAY_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RELAY_ATTN_ABI_VERSION 1
+
+/* element types */
+#define RELAY_F32 0  /* IEEE float32 */
+#define RELAY_BF16 1 /* bfloat16 (bit pattern, round-to-nearest-even producers) */
+
+/* return codes */
+#define RELAY_OK 0
+#define RELAY_ERR_INVALID (-1)     /* bad argument: NULL pointer, bad size, misaligned */
+#define RELAY_ERR_UNSUPPORTED (-2) /* valid but unsupported: head_dim, block size, dtype */
+#define RELAY_ERR_WORKSPACE (-3)   /* workspace smaller than relay_workspace_size() */
+#define RELAY_ERR_HIP (-4)         /* a HIP launch failed; see relay_last_error() */
+#define RELAY_ERR_DATA (-5)        /* relay_validate(): inconsistent host data */
+
+/* Problem dimensions, passed by host pointer. */
+typedef struct {
+  int32_t batch;              /* B >= 1 */
+  int32_t num_q_heads;        /* H_q, a multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* H_kv >= 1 */
+  int32_t head_dim;           /* d: 64 or 128 */
+  int32_t block_size;         /* context page size in tokens: must be 16 */
+  int32_t max_blocks_per_seq; /* columns of block_tables */
+  int32_t num_blocks;         /* pages in the context pool */
+  int32_t total_q;            /* T_q = cu_q_lens[B] (== B when cu_q_lens is NULL) */
+  int32_t max_q_len;          /* upper bound on n_b (1 when cu_q_lens is NULL) */
+  int32_t max_ctx_len;        /* upper bound on c_b; sizes the split plan on the host */
+  float scale;                /* softmax scale, e.g. 1/sqrt(d) */
+  int32_t in_dtype;           /* RELAY_F32 or RELAY_BF16: q, K and V */
+  int32_t out_dtype;          /* RELAY_F32 or RELAY_BF16: out of relay_attn_decode */
+} relay_dims;
+
+/* How a call is split into work units (for benchmarks and tests). */
+typedef struct {
+  int32_t sys_chunks;      /* system keys are processed in this many chunks */
+  int32_t sys_chunk_len;   /* keys per chunk (a multiple of 32) */
+  int32_t sys_row_blocks;  /* query-row blocks per KV head in the system step */
+  int32_t sys_wgs;         /* workgroups of one system-attention launch */
+  int32_t ctx_split_len;   /* context keys per split (a multiple of 32) */
+  int32_t ctx_max_splits;  /* ceil(max_ctx_len / ctx_split_len) */
+  int32_t ctx_row_blocks;  /* query-row blocks per (request, KV head) */
+  int32_t ctx_wgs;         /* workgroups of one context-attention launch (upper bound) */
+  int32_t fuse_wgs;        /* workgroups of one fusion launch */
+} relay_plan;
+
+/* ABI version compiled into the library (RELAY_ATTN_ABI_VERSION). */
+int relay_abi_version(void);
+
+/* Static string for a return code. */
+const char* relay_strerror(int code);
+
+/* Thread-local description of the most recent failure of this thread ("" if none). */
+const char* relay_last_error(void);
+
+/*
+ * Bytes of device workspace that relay_attn_decode, relay_sys_attn and
+ * relay_ctx_attn need for these dimensions and system length (the partial
+ * outputs and log-sum-exps of system chunks and context splits).  Returns 0 on
+ * invalid dims (see relay_last_error()).
+ */
+size_t relay_workspace_size(const relay_dims* dims, int32_t sys_len);
+
+/* Fills *plan with the work split for these dims; RELAY_OK or an error code. */
+int relay_get_plan(const relay_dims* dims, int32_t sys_len, relay_plan* plan);
+
+/*
+ * The whole RelayAttention decode step: system attention (skipped when
+ * sys_len == 0), context attention and relay fusion, written to out.
+ * Equals exact causal attention of each query row over its visible
+ * [system; context] keys.  Three kernels are enqueued on `stream`:
+ * sys_attn, ctx_attn and relay_fuse.  workspace must hold
+ * relay_workspace_size(dims, sys_len) bytes (256-byte aligned); its contents on
+ * entry are irrelevant and on return unspecified.
+ */
+int relay_attn_decode(const relay_dims* dims, const void* q, const void* sys_k,
+                      const void* sys_v, int32_t sys_len, const void* ctx_k_pages,
+                      const void* ctx_v_pages, const int32_t* block_tables,
+                      const int32_t* ctx_lens, const int32_t* cu_q_lens, void* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * relay_attn_decode with per-kernel timing: identical work, plus events[0..3]
+ * (hipEvent_t handles created by the caller; any entry may be NULL) recorded on
+ * `stream` before sys_attn, before ctx_attn, before relay_fuse and after
+ * relay_fuse.  For benchmarks; events must not be NULL.
+ */
+int relay_attn_decode_timed(const relay_dims* dims, const void* q, const void* sys_k,
+                            const void* sys_v, int32_t sys_len, const void* ctx_k_pages,
+                            const void* ctx_v_pages, const int32_t* block_tables,
+                            const int32_t* ctx_lens, const int32_t* cu_q_lens, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events);
+
+/*
+ * System-attention step alone (RelayAttention's first step): for every query row,
+ * attention over the system keys only.  o_sys: float32 [T_q, H_q, d]; lse_sys:
+ * float32 [T_q, H_q].  sys_len == 0 gives o_sys = 0 and lse_sys = -inf.  Enqueues
+ * sys_attn and a relay_fuse that merges the chunk partials.
+ */
+int relay_sys_attn(const relay_dims* dims, const void* q, const void* sys_k, const void* sys_v,
+                   int32_t sys_len, float* o_sys, float* lse_sys, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * Context-attention step alone (RelayAttention's second step): for every query
+ * row, causal attention over its request's visible context keys only.
+ * o_ctx / lse_ctx as for relay_sys_attn.  Enqueues ctx_attn and a relay_fuse
+ * that merges the split partials.
+ */
+int relay_ctx_attn(const relay_dims* dims, const void* q, const void* ctx_k_pages,
+                   const void* ctx_v_pages, const int32_t* block_tables,
+                   const int32_t* ctx_lens, const int32_t* cu_q_lens, float* o_ctx,
+                   float* lse_ctx, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Relay fusion alone (RelayAttention's third step) over n_rows rows of head_dim
+ * values: out = alpha_sys * o_sys + alpha_ctx * o_ctx with the LSE weights above.
+ * o_*: float32 [n_rows, head_dim]; lse_*: float32 [n_rows]; a part with LSE = -inf
+ * has weight 0.  out: [n_rows, head_dim] of out_dtype.  lse_out (may be NULL):
+ * float32 [n_rows], ln(e^lse_sys + e^lse_ctx).  head_dim: 64 or 128.
+ */
+int relay_fuse(int64_t n_rows, int32_t head_dim, const float* o_sys, const float* lse_sys,
+               const float* o_ctx, const float* lse_ctx, void* out, int32_t out_dtype,
+               float* lse_out, void* stream);
+
+/*
+ * Host-side check of the data-dependent preconditions on HOST copies of the
+ * integer arrays: 1 <= n_b <= c_b <= max_ctx_len, n_b <= max_q_len,
+ * ceil(c_b/16) <= max_blocks_per_seq, used block ids in [0, num_blocks), and
+ * cu_q_lens consistent with total_q.  h_cu_q_lens may be NULL (n_b = 1).
+ * RELAY_OK or RELAY_ERR_DATA / RELAY_ERR_INVALID; enqueues nothing.
+ */
+int relay_validate(const relay_dims* dims, const int32_t* h_block_tables,
+                   const int32_t* h_ctx_lens, const int32_t* h_cu_q_lens, int32_t sys_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RELAY_ATTN_H */

@@ -1,0 +1,448 @@
+// C-ABI host layer of librelay_attn.so: argument checks, the work plan, workspace
+// carving and the kernel launches.  Declarations and the contract of every entry
+// point are in include/relay_attn.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/relay_attn.h"
+#include "relay_internal.hpp"
+
+namespace {
+
+using relay::CtxArgs;
+using relay::CtxConfig;
+using relay::FuseArgs;
+using relay::SysArgs;
+using relay::SysConfig;
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+constexpr int kNumCUs = 256;  // MI355X
+constexpr float kLog2e = 1.4426950408889634f;
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  char* end = nullptr;
+  long x = strtol(v, &end, 10);
+  return (end && *end == 0 && x > 0 && x < (1L << 30)) ? (int)x : dflt;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+int round_up32(long long x) { return (int)(((x + 31) / 32) * 32); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Plan {
+  SysConfig sc;
+  int sys_chunks = 0, sys_chunk_len = 0, sys_row_blocks = 0, sys_wgs = 0, xcd_remap = 0;
+  CtxConfig cc;
+  int ctx_split_len = 0, ctx_max_splits = 0, ctx_row_blocks = 0, ctx_wgs = 0;
+  int fuse_wgs = 0;
+  size_t off_sys_o = 0, off_sys_lse = 0, off_ctx_o = 0, off_ctx_lse = 0, ws_bytes = 0;
+};
+
+int check_dims(const relay_dims* d, int32_t sys_len) {
+  if (!d) return fail(RELAY_ERR_INVALID, "dims is NULL");
+  if (d->batch < 1) return fail(RELAY_ERR_INVALID, "batch must be >= 1 (got %d)", d->batch);
+  if (d->num_kv_heads < 1 || d->num_q_heads < 1 || d->num_q_heads % d->num_kv_heads)
+    return fail(RELAY_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(RELAY_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", d->head_dim);
+  if (d->block_size != 16)
+    return fail(RELAY_ERR_UNSUPPORTED, "block_size %d unsupported (16)", d->block_size);
+  if ((d->in_dtype != RELAY_F32 && d->in_dtype != RELAY_BF16) ||
+      (d->out_dtype != RELAY_F32 && d->out_dtype != RELAY_BF16))
+    return fail(RELAY_ERR_UNSUPPORTED, "dtype unsupported (in %d, out %d)", d->in_dtype, d->out_dtype);
+  if (d->total_q < 1 || d->max_q_len < 1 || d->max_q_len > d->total_q)
+    return fail(RELAY_ERR_INVALID, "total_q (%d) and max_q_len (%d) must satisfy 1 <= max_q_len <= total_q",
+                d->total_q, d->max_q_len);
+  if (d->max_ctx_len < 1 || d->max_ctx_len < d->max_q_len)
+    return fail(RELAY_ERR_INVALID, "max_ctx_len (%d) must be >= max(1, max_q_len)", d->max_ctx_len);
+  if (d->max_blocks_per_seq < ceil_div(d->max_ctx_len, 16))
+    return fail(RELAY_ERR_INVALID, "max_blocks_per_seq (%d) < ceil(max_ctx_len/16) (%d)",
+                d->max_blocks_per_seq, ceil_div(d->max_ctx_len, 16));
+  if (d->num_blocks < 1) return fail(RELAY_ERR_INVALID, "num_blocks must be >= 1");
+  if (!(isfinite(d->scale))) return fail(RELAY_ERR_INVALID, "scale must be finite");
+  if (sys_len < 0) return fail(RELAY_ERR_INVALID, "sys_len must be >= 0 (got %d)", sys_len);
+  const long long rows = (long long)d->total_q * d->num_q_heads;
+  if (rows * d->head_dim > (1LL << 40) || (long long)d->total_q * (d->num_q_heads / d->num_kv_heads) > (1 << 30))
+    return fail(RELAY_ERR_INVALID, "problem too large");
+  return RELAY_OK;
+}
+
+void make_plan(const relay_dims* d, int32_t sys_len, Plan* p) {
+  const int g = d->num_q_heads / d->num_kv_heads;
+  const long long rows = (long long)d->total_q * d->num_q_heads;
+  // ---- system step
+  const int M = d->total_q * g;
+  p->sc = relay::sys_config(M);
+  const int rows_per_wg = p->sc.wr * p->sc.rt * 16;
+  p->sys_row_blocks = ceil_div(M, rows_per_wg);
+  if (sys_len > 0) {
+    const int target = env_int("RELAY_SYS_TARGET_WGS", 2 * kNumCUs);
+    int chunk = env_int("RELAY_SYS_CHUNK", 0);
+    if (chunk <= 0) {
+      const long long per = (long long)sys_len * d->num_kv_heads * p->sys_row_blocks / target;
+      chunk = round_up32(per < 1 ? 1 : per);
+      const int min_chunk = 32 * p->sc.wk;
+      if (chunk < min_chunk) chunk = min_chunk;
+    }
+    chunk = round_up32(chunk);
+    p->sys_chunk_len = chunk;
+    p->sys_chunks = ceil_div(sys_len, chunk);
+    p->sys_wgs = p->sys_row_blocks * p->sys_chunks * d->num_kv_heads;
+    p->xcd_remap = (p->sys_row_blocks > 1 && p->sys_wgs % 8 == 0) ? 1 : 0;
+  }
+  // ---- context step
+  const int R = d->max_q_len * g;
+  p->cc = relay::ctx_config(R);
+  p->ctx_row_blocks = ceil_div(R, p->cc.wr * p->cc.rt * 16);
+  int split = env_int("RELAY_CTX_SPLIT", 0);
+  if (split <= 0) split = (R <= 16) ? 128 : 512;
+  split = round_up32(split);
+  p->ctx_split_len = split;
+  p->ctx_max_splits = ceil_div(d->max_ctx_len, split);
+  p->ctx_wgs = p->ctx_row_blocks * p->ctx_max_splits * d->num_kv_heads * d->batch;
+  // ---- fusion
+  p->fuse_wgs = ceil_div(rows, 1024 / d->head_dim);
+  // ---- workspace
+  size_t off = 0;
+  p->off_sys_o = off;
+  off += align256((size_t)p->sys_chunks * rows * d->head_dim * sizeof(float));
+  p->off_sys_lse = off;
+  off += align256((size_t)p->sys_chunks * rows * sizeof(float));
+  p->off_ctx_o = off;
+  off += align256((size_t)p->ctx_max_splits * rows * d->head_dim * sizeof(float));
+  p->off_ctx_lse = off;
+  off += align256((size_t)p->ctx_max_splits * rows * sizeof(float));
+  p->ws_bytes = off;
+}
+
+int grid_ok(long long n) { return n > 0 && n < (1LL << 31); }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(RELAY_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int launch_sys(const relay_dims* d, const Plan& p, const void* q, const void* sys_k,
+               const void* sys_v, int32_t sys_len, char* ws, hipStream_t s) {
+  if (!grid_ok(p.sys_wgs)) return fail(RELAY_ERR_INVALID, "system grid too large");
+  SysArgs a;
+  a.q = q;
+  a.sys_k = sys_k;
+  a.sys_v = sys_v;
+  a.o_part = reinterpret_cast<float*>(ws + p.off_sys_o);
+  a.lse_part = reinterpret_cast<float*>(ws + p.off_sys_lse);
+  a.sys_len = sys_len;
+  a.total_q = d->total_q;
+  a.num_q_heads = d->num_q_heads;
+  a.group = d->num_q_heads / d->num_kv_heads;
+  a.chunk_len = p.sys_chunk_len;
+  a.n_chunks = p.sys_chunks;
+  a.row_blocks = p.sys_row_blocks;
+  a.xcd_remap = p.xcd_remap;
+  a.scale_log2 = d->scale * kLog2e;
+  hipError_t e = relay::launch_sys_attn(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s);
+  return e == hipSuccess ? RELAY_OK : hip_fail(e, "sys_attn launch");
+}
+
+int launch_ctx(const relay_dims* d, const Plan& p, const void* q, const void* ck, const void* cv,
+               const int32_t* bt, const int32_t* cl, const int32_t* cu, char* ws, hipStream_t s) {
+  if (!grid_ok(p.ctx_wgs)) return fail(RELAY_ERR_INVALID, "context grid too large");
+  CtxArgs a;
+  a.q = q;
+  a.ctx_k = ck;
+  a.ctx_v = cv;
+  a.block_tables = bt;
+  a.ctx_lens = cl;
+  a.cu_q_lens = cu;
+  a.o_part = reinterpret_cast<float*>(ws + p.off_ctx_o);
+  a.lse_part = reinterpret_cast<float*>(ws + p.off_ctx_lse);
+  a.batch = d->batch;
+  a.total_q = d->total_q;
+  a.num_q_heads = d->num_q_heads;
+  a.num_kv_heads = d->num_kv_heads;
+  a.group = d->num_q_heads / d->num_kv_heads;
+  a.num_blocks = d->num_blocks;
+  a.max_blocks_per_seq = d->max_blocks_per_seq;
+  a.max_ctx_len = d->max_ctx_len;
+  a.split_len = p.ctx_split_len;
+  a.max_splits = p.ctx_max_splits;
+  a.row_blocks = p.ctx_row_blocks;
+  a.scale_log2 = d->scale * kLog2e;
+  hipError_t e = relay::launch_ctx_attn(a, p.cc, d->in_dtype, d->head_dim, p.ctx_wgs, s);
+  return e == hipSuccess ? RELAY_OK : hip_fail(e, "ctx_attn launch");
+}
+
+int launch_fuse(FuseArgs& a, int head_dim, hipStream_t s) {
+  const long long nwg = (a.n_rows + (1024 / head_dim) - 1) / (1024 / head_dim);
+  if (!grid_ok(nwg)) return fail(RELAY_ERR_INVALID, "fusion grid too large");
+  hipError_t e = relay::launch_relay_fuse(a, head_dim, (int)nwg, s);
+  return e == hipSuccess ? RELAY_OK : hip_fail(e, "relay_fuse launch");
+}
+
+int check_ws(const Plan& p, void* ws, size_t bytes) {
+  if (p.ws_bytes == 0) return RELAY_OK;
+  if (!ws) return fail(RELAY_ERR_INVALID, "workspace is NULL");
+  if (((uintptr_t)ws & 255u) != 0) return fail(RELAY_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (bytes < p.ws_bytes)
+    return fail(RELAY_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", bytes, p.ws_bytes);
+  return RELAY_OK;
+}
+
+// Records events[i] (a hipEvent_t, may be NULL) on the stream; no-op without events.
+int record(void* const* events, int i, hipStream_t s) {
+  if (!events || !events[i]) return RELAY_OK;
+  hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+  return e == hipSuccess ? RELAY_OK : hip_fail(e, "hipEventRecord");
+}
+
+int check_q_layout(const relay_dims* d, const int32_t* cu) {
+  if (!cu && (d->total_q != d->batch || d->max_q_len != 1))
+    return fail(RELAY_ERR_INVALID, "cu_q_lens is NULL: total_q must equal batch and max_q_len must be 1");
+  return RELAY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int relay_abi_version(void) { return RELAY_ATTN_ABI_VERSION; }
+
+const char* relay_strerror(int code) {
+  switch (code) {
+    case RELAY_OK: return "ok";
+    case RELAY_ERR_INVALID: return "invalid argument";
+    case RELAY_ERR_UNSUPPORTED: return "unsupported configuration";
+    case RELAY_ERR_WORKSPACE: return "workspace too small";
+    case RELAY_ERR_HIP: return "HIP error";
+    case RELAY_ERR_DATA: return "inconsistent data";
+    default: return "unknown error";
+  }
+}
+
+const char* relay_last_error(void) { return g_err; }
+
+size_t relay_workspace_size(const relay_dims* dims, int32_t sys_len) {
+  if (check_dims(dims, sys_len) != RELAY_OK) return 0;
+  Plan p;
+  make_plan(dims, sys_len, &p);
+  return p.ws_bytes;
+}
+
+int relay_get_plan(const relay_dims* dims, int32_t sys_len, relay_plan* out) {
+  int rc = check_dims(dims, sys_len);
+  if (rc != RELAY_OK) return rc;
+  if (!out) return fail(RELAY_ERR_INVALID, "plan is NULL");
+  Plan p;
+  make_plan(dims, sys_len, &p);
+  out->sys_chunks = p.sys_chunks;
+  out->sys_chunk_len = p.sys_chunk_len;
+  out->sys_row_blocks = p.sys_row_blocks;
+  out->sys_wgs = p.sys_wgs;
+  out->ctx_split_len = p.ctx_split_len;
+  out->ctx_max_splits = p.ctx_max_splits;
+  out->ctx_row_blocks = p.ctx_row_blocks;
+  out->ctx_wgs = p.ctx_wgs;
+  out->fuse_wgs = p.fuse_wgs;
+  return RELAY_OK;
+}
+
+static int decode_impl(const relay_dims* dims, const void* q, const void* sys_k, const void* sys_v,
+                       int32_t sys_len, const void* ctx_k_pages, const void* ctx_v_pages,
+                       const int32_t* block_tables, const int32_t* ctx_lens,
+                       const int32_t* cu_q_lens, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream, void* const* events) {
+  int rc = check_dims(dims, sys_len);
+  if (rc != RELAY_OK) return rc;
+  if ((rc = check_q_layout(dims, cu_q_lens)) != RELAY_OK) return rc;
+  if (!q || !ctx_k_pages || !ctx_v_pages || !block_tables || !ctx_lens || !out)
+    return fail(RELAY_ERR_INVALID, "NULL array argument");
+  if (sys_len > 0 && (!sys_k || !sys_v)) return fail(RELAY_ERR_INVALID, "sys_k/sys_v NULL with sys_len > 0");
+  if (!aligned16(q) || !aligned16(sys_k) || !aligned16(sys_v) || !aligned16(ctx_k_pages) ||
+      !aligned16(ctx_v_pages) || !aligned16(out))
+    return fail(RELAY_ERR_INVALID, "arrays must be 16-byte aligned");
+  Plan p;
+  make_plan(dims, sys_len, &p);
+  if ((rc = check_ws(p, workspace, workspace_bytes)) != RELAY_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if ((rc = record(events, 0, s)) != RELAY_OK) return rc;
+  if (sys_len > 0 && (rc = launch_sys(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
+  if ((rc = record(events, 1, s)) != RELAY_OK) return rc;
+  if ((rc = launch_ctx(dims, p, q, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens, ws, s)) != RELAY_OK)
+    return rc;
+  if ((rc = record(events, 2, s)) != RELAY_OK) return rc;
+  FuseArgs f{};
+  f.a_o = reinterpret_cast<const float*>(ws + p.off_sys_o);
+  f.a_lse = reinterpret_cast<const float*>(ws + p.off_sys_lse);
+  f.a_count = sys_len > 0 ? p.sys_chunks : 0;
+  f.b_o = reinterpret_cast<const float*>(ws + p.off_ctx_o);
+  f.b_lse = reinterpret_cast<const float*>(ws + p.off_ctx_lse);
+  f.b_count = p.ctx_max_splits;
+  f.b_split_len = p.ctx_split_len;
+  f.ctx_lens = ctx_lens;
+  f.cu_q_lens = cu_q_lens;
+  f.out = out;
+  f.lse_out = nullptr;
+  f.n_rows = (long long)dims->total_q * dims->num_q_heads;
+  f.num_q_heads = dims->num_q_heads;
+  f.batch = dims->batch;
+  f.out_bf16 = dims->out_dtype == RELAY_BF16;
+  if ((rc = launch_fuse(f, dims->head_dim, s)) != RELAY_OK) return rc;
+  return record(events, 3, s);
+}
+
+int relay_attn_decode(const relay_dims* dims, const void* q, const void* sys_k, const void* sys_v,
+                      int32_t sys_len, const void* ctx_k_pages, const void* ctx_v_pages,
+                      const int32_t* block_tables, const int32_t* ctx_lens,
+                      const int32_t* cu_q_lens, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return decode_impl(dims, q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens,
+                     cu_q_lens, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int relay_attn_decode_timed(const relay_dims* dims, const void* q, const void* sys_k,
+                            const void* sys_v, int32_t sys_len, const void* ctx_k_pages,
+                            const void* ctx_v_pages, const int32_t* block_tables,
+                            const int32_t* ctx_lens, const int32_t* cu_q_lens, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events) {
+  if (!events) return fail(RELAY_ERR_INVALID, "events is NULL");
+  return decode_impl(dims, q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens,
+                     cu_q_lens, out, workspace, workspace_bytes, stream, events);
+}
+
+
+
+int relay_sys_attn(const relay_dims* dims, const void* q, const void* sys_k, const void* sys_v,
+                   int32_t sys_len, float* o_sys, float* lse_sys, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims, sys_len);
+  if (rc != RELAY_OK) return rc;
+  if (!q || !o_sys || !lse_sys) return fail(RELAY_ERR_INVALID, "NULL array argument");
+  if (sys_len > 0 && (!sys_k || !sys_v)) return fail(RELAY_ERR_INVALID, "sys_k/sys_v NULL with sys_len > 0");
+  if (!aligned16(q) || !aligned16(sys_k) || !aligned16(sys_v) || !aligned16(o_sys))
+    return fail(RELAY_ERR_INVALID, "arrays must be 16-byte aligned");
+  Plan p;
+  make_plan(dims, sys_len, &p);
+  if ((rc = check_ws(p, workspace, workspace_bytes)) != RELAY_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if (sys_len > 0 && (rc = launch_sys(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
+  FuseArgs f{};
+  f.a_o = reinterpret_cast<const float*>(ws + p.off_sys_o);
+  f.a_lse = reinterpret_cast<const float*>(ws + p.off_sys_lse);
+  f.a_count = sys_len > 0 ? p.sys_chunks : 0;
+  f.out = o_sys;
+  f.lse_out = lse_sys;
+  f.n_rows = (long long)dims->total_q * dims->num_q_heads;
+  f.num_q_heads = dims->num_q_heads;
+  f.batch = dims->batch;
+  return launch_fuse(f, dims->head_dim, s);
+}
+
+int relay_ctx_attn(const relay_dims* dims, const void* q, const void* ctx_k_pages,
+                   const void* ctx_v_pages, const int32_t* block_tables, const int32_t* ctx_lens,
+                   const int32_t* cu_q_lens, float* o_ctx, float* lse_ctx, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims, 0);
+  if (rc != RELAY_OK) return rc;
+  if ((rc = check_q_layout(dims, cu_q_lens)) != RELAY_OK) return rc;
+  if (!q || !ctx_k_pages || !ctx_v_pages || !block_tables || !ctx_lens || !o_ctx || !lse_ctx)
+    return fail(RELAY_ERR_INVALID, "NULL array argument");
+  if (!aligned16(q) || !aligned16(ctx_k_pages) || !aligned16(ctx_v_pages) || !aligned16(o_ctx))
+    return fail(RELAY_ERR_INVALID, "arrays must be 16-byte aligned");
+  Plan p;
+  make_plan(dims, 0, &p);
+  if ((rc = check_ws(p, workspace, workspace_bytes)) != RELAY_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if ((rc = launch_ctx(dims, p, q, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens, ws, s)) != RELAY_OK)
+    return rc;
+  FuseArgs f{};
+  f.b_o = reinterpret_cast<const float*>(ws + p.off_ctx_o);
+  f.b_lse = reinterpret_cast<const float*>(ws + p.off_ctx_lse);
+  f.b_count = p.ctx_max_splits;
+  f.b_split_len = p.ctx_split_len;
+  f.ctx_lens = ctx_lens;
+  f.cu_q_lens = cu_q_lens;
+  f.out = o_ctx;
+  f.lse_out = lse_ctx;
+  f.n_rows = (long long)dims->total_q * dims->num_q_heads;
+  f.num_q_heads = dims->num_q_heads;
+  f.batch = dims->batch;
+  return launch_fuse(f, dims->head_dim, s);
+}
+
+int relay_fuse(int64_t n_rows, int32_t head_dim, const float* o_sys, const float* lse_sys,
+               const float* o_ctx, const float* lse_ctx, void* out, int32_t out_dtype,
+               float* lse_out, void* stream) {
+  if (n_rows < 0) return fail(RELAY_ERR_INVALID, "n_rows must be >= 0");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(RELAY_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", head_dim);
+  if (out_dtype != RELAY_F32 && out_dtype != RELAY_BF16)
+    return fail(RELAY_ERR_UNSUPPORTED, "out_dtype %d unsupported", out_dtype);
+  if (n_rows == 0) return RELAY_OK;
+  if (!o_sys || !lse_sys || !o_ctx || !lse_ctx || !out) return fail(RELAY_ERR_INVALID, "NULL array argument");
+  if (!aligned16(o_sys) || !aligned16(o_ctx) || !aligned16(out))
+    return fail(RELAY_ERR_INVALID, "arrays must be 16-byte aligned");
+  FuseArgs f{};
+  f.a_o = o_sys;
+  f.a_lse = lse_sys;
+  f.a_count = 1;
+  f.b_o = o_ctx;
+  f.b_lse = lse_ctx;
+  f.b_count = 1;
+  f.b_split_len = 0;
+  f.out = out;
+  f.lse_out = lse_out;
+  f.n_rows = n_rows;
+  f.num_q_heads = 1;
+  f.batch = 1;
+  f.out_bf16 = out_dtype == RELAY_BF16;
+  return launch_fuse(f, head_dim, static_cast<hipStream_t>(stream));
+}
+
+int relay_validate(const relay_dims* dims, const int32_t* h_block_tables, const int32_t* h_ctx_lens,
+                   const int32_t* h_cu_q_lens, int32_t sys_len) {
+  int rc = check_dims(dims, sys_len);
+  if (rc != RELAY_OK) return rc;
+  if ((rc = check_q_layout(dims, h_cu_q_lens)) != RELAY_OK) return rc;
+  if (!h_block_tables || !h_ctx_lens) return fail(RELAY_ERR_INVALID, "NULL host array");
+  if (h_cu_q_lens && h_cu_q_lens[0] != 0) return fail(RELAY_ERR_DATA, "cu_q_lens[0] must be 0");
+  if (h_cu_q_lens && h_cu_q_lens[dims->batch] != dims->total_q)
+    return fail(RELAY_ERR_DATA, "cu_q_lens[B] = %d != total_q = %d", h_cu_q_lens[dims->batch], dims->total_q);
+  for (int b = 0; b < dims->batch; ++b) {
+    const int nb = h_cu_q_lens ? h_cu_q_lens[b + 1] - h_cu_q_lens[b] : 1;
+    const int c = h_ctx_lens[b];
+    if (nb < 1 || nb > dims->max_q_len)
+      return fail(RELAY_ERR_DATA, "request %d: n_b = %d outside [1, max_q_len = %d]", b, nb, dims->max_q_len);
+    if (c < nb || c > dims->max_ctx_len)
+      return fail(RELAY_ERR_DATA, "request %d: ctx_len = %d outside [n_b = %d, max_ctx_len = %d]", b, c, nb,
+                  dims->max_ctx_len);
+    const int pages = (c + 15) / 16;
+    for (int i = 0; i < pages; ++i) {
+      const int blk = h_block_tables[(size_t)b * dims->max_blocks_per_seq + i];
+      if (blk < 0 || blk >= dims->num_blocks)
+        return fail(RELAY_ERR_DATA, "request %d: block_tables[%d] = %d outside [0, %d)", b, i, blk,
+                    dims->num_blocks);
+    }
+  }
+  return RELAY_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,264 @@
+// Device building blocks of the RelayAttention decode kernels for gfx950 (CDNA4).
+//
+// Matrix-core mapping (one 64-lane wavefront, 16x16 output tiles):
+//
+//   * Scores are computed transposed, S^T = K Q^T: the A operand is 16 keys, the B
+//     operand 16 query rows.  Lane l then holds scores of query row l%16 for keys
+//     4*(l/16)+i, i = 0..3 (the 16x16 accumulator layout), so every per-row
+//     softmax quantity lives in the lanes with the same l%16.
+//   * Outputs are computed transposed too, O^T = V^T P^T: the A operand is 16
+//     value dimensions, the B operand is P taken straight from the score
+//     accumulators (no cross-lane shuffle), and the accumulator gives lane l the
+//     outputs of row l%16 for dimensions 16*t + 4*(l/16) + i.
+//   * One step covers 32 keys as two 16-key score tiles whose rows are permuted so
+//     that lane group q = l/16 ends up with the scores of 8 consecutive keys
+//     8q..8q+7 (tile A holds keys 8q+i, tile B keys 8q+4+i).  Those 8 keys are then
+//     the reduction slice of lane group q in O^T = V^T P^T, and because values are
+//     stored dimension-major in 16-key tiles, V^T for them is one contiguous
+//     16-byte (bf16) or 32-byte (fp32) load.
+//   * The reduction order inside one MFMA does not matter for the sum, so any
+//     assignment of head dimensions (for S) or keys (for O) to the k slots is
+//     valid as long as the A and B operands use the same one.  Each lane loads
+//     16 bytes of its row at byte offset 64*kk + 16*(l/16).
+//
+// bf16 uses v_mfma_f32_16x16x32_bf16 (one 16-byte chunk = 8 elements per
+// instruction); fp32 uses v_mfma_f32_16x16x4f32 (one chunk = 4 instructions).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace relay {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kStep = 32;   // keys per step
+constexpr int kTile = 16;   // keys per page / per system V tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct bf16_t {};  // tag: storage is bfloat16 bit patterns
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kBytes = 4;
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int kBytes = 2;
+};
+
+__device__ inline int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ inline float neg_inf() { return -__builtin_inff(); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline float xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+
+// Max / sum over the four lane groups (lanes l, l^16, l^32, l^48) that hold the same row.
+__device__ inline float row_max4(float v) { return xor_max(xor_max(v, 16), 32); }
+__device__ inline float row_sum4(float v) {
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// ---- matrix-core primitives ---------------------------------------------------------
+
+// acc += A(chunk a) * B(chunk b) over the k slots carried by one 16-byte chunk.
+__device__ inline void mfma_chunk(f32x4& acc, u32x4 a, u32x4 b, float) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+__device__ inline void mfma_chunk(f32x4& acc, u32x4 a, u32x4 b, bf16_t) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+// Value fragment: V^T for one 16-dimension tile and the 8 keys of this lane group.
+template <typename T> struct VFrag;
+template <> struct VFrag<bf16_t> {
+  u32x4 c;  // 8 bf16 keys
+};
+template <> struct VFrag<float> {
+  u32x4 c0, c1;  // 8 fp32 keys
+};
+
+// Probability fragment: the 8 probabilities of this lane's row for the same keys.
+// For bf16, c holds P rounded to bf16 and lo the rounding residual P - c (also bf16),
+// used when the product must keep fp32-level accuracy: O = V^T c + V^T lo.
+template <typename T> struct PFrag;
+template <> struct PFrag<bf16_t> {
+  u32x4 c, lo;
+};
+template <> struct PFrag<float> {
+  float p[8];
+};
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  // Round to nearest even (gfx950 converts in hardware).
+  __bf16 a = static_cast<__bf16>(lo);
+  __bf16 b = static_cast<__bf16>(hi);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+__device__ inline float bf16_lo_as_float(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi_as_float(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <bool SPLIT>
+__device__ inline void make_p(PFrag<bf16_t>& f, const float (&p)[8]) {
+  f.c.x = pack_bf16x2(p[0], p[1]);
+  f.c.y = pack_bf16x2(p[2], p[3]);
+  f.c.z = pack_bf16x2(p[4], p[5]);
+  f.c.w = pack_bf16x2(p[6], p[7]);
+  if constexpr (SPLIT) {
+    f.lo.x = pack_bf16x2(p[0] - bf16_lo_as_float(f.c.x), p[1] - bf16_hi_as_float(f.c.x));
+    f.lo.y = pack_bf16x2(p[2] - bf16_lo_as_float(f.c.y), p[3] - bf16_hi_as_float(f.c.y));
+    f.lo.z = pack_bf16x2(p[4] - bf16_lo_as_float(f.c.z), p[5] - bf16_hi_as_float(f.c.z));
+    f.lo.w = pack_bf16x2(p[6] - bf16_lo_as_float(f.c.w), p[7] - bf16_hi_as_float(f.c.w));
+  }
+}
+template <bool SPLIT>
+__device__ inline void make_p(PFrag<float>& f, const float (&p)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.p[i] = p[i];
+}
+
+template <bool SPLIT>
+__device__ inline void mfma_pv(f32x4& acc, const VFrag<bf16_t>& v, const PFrag<bf16_t>& p) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v.c),
+                                                __builtin_bit_cast(bf16x8, p.c), acc, 0, 0, 0);
+  if constexpr (SPLIT)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v.c),
+                                                  __builtin_bit_cast(bf16x8, p.lo), acc, 0, 0, 0);
+}
+template <bool SPLIT>
+__device__ inline void mfma_pv(f32x4& acc, const VFrag<float>& v, const PFrag<float>& p) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c0.x), p.p[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c0.y), p.p[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c0.z), p.p[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c0.w), p.p[3], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c1.x), p.p[4], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c1.y), p.p[5], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c1.z), p.p[6], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c1.w), p.p[7], acc, 0, 0, 0);
+}
+
+// Loads V^T[dim][k0..k0+7] from a dimension-major 16-key tile row (k0 in {0, 8}).
+__device__ inline void load_v(VFrag<bf16_t>& f, const char* row_k0) { f.c = ld16(row_k0); }
+__device__ inline void load_v(VFrag<float>& f, const char* row_k0) {
+  f.c0 = ld16(row_k0);
+  f.c1 = ld16(row_k0 + 16);
+}
+
+// Zeroes the keys of a value fragment whose index (0..7 within the lane group) is
+// >= nvalid.  Poisoned (NaN) padding must not reach an output through 0 * NaN.
+__device__ inline uint32_t keep_bf16_pair(uint32_t w, int k, int nvalid) {
+  uint32_t lo = (k < nvalid) ? (w & 0xFFFFu) : 0u;
+  uint32_t hi = (k + 1 < nvalid) ? (w & 0xFFFF0000u) : 0u;
+  return lo | hi;
+}
+__device__ inline void mask_v(VFrag<bf16_t>& f, int nvalid) {
+  f.c.x = keep_bf16_pair(f.c.x, 0, nvalid);
+  f.c.y = keep_bf16_pair(f.c.y, 2, nvalid);
+  f.c.z = keep_bf16_pair(f.c.z, 4, nvalid);
+  f.c.w = keep_bf16_pair(f.c.w, 6, nvalid);
+}
+__device__ inline void mask_v(VFrag<float>& f, int nvalid) {
+  f.c0.x = 0 < nvalid ? f.c0.x : 0u;
+  f.c0.y = 1 < nvalid ? f.c0.y : 0u;
+  f.c0.z = 2 < nvalid ? f.c0.z : 0u;
+  f.c0.w = 3 < nvalid ? f.c0.w : 0u;
+  f.c1.x = 4 < nvalid ? f.c1.x : 0u;
+  f.c1.y = 5 < nvalid ? f.c1.y : 0u;
+  f.c1.z = 6 < nvalid ? f.c1.z : 0u;
+  f.c1.w = 7 < nvalid ? f.c1.w : 0u;
+}
+
+// Row permutation of the two 16-key score tiles of a 32-key step: A-operand row m
+// of tile A holds key 8*(m/4) + m%4, of tile B key 8*(m/4) + 4 + m%4.
+__device__ inline int step_key_a(int m) { return 8 * (m >> 2) + (m & 3); }
+__device__ inline int step_key_b(int m) { return 8 * (m >> 2) + 4 + (m & 3); }
+
+// ---- online softmax ------------------------------------------------------------------
+
+// Running state of the 16 rows of one row tile, as held by one lane (row l%16).
+template <int D>
+struct RowState {
+  static constexpr int kDT = D / 16;  // 16-dim output tiles
+  float m;                            // running max of scaled scores (log2 domain)
+  float l;                            // this lane's partial sum of 2^(s - m)
+  f32x4 o[kDT];                       // O^T accumulators: dims 16*t + 4*(l/16) + i
+  __device__ void init() {
+    m = neg_inf();
+    l = 0.f;
+#pragma unroll
+    for (int t = 0; t < kDT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// Folds 8 scores (log2 domain, -inf = masked) into the state and returns their
+// probabilities relative to the new running max.
+template <int D>
+__device__ inline void softmax_step(RowState<D>& st, float (&s)[8]) {
+  float mx = s[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+  mx = row_max4(mx);
+  const float m_new = fmaxf(st.m, mx);
+  const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - m_use);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    s[i] = fast_exp2(s[i] - m_use);
+    sum += s[i];
+  }
+  st.l = st.l * alpha + sum;
+#pragma unroll
+  for (int t = 0; t < RowState<D>::kDT; ++t) st.o[t] *= alpha;
+  st.m = m_new;
+}
+
+// Merges state b into a (both per-lane partial sums over the same rows).
+template <int D>
+__device__ inline void merge_state(RowState<D>& a, float mb, float lb, const f32x4* ob) {
+  const float m_new = fmaxf(a.m, mb);
+  const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+  const float wa = fast_exp2(a.m - m_use);
+  const float wb = fast_exp2(mb - m_use);
+  a.l = a.l * wa + lb * wb;
+#pragma unroll
+  for (int t = 0; t < RowState<D>::kDT; ++t) a.o[t] = a.o[t] * wa + ob[t] * wb;
+  a.m = m_new;
+}
+
+// Writes a finished row tile: O = acc / l (0 when the row saw no key) and the
+// natural-log LSE (-inf when empty).  o_row: this lane's row, or nullptr when the
+// row is padding.
+template <int D>
+__device__ inline void store_row_tile(const RowState<D>& st, float* o_row, float* lse_row) {
+  const int q = lane_id() >> 4;
+  const float l = row_sum4(st.l);
+  if (o_row == nullptr) return;
+  const bool empty = !(l > 0.f);
+  const float inv = empty ? 0.f : 1.f / l;
+#pragma unroll
+  for (int t = 0; t < RowState<D>::kDT; ++t) {
+    f32x4 v = st.o[t] * inv;
+    *reinterpret_cast<f32x4*>(o_row + 16 * t + 4 * q) = v;
+  }
+  if (q == 0) *lse_row = empty ? neg_inf() : (st.m + __builtin_amdgcn_logf(l)) * kLn2;
+}
+
+}  // namespace relay

@@ -1,0 +1,293 @@
+"""Python binding of librelay_attn.so (ctypes; argument marshalling only).
+
+Every function has the name of the C entry point it calls (see
+``include/relay_attn.h`` for the contract).  Tensors are torch device tensors;
+PyTorch supplies the device memory and the current stream, nothing else: every
+step of the computation runs in the library's HIP kernels.  There is no fallback:
+if the library is missing or the device is not a GPU, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librelay_attn.so")
+
+RELAY_F32, RELAY_BF16 = 0, 1
+RELAY_OK = 0
+
+
+class relay_dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("max_q_len", ctypes.c_int32),
+        ("max_ctx_len", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("in_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+    ]
+
+
+class relay_plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "sys_chunks", "sys_chunk_len", "sys_row_blocks", "sys_wgs", "ctx_split_len",
+        "ctx_max_splits", "ctx_row_blocks", "ctx_wgs", "fuse_wgs")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class RelayError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"relay error {code}: {msg}")
+        self.code = code
+
+
+EXPORTS = ("relay_abi_version", "relay_strerror", "relay_last_error", "relay_workspace_size",
+           "relay_get_plan", "relay_attn_decode", "relay_attn_decode_timed", "relay_sys_attn",
+           "relay_ctx_attn", "relay_fuse", "relay_validate")
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load librelay_attn.so and declare its signatures (no GPU needed)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m shared_prompt_kv_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    D = ctypes.POINTER(relay_dims)
+    lib.relay_abi_version.argtypes, lib.relay_abi_version.restype = [], ctypes.c_int
+    lib.relay_strerror.argtypes, lib.relay_strerror.restype = [ctypes.c_int], ctypes.c_char_p
+    lib.relay_last_error.argtypes, lib.relay_last_error.restype = [], ctypes.c_char_p
+    lib.relay_workspace_size.argtypes, lib.relay_workspace_size.restype = [D, i32], sz
+    lib.relay_get_plan.argtypes = [D, i32, ctypes.POINTER(relay_plan)]
+    lib.relay_get_plan.restype = ctypes.c_int
+    lib.relay_attn_decode.argtypes = [D, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.relay_attn_decode.restype = ctypes.c_int
+    lib.relay_attn_decode_timed.argtypes = [D, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                            ctypes.POINTER(vp)]
+    lib.relay_attn_decode_timed.restype = ctypes.c_int
+    lib.relay_sys_attn.argtypes = [D, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.relay_sys_attn.restype = ctypes.c_int
+    lib.relay_ctx_attn.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.relay_ctx_attn.restype = ctypes.c_int
+    lib.relay_fuse.argtypes = [ctypes.c_int64, i32, vp, vp, vp, vp, vp, i32, vp, vp]
+    lib.relay_fuse.restype = ctypes.c_int
+    lib.relay_validate.argtypes = [D, vp, vp, vp, i32]
+    lib.relay_validate.restype = ctypes.c_int
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != RELAY_OK:
+        lib = load_library()
+        raise RelayError(rc, f"{lib.relay_strerror(rc).decode()}: {lib.relay_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return RELAY_F32
+    if dt == torch.bfloat16:
+        return RELAY_BF16
+    raise ValueError(f"unsupported dtype {dt} (float32 or bfloat16)")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require_device(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be GPU tensors")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def make_dims(q: torch.Tensor, ctx_k_pages: torch.Tensor, block_tables: torch.Tensor, *,
+              scale: float, max_ctx_len: int, max_q_len: int = 1,
+              out_dtype: torch.dtype = torch.float32) -> relay_dims:
+    """relay_dims from tensor shapes plus the host-known maxima."""
+    Tq, Hq, d = q.shape
+    nb, Hkv, bs, d2 = ctx_k_pages.shape
+    if d2 != d:
+        raise ValueError("head_dim mismatch between q and ctx_k_pages")
+    B, mb = block_tables.shape
+    return relay_dims(B, Hq, Hkv, d, bs, mb, nb, Tq, max_q_len, max_ctx_len, float(scale),
+                      _dtype_code(q.dtype), _dtype_code(out_dtype))
+
+
+def relay_abi_version() -> int:
+    return load_library().relay_abi_version()
+
+
+def relay_workspace_size(dims: relay_dims, sys_len: int) -> int:
+    n = load_library().relay_workspace_size(ctypes.byref(dims), sys_len)
+    if n == 0:
+        lib = load_library()
+        msg = lib.relay_last_error().decode()
+        if msg:
+            raise RelayError(-1, msg)
+    return int(n)
+
+
+def relay_get_plan(dims: relay_dims, sys_len: int) -> dict:
+    p = relay_plan()
+    _check(load_library().relay_get_plan(ctypes.byref(dims), sys_len, ctypes.byref(p)))
+    return p.as_dict()
+
+
+def workspace(dims: relay_dims, sys_len: int, device) -> torch.Tensor:
+    n = max(relay_workspace_size(dims, sys_len), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def relay_attn_decode(q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens,
+                      cu_q_lens=None, out=None, *, scale: float, max_ctx_len: int,
+                      max_q_len: int = 1, out_dtype=torch.float32, workspace_buf=None,
+                      stream=None) -> torch.Tensor:
+    """RelayAttention decode step (system + context attention + relay fusion)."""
+    _require_device(q, sys_k, sys_v, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens, out)
+    dims = make_dims(q, ctx_k_pages, block_tables, scale=scale, max_ctx_len=max_ctx_len,
+                     max_q_len=max_q_len, out_dtype=out_dtype)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    ws = workspace_buf if workspace_buf is not None else workspace(dims, sys_len, q.device)
+    _check(load_library().relay_attn_decode(
+        ctypes.byref(dims), _ptr(q), _ptr(sys_k), _ptr(sys_v), int(sys_len), _ptr(ctx_k_pages),
+        _ptr(ctx_v_pages), _ptr(block_tables), _ptr(ctx_lens), _ptr(cu_q_lens), _ptr(out), _ptr(ws),
+        ws.numel(), _stream(stream)))
+    return out
+
+
+def relay_attn_decode_timed(t: dict, out, workspace_buf, events, out_dtype=torch.float32,
+                            stream=None):
+    """relay_attn_decode on a ``to_device`` dict, recording 4 raw hipEvent_t handles
+    (ints) between the kernels."""
+    dims = dims_of(t, out_dtype)
+    ev = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) if e else None for e in events])
+    _check(load_library().relay_attn_decode_timed(
+        ctypes.byref(dims), _ptr(t["q"]), _ptr(t["sys_k"]), _ptr(t["sys_v"]), int(t["sys_len"]),
+        _ptr(t["ctx_k_pages"]), _ptr(t["ctx_v_pages"]), _ptr(t["block_tables"]), _ptr(t["ctx_lens"]),
+        _ptr(t["cu_q_lens"]), _ptr(out), _ptr(workspace_buf), workspace_buf.numel(), _stream(stream), ev))
+    return out
+
+
+def relay_sys_attn(q, sys_k, sys_v, sys_len, dims: relay_dims, *, workspace_buf=None, stream=None):
+    """System-attention step alone -> (o_sys float32 [T_q,H_q,d], lse_sys float32 [T_q,H_q])."""
+    _require_device(q, sys_k, sys_v)
+    o = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    ws = workspace_buf if workspace_buf is not None else workspace(dims, sys_len, q.device)
+    _check(load_library().relay_sys_attn(ctypes.byref(dims), _ptr(q), _ptr(sys_k), _ptr(sys_v),
+                                         int(sys_len), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
+                                         _stream(stream)))
+    return o, lse
+
+
+def relay_ctx_attn(q, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens, dims: relay_dims,
+                   *, workspace_buf=None, stream=None):
+    """Context-attention step alone -> (o_ctx, lse_ctx)."""
+    _require_device(q, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens)
+    o = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    ws = workspace_buf if workspace_buf is not None else workspace(dims, 0, q.device)
+    _check(load_library().relay_ctx_attn(ctypes.byref(dims), _ptr(q), _ptr(ctx_k_pages),
+                                         _ptr(ctx_v_pages), _ptr(block_tables), _ptr(ctx_lens),
+                                         _ptr(cu_q_lens), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
+                                         _stream(stream)))
+    return o, lse
+
+
+def relay_fuse(o_sys, lse_sys, o_ctx, lse_ctx, *, out_dtype=torch.float32, with_lse=True,
+               stream=None):
+    """Relay fusion alone -> (out, lse or None)."""
+    _require_device(o_sys, lse_sys, o_ctx, lse_ctx)
+    d = o_sys.shape[-1]
+    n = lse_sys.numel()
+    out = torch.empty(o_sys.shape, dtype=out_dtype, device=o_sys.device)
+    lse = torch.empty(lse_sys.shape, dtype=torch.float32, device=o_sys.device) if with_lse else None
+    _check(load_library().relay_fuse(n, d, _ptr(o_sys), _ptr(lse_sys), _ptr(o_ctx), _ptr(lse_ctx),
+                                     _ptr(out), _dtype_code(out_dtype), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def relay_validate(dims: relay_dims, block_tables, ctx_lens, cu_q_lens, sys_len: int) -> None:
+    """Host-side data check on CPU int32 tensors / numpy arrays; raises RelayError."""
+    import numpy as np
+
+    def host(a):
+        if a is None:
+            return None
+        if isinstance(a, torch.Tensor):
+            a = a.cpu().numpy()
+        return np.ascontiguousarray(a, dtype=np.int32)
+
+    bt, cl, cu = host(block_tables), host(ctx_lens), host(cu_q_lens)
+    _check(load_library().relay_validate(
+        ctypes.byref(dims), bt.ctypes.data_as(ctypes.c_void_p), cl.ctypes.data_as(ctypes.c_void_p),
+        None if cu is None else cu.ctypes.data_as(ctypes.c_void_p), int(sys_len)))
+
+
+# ---- marshalling of generator workloads -------------------------------------------------
+
+
+def to_device(w, device="cuda", single_query_null_cu: bool = True) -> dict:
+    """Upload a ``workloads.Workload`` to ``device`` in the C-ABI layouts."""
+    import numpy as np
+
+    def arr(a):
+        if w.spec.dtype == "bf16":
+            t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+        return t.to(device)
+
+    ints = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+    multi = int(w.q_lens.max()) > 1
+    dt = torch.bfloat16 if w.spec.dtype == "bf16" else torch.float32
+    sys_k = arr(w.sys_k) if w.spec.sys_len > 0 else torch.zeros(16, dtype=dt, device=device)
+    sys_v = arr(w.sys_v) if w.spec.sys_len > 0 else torch.zeros(16, dtype=dt, device=device)
+    return dict(
+        q=arr(w.q), sys_k=sys_k, sys_v=sys_v, sys_len=w.spec.sys_len,
+        ctx_k_pages=arr(w.ctx_k_pages), ctx_v_pages=arr(w.ctx_v_pages),
+        block_tables=ints(w.block_tables), ctx_lens=ints(w.ctx_lens),
+        cu_q_lens=ints(w.cu_q_lens) if (multi or not single_query_null_cu) else None,
+        scale=w.spec.scale, max_ctx_len=int(w.ctx_lens.max()), max_q_len=int(w.q_lens.max()))
+
+
+def decode_workload(t: dict, out_dtype=torch.float32, workspace_buf=None, stream=None, out=None):
+    """relay_attn_decode on the dict returned by ``to_device``."""
+    return relay_attn_decode(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], t["ctx_k_pages"],
+                             t["ctx_v_pages"], t["block_tables"], t["ctx_lens"], t["cu_q_lens"], out,
+                             scale=t["scale"], max_ctx_len=t["max_ctx_len"], max_q_len=t["max_q_len"],
+                             out_dtype=out_dtype, workspace_buf=workspace_buf, stream=stream)
+
+
+def dims_of(t: dict, out_dtype=torch.float32) -> relay_dims:
+    return make_dims(t["q"], t["ctx_k_pages"], t["block_tables"], scale=t["scale"],
+                     max_ctx_len=t["max_ctx_len"], max_q_len=t["max_q_len"], out_dtype=out_dtype)

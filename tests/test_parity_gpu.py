@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: fp32 inputs max|gpu - oracle| <= 1e-5; bf16 inputs (fp32 accumulation)
+max|gpu - oracle| <= 2e-3 and ||gpu - oracle||_2 / ||oracle||_2 <= 1e-2 over the
+whole output.  Integer-valued properties (page relabelling, batch permutation,
+poison, determinism) are checked bitwise.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from shared_prompt_kv_amd import relay as R
+from shared_prompt_kv_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16_ABS = 2e-3
+TOL_BF16_REL = 1e-2
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    R.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def check(gpu, ref, dtype, what=""):
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    gi, ri = np.isneginf(g), np.isneginf(r)
+    np.testing.assert_array_equal(gi, ri, err_msg=f"{what}: -inf pattern")
+    assert np.all(np.isfinite(g[~gi])), f"{what}: non-finite values"
+    diff = np.abs(g[~gi] - r[~ri])
+    err = float(diff.max()) if diff.size else 0.0
+    if dtype == "f32":
+        assert err <= TOL_F32, f"{what}: max abs {err:.3e} > {TOL_F32}"
+    else:
+        rel = float(np.linalg.norm(g[~gi] - r[~ri]) / max(np.linalg.norm(r[~ri]), 1e-30))
+        assert err <= TOL_BF16_ABS, f"{what}: max abs {err:.3e} > {TOL_BF16_ABS}"
+        assert rel <= TOL_BF16_REL, f"{what}: rel L2 {rel:.3e} > {TOL_BF16_REL}"
+    return err
+
+
+@functools.lru_cache(maxsize=4)
+def workload(spec):
+    return W.generate(spec)
+
+
+def upload(w):
+    return R.to_device(w, "cuda")
+
+
+# ------------------------------------------------------------------------------------------
+# small and medium cases: several tiles, ragged tails, every row checked
+
+SMALL = [
+    W.config_spec(1),
+    W.config_spec(1).replace(name="c1-d128", head_dim=128, sys_len=77, ctx_lo=1, ctx_hi=70),
+    W.config_spec(2).replace(batch=5, sys_len=333, ctx_lo=16, ctx_hi=100),
+    W.config_spec(2).replace(name="c2-d64", head_dim=64, batch=3, sys_len=100, ctx_lo=1, ctx_hi=50),
+    W.config_spec(3, 0).replace(batch=3, num_q_heads=6, num_kv_heads=6, sys_len=200),
+    W.config_spec(4).replace(batch=9, sys_len=515, ctx_median=60, ctx_cap=200),
+    W.config_spec(5).replace(batch=5, sys_len=290, ctx_lo=64, ctx_hi=300),
+    W.config_spec(5).replace(name="c5-f32", dtype="f32", batch=3, sys_len=40, ctx_lo=17, ctx_hi=99),
+    W.config_spec(5).replace(name="c5-g8", batch=3, num_q_heads=32, num_kv_heads=4, sys_len=64,
+                             ctx_lo=20, ctx_hi=90),
+]
+SMALL_IDS = [f"{s.name}-B{s.batch}-L{s.sys_len}-d{s.head_dim}" for s in SMALL]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=SMALL_IDS)
+def test_decode_matches_oracle_small(spec):
+    say(f"[parity] relay_attn_decode {spec}")
+    w = workload(spec)
+    t = upload(w)
+    out = R.decode_workload(t)
+    torch.cuda.synchronize()
+    ref, _ = oracle.Problem(w).attention()
+    check(out.cpu().numpy(), ref, spec.dtype, "out")
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=SMALL_IDS)
+def test_system_step_matches_oracle(spec):
+    say(f"[parity] relay_sys_attn {spec}")
+    w = workload(spec)
+    t = upload(w)
+    o, lse = R.relay_sys_attn(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], R.dims_of(t))
+    torch.cuda.synchronize()
+    ro, rl = oracle.Problem(w).system_part()
+    check(o.cpu().numpy(), ro, spec.dtype, "o_sys")
+    check(lse.cpu().numpy(), rl, spec.dtype, "lse_sys")
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=SMALL_IDS)
+def test_context_step_matches_oracle(spec):
+    say(f"[parity] relay_ctx_attn {spec}")
+    w = workload(spec)
+    t = upload(w)
+    o, lse = R.relay_ctx_attn(t["q"], t["ctx_k_pages"], t["ctx_v_pages"], t["block_tables"],
+                              t["ctx_lens"], t["cu_q_lens"], R.dims_of(t))
+    torch.cuda.synchronize()
+    ro, rl = oracle.Problem(w).context_part()
+    check(o.cpu().numpy(), ro, spec.dtype, "o_ctx")
+    check(lse.cpu().numpy(), rl, spec.dtype, "lse_ctx")
+
+
+def test_fuse_on_oracle_partials():
+    say("[parity] relay_fuse on oracle partials")
+    w = workload(W.config_spec(5).replace(batch=4, sys_len=150, ctx_lo=64, ctx_hi=200))
+    P = oracle.Problem(w)
+    o_s, l_s = P.system_part()
+    o_c, l_c = P.context_part()
+    ref, ref_lse, _ = oracle.relay_fuse(o_s, l_s, o_c, l_c)
+    # force empty parts on some rows: a -inf LSE carries weight 0
+    l_s = l_s.copy()
+    l_s[0, :] = -np.inf
+    o_s = o_s.copy()
+    o_s[0, :] = 0.0
+    ref[0], ref_lse[0] = o_c[0], l_c[0]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    out, lse = R.relay_fuse(dev(o_s), dev(l_s), dev(o_c), dev(l_c))
+    torch.cuda.synchronize()
+    assert np.max(np.abs(out.cpu().numpy() - ref)) <= 1e-6
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= 1e-5
+    out16, _ = R.relay_fuse(dev(o_s), dev(l_s), dev(o_c), dev(l_c), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    # bf16 output: within one bf16 ulp of the fp64 result
+    o16 = out16.float().cpu().numpy().astype(np.float64)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    assert np.all(np.abs(o16 - ref) <= ulp + 1e-6)
+
+
+# ------------------------------------------------------------------------------------------
+# edge cases
+
+
+def test_zero_system_length_equals_context_attention():
+    spec = W.config_spec(2).replace(batch=4, sys_len=0, ctx_lo=1, ctx_hi=90)
+    say(f"[parity] sys_len=0 {spec}")
+    w = workload(spec)
+    t = upload(w)
+    out = R.decode_workload(t)
+    o, lse = R.relay_sys_attn(t["q"], t["sys_k"], t["sys_v"], 0, R.dims_of(t))
+    torch.cuda.synchronize()
+    ref, _ = oracle.Problem(w).attention()
+    check(out.cpu().numpy(), ref, "bf16", "out")
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_single_token_contexts_and_tiny_system():
+    spec = W.config_spec(1).replace(batch=7, sys_len=1, ctx_lo=1, ctx_hi=1)
+    say(f"[parity] ctx_len=1 {spec}")
+    w = workload(spec)
+    out = R.decode_workload(upload(w))
+    torch.cuda.synchronize()
+    check(out.cpu().numpy(), oracle.Problem(w).attention()[0], "f32", "out")
+
+
+def test_nan_poison_never_reaches_output():
+    spec = W.config_spec(5).replace(batch=4, sys_len=45, ctx_lo=20, ctx_hi=75)
+    say(f"[parity] NaN poison {spec}")
+    a = R.decode_workload(upload(workload(spec)))
+    b = R.decode_workload(upload(workload(spec.replace(poison="nan"))))
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(b))
+    assert torch.equal(a, b)
+
+
+def test_page_relabelling_is_bitwise_invariant():
+    spec = W.config_spec(4).replace(batch=6, sys_len=100, ctx_median=50, ctx_cap=150)
+    say(f"[parity] relabel {spec}")
+    w = workload(spec)
+    a = R.decode_workload(upload(w))
+    b = R.decode_workload(upload(W.relabel_pages(w, 11)))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_batch_permutation_permutes_output():
+    import dataclasses
+    spec = W.config_spec(5).replace(batch=4, sys_len=70, ctx_lo=20, ctx_hi=60)
+    say(f"[parity] batch permutation {spec}")
+    w = workload(spec)
+    perm = np.array([3, 1, 0, 2])
+    cu = w.cu_q_lens
+    q2 = np.concatenate([w.q[cu[b]:cu[b + 1]] for b in perm])
+    ql = w.q_lens[perm]
+    w2 = dataclasses.replace(w, q=np.ascontiguousarray(q2), block_tables=np.ascontiguousarray(w.block_tables[perm]),
+                             ctx_lens=np.ascontiguousarray(w.ctx_lens[perm]), q_lens=ql,
+                             cu_q_lens=np.concatenate([[0], np.cumsum(ql)]).astype(np.int32))
+    a = R.decode_workload(upload(w)).cpu()
+    b = R.decode_workload(upload(w2)).cpu()
+    assert torch.equal(b, torch.cat([a[cu[i]:cu[i + 1]] for i in perm]))
+
+
+def test_run_to_run_determinism():
+    spec = W.config_spec(2).replace(batch=8, sys_len=700, ctx_lo=16, ctx_hi=300)
+    say(f"[parity] determinism {spec}")
+    t = upload(workload(spec))
+    a = R.decode_workload(t)
+    b = R.decode_workload(t)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_bf16_output():
+    spec = W.config_spec(2).replace(batch=4, sys_len=260, ctx_lo=16, ctx_hi=90)
+    say(f"[parity] bf16 out {spec}")
+    w = workload(spec)
+    out = R.decode_workload(upload(w), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, _ = oracle.Problem(w).attention()
+    g = out.float().cpu().numpy().astype(np.float64)
+    # fp32 tolerance plus one bf16 ulp of the value
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    assert np.all(np.abs(g - ref) <= TOL_BF16_ABS + ulp)
+
+
+# ------------------------------------------------------------------------------------------
+# full configuration sizes (sampled rows where the oracle would take minutes)
+
+FULL = [(1, 0, None), (2, 0, None), (3, 0, None), (3, 5, 400), (4, 0, 600), (5, 0, 160)]
+
+
+@pytest.mark.parametrize("cfg,sweep,n_rows", FULL, ids=[f"c{c}s{s}" for c, s, _ in FULL])
+def test_decode_matches_oracle_full_size(cfg, sweep, n_rows):
+    spec = W.config_spec(cfg, sweep)
+    say(f"[parity] full size {spec} rows={n_rows or 'all'}")
+    w = W.generate(spec)
+    t = upload(w)
+    out = R.decode_workload(t)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().reshape(-1, spec.head_dim)
+    P = oracle.Problem(w)
+    if n_rows is None:
+        ref, _ = P.attention()
+        check(out, ref.reshape(-1, spec.head_dim), spec.dtype, "out")
+    else:
+        n_all = w.total_q * spec.num_q_heads
+        rng = np.random.default_rng(1000 + cfg)
+        rows = np.unique(np.concatenate([[0, n_all - 1], rng.integers(0, n_all, n_rows)]))
+        ref, _ = P.attention(rows)
+        check(out[rows], ref, spec.dtype, "out")
+    del t
+    torch.cuda.empty_cache()
