@@ -73,6 +73,8 @@ def work_of(w):
         "step_flops": 4 * Hq * d * (Tq * s.sys_len + vis),
         "sys_attn": kv_sys + q_bytes + part_row,
         "ctx_attn": kv_ctx + q_bytes + tables + part_row,
+        # both steps in one launch: every input once, both intermediate outputs
+        "sys_ctx_attn": kv_sys + kv_ctx + q_bytes + tables + 2 * part_row,
         "relay_fuse": 2 * part_row + rows * d * 4,
         "sys_flops": 4 * Hq * d * Tq * s.sys_len,
         "ctx_flops": 4 * Hq * d * vis,
@@ -120,7 +122,14 @@ def clone_set(torch, t):
 
 
 def measure(torch, relay, w, steps, warmup, per_kernel=True):
-    """Times `steps` decode steps rotating over input copies; returns a dict."""
+    """Times decode steps over rotating input copies.
+
+    graph: the steps captured in one HIP graph (a full rotation over the copies)
+    and replayed, as a served model replays its decode step; the timed region holds
+    `steps` steps.  eager: the same steps launched one by one through the prepared
+    C-ABI call.  Per-kernel durations come from HIP events recorded by the library
+    between its launches (eager).
+    """
     t0 = relay.to_device(w, "cuda")
     work = work_of(w)
     n_sets = max(2, math.ceil(3 * MALL_BYTES / max(work["step_bytes"], 1)))
@@ -129,33 +138,64 @@ def measure(torch, relay, w, steps, warmup, per_kernel=True):
     dims = relay.dims_of(t0)
     ws = relay.workspace(dims, t0["sys_len"], "cuda")
     outs = [torch.empty(t0["q"].shape, dtype=torch.float32, device="cuda") for _ in range(n_sets)]
+    calls = [relay.DecodeCall(sets[i], outs[i], ws) for i in range(n_sets)]
+    res = {"n_sets": n_sets, "work": work, "plan": relay.relay_get_plan(dims, t0["sys_len"])}
+
     for i in range(warmup):
-        relay.decode_workload(sets[i % n_sets], workspace_buf=ws, out=outs[i % n_sets])
+        calls[i % n_sets]()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
-        relay.decode_workload(sets[i % n_sets], workspace_buf=ws, out=outs[i % n_sets])
+        calls[i % n_sets]()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    res = {"ms_per_step": ms, "n_sets": n_sets, "work": work, "plan": relay.relay_get_plan(dims, t0["sys_len"])}
+    res["eager_ms_per_step"] = e0.elapsed_time(e1) / steps
+
+    # HIP graph of one rotation (n_sets steps), replayed
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for c in calls:
+            c()
+    reps = max(1, steps // n_sets)
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    res["graph_ms_per_step"] = e0.elapsed_time(e1) / (reps * n_sets)
+    res["graph_steps"] = reps * n_sets
+    res["ms_per_step"] = res["graph_ms_per_step"]
+    del graph
+
     if per_kernel:
         he = HipEvents(torch)
         evs = he.create(4 * steps)
         for i in range(steps):
-            relay.relay_attn_decode_timed(sets[i % n_sets], outs[i % n_sets], ws, evs[4 * i:4 * i + 4])
+            calls[i % n_sets].timed(evs[4 * i:4 * i + 4])
         torch.cuda.synchronize()
-        acc = {"sys_attn": 0.0, "ctx_attn": 0.0, "relay_fuse": 0.0}
+        # launch names: a separate (tiled) system launch, then the attention launch
+        # (both steps together when sys_mode == 1), then relay_fuse
+        mode = res["plan"]["sys_mode"]
+        names = ("sys_attn", "ctx_attn" if mode != 1 else "sys_ctx_attn", "relay_fuse")
+        acc = dict.fromkeys(names, 0.0)
         for i in range(steps):
             e = evs[4 * i:4 * i + 4]
-            acc["sys_attn"] += he.elapsed_ms(e[0], e[1])
-            acc["ctx_attn"] += he.elapsed_ms(e[1], e[2])
-            acc["relay_fuse"] += he.elapsed_ms(e[2], e[3])
+            for j, k in enumerate(names):
+                acc[k] += he.elapsed_ms(e[j], e[j + 1])
         he.destroy(evs)
-        res["kernel_us"] = {k: 1000.0 * v / steps for k, v in acc.items()}
-    del sets, outs, ws
+        res["kernel_us"] = {k: 1000.0 * v / steps for k, v in acc.items() if mode == 2 or k != "sys_attn"}
+    del calls, sets, outs, ws
     torch.cuda.empty_cache()
     return res
 
@@ -218,6 +258,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "timing": "HIP graph replay of the decode step (eager launch: %.5f ms/step)" % r["eager_ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -244,7 +285,7 @@ def main():
             rr = measure(torch, relay, ws_, min(args.steps, 50), min(args.warmup, 10), per_kernel=True)
             m = rr["ms_per_step"]
             sweep.append({"sys_len": Ls, "qtok_s": round(ws_.total_q / (m * 1e-3), 1),
-                          "us_per_step": round(1000 * m, 2),
+                          "us_per_step": round(1000 * m, 2), "eager_us_per_step": round(1000 * rr["eager_ms_per_step"], 2),
                           "hbm_frac": round(rr["work"]["step_bytes"] / (m * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
                           "kernel_us": {k: round(v, 2) for k, v in rr["kernel_us"].items()}})
             del ws_

@@ -122,8 +122,11 @@ typedef struct {
   int32_t ctx_split_len;   /* context keys per split (a multiple of 32) */
   int32_t ctx_max_splits;  /* ceil(max_ctx_len / ctx_split_len) */
   int32_t ctx_row_blocks;  /* query-row blocks per (request, KV head) */
-  int32_t ctx_wgs;         /* workgroups of one context-attention launch (upper bound) */
+  int32_t ctx_wgs;         /* context-attention work units (workgroups; some exit at once) */
   int32_t fuse_wgs;        /* workgroups of one fusion launch */
+  int32_t sys_mode;        /* 0: no system step; 1: single-wave units, launched together with
+                              the context units; 2: tiled kernel (many stacked query rows) */
+  int32_t launches;        /* kernel launches of one relay_attn_decode call */
 } relay_plan;
 
 /* ABI version compiled into the library (RELAY_ATTN_ABI_VERSION). */
@@ -164,7 +167,8 @@ int relay_attn_decode(const relay_dims* dims, const void* q, const void* sys_k,
 /*
  * relay_attn_decode with per-kernel timing: identical work, plus events[0..3]
  * (hipEvent_t handles created by the caller; any entry may be NULL) recorded on
- * `stream` before sys_attn, before ctx_attn, before relay_fuse and after
+ * `stream`: [0] first, [1] after a separate system-attention launch (right after
+ * [0] when the steps share one launch), [2] after the attention launch, [3] after
  * relay_fuse.  For benchmarks; events must not be NULL.
  */
 int relay_attn_decode_timed(const relay_dims* dims, const void* q, const void* sys_k,

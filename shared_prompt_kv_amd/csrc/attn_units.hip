@@ -1,0 +1,327 @@
+// Streaming attention units for gfx950: RelayAttention's system-attention and
+// context-attention steps as workgroup-sized work units.
+//
+// System unit (KV head h, key chunk, 16-row tile): the tile holds 16 of the
+// M = T_q * g query rows that use KV head h, stacked across all requests of the
+// batch, so the system K/V of the chunk serve every request's query at once
+// (RelayAttention paper, abstract; atyun.com article, section "RelayAttention":
+// matrix-vector products against the system prompt grouped into matrix-matrix
+// products).  When M > 16 the row tiles of one chunk are separate units placed on
+// the same XCD back to back, so the chunk leaves HBM once and the repeat reads hit
+// that XCD's L2.
+//
+// Context unit (request b, KV head h, split, row block): causal attention of the
+// request's g * n_b query rows over one fixed-length run of its paged context.
+// Query token t sits at context position c_b - n_b + t.  The page ids of the whole
+// split are fetched once, one per lane, and broadcast per step.  A unit whose split
+// lies past the end of the context writes LSE = -inf for its rows, so relay_fuse
+// can read every split slot without knowing the context lengths.
+//
+// A unit is one workgroup of WK waves (key lanes).  Key lane kl streams the 16-key
+// steps (pages) kl, kl+WK, ... of the unit, so a unit's critical path is 1/WK of its steps;
+// the lanes' softmax states are merged through LDS (fixed order) and key lane 0
+// writes one partial (O, LSE) per row.  sys_ctx_attn_kernel carries both kinds of
+// unit in one launch (system units first: they are the longest), so the two steps
+// overlap and the machine fills even when one step alone could not.
+#include "relay_device.hpp"
+#include "relay_internal.hpp"
+
+namespace relay {
+
+// Runs the steps kl, kl+WK, ... < nsteps.  PF: double-buffered, the loads of the
+// next step are issued before the current one is computed; otherwise one step's
+// loads at a time (fewer registers, more resident waves).
+template <bool PF, int WK, class Frag, class Issue, class Run>
+__device__ inline void stream_steps(int kl, int nsteps, Issue&& issue, Run&& run) {
+  if constexpr (PF) {
+    Frag f0, f1;
+    if (kl < nsteps) issue(f0, kl);
+    for (int s = kl; s < nsteps; s += 2 * WK) {
+      if (s + WK < nsteps) issue(f1, s + WK);
+      run(f0, s);
+      if (s + WK >= nsteps) break;
+      if (s + 2 * WK < nsteps) issue(f0, s + 2 * WK);
+      run(f1, s + WK);
+    }
+  } else {
+    Frag f;
+    for (int s = kl; s < nsteps; s += WK) {
+      issue(f, s);
+      run(f, s);
+    }
+  }
+}
+
+template <typename T, int D>
+__device__ inline void load_q_tile(u32x4* qf, const void* q, size_t row_index, bool valid) {
+  constexpr int E = Elem<T>::kBytes;
+  const int q4 = lane_id() >> 4;
+  const char* qp = static_cast<const char*>(q) + row_index * D * E;
+#pragma unroll
+  for (int kk = 0; kk < PageFrag<T, D>::NCH; ++kk)
+    qf[kk] = valid ? ld16(qp + 64 * kk + 16 * q4) : u32x4{0u, 0u, 0u, 0u};
+}
+
+template <typename T, int D, int WK, bool PF>
+__device__ void sys_unit(const UnitArgs& a, int u, float* lds) {
+  constexpr int E = Elem<T>::kBytes;
+  const int lane = lane_id();
+  const int kl = threadIdx.x / kWave;
+  const int q4 = lane >> 4, r16 = lane & 15;
+  // unit id -> (row tile, chunk group): the row tiles of one chunk are 8 ids apart,
+  // i.e. on the same XCD (workgroup i runs on XCD i % 8) and dispatched together.
+  const int slot = u >> 3;
+  const int rt = slot % a.sys_row_tiles;
+  const int grp = (u & 7) + 8 * (slot / a.sys_row_tiles);
+  const int chunk = grp % a.sys_chunks;
+  const int h = grp / a.sys_chunks;
+  if (h >= a.num_kv_heads) return;  // padding unit: uniform over the workgroup
+
+  const int M = a.total_q * a.group;
+  const int row = rt * 16 + r16;
+  const int t = row / a.group, gi = row % a.group;
+  const size_t qrow = (size_t)t * a.num_q_heads + (size_t)h * a.group + gi;
+  u32x4 qf[1][PageFrag<T, D>::NCH];
+  load_q_tile<T, D>(qf[0], a.q, qrow, row < M);
+  RowState<D> st[1];
+  st[0].init();
+  const int last[1] = {a.sys_len - 1};
+
+  const int Ls = a.sys_len;
+  const int key_begin = chunk * a.sys_chunk_len;
+  const int key_end = min(key_begin + a.sys_chunk_len, Ls);
+  const int nsteps = (key_end - key_begin + kTile - 1) / kTile;
+  const int ntile = (Ls + kTile - 1) / kTile;
+  const char* kbase = static_cast<const char*>(a.sys_k) + (size_t)h * Ls * D * E;
+  const char* vbase = static_cast<const char*>(a.sys_v) + (size_t)h * ntile * D * kTile * E;
+
+  // step s is system tile key_begin/16 + s; K rows past the end of the keys are
+  // clamped (their scores are masked, their values zeroed)
+  auto issue = [&](PageFrag<T, D>& f, int s) {
+    const int key0 = key_begin + s * kTile;
+    load_page<T, D>(f, kbase + (size_t)key0 * D * E, vbase + (size_t)(key0 / kTile) * D * kTile * E,
+                    min(r16, Ls - 1 - key0));
+  };
+  auto run = [&](PageFrag<T, D>& f, int s) {
+    compute_page<T, D, 1, true>(f, qf, st, key_begin + s * kTile + 4 * q4, Ls, last, a.scale_log2);
+  };
+  stream_steps<PF, WK, PageFrag<T, D>>(kl, nsteps, issue, run);
+  merge_key_lanes<D, 1, WK>(st, kl, lds);
+
+  if (kl == 0) {
+    float* orow = nullptr;
+    float* lrow = nullptr;
+    if (row < M) {
+      const size_t r = (size_t)chunk * a.total_q * a.num_q_heads + qrow;
+      orow = a.sys_o + r * D;
+      lrow = a.sys_lse + r;
+    }
+    store_row_tile(st[0], orow, lrow);
+  }
+}
+
+template <typename T, int D, int RT, int WK, bool PF>
+__device__ void ctx_unit(const UnitArgs& a, int v, float* lds) {
+  constexpr int E = Elem<T>::kBytes;
+  constexpr int NCH = PageFrag<T, D>::NCH;
+  const int lane = lane_id();
+  const int kl = threadIdx.x / kWave;
+  const int q4 = lane >> 4, r16 = lane & 15;
+  const int slot = v >> 3;
+  const int rb = slot % a.ctx_row_blocks;
+  int grp = (v & 7) + 8 * (slot / a.ctx_row_blocks);
+  const int split = grp % a.ctx_max_splits;
+  grp /= a.ctx_max_splits;
+  const int h = grp % a.num_kv_heads;
+  const int b = grp / a.num_kv_heads;
+  if (b >= a.batch) return;  // padding unit
+
+  // Clamped per-request sizes: bad inputs cannot move an access out of bounds.
+  const int cap = min(a.max_ctx_len, a.max_blocks_per_seq * kTile);
+  const int c = min(max(a.ctx_lens[b], 0), cap);
+  int qs = b, nq = 1;
+  if (a.cu_q_lens) {
+    qs = min(max(a.cu_q_lens[b], 0), a.total_q);
+    nq = min(max(a.cu_q_lens[b + 1] - qs, 0), a.total_q - qs);
+  }
+  const int R = nq * a.group;
+  const int row0 = rb * RT * 16;
+  if (row0 >= R) return;  // no rows in this block: uniform over the workgroup
+  const int key_begin = split * a.ctx_split_len;
+  const int key_end = min(key_begin + a.ctx_split_len, c);
+
+  size_t qrow[RT];
+  int last[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = row0 + rt * 16 + r16;
+    const int tl = row / a.group, gi = row % a.group;
+    qrow[rt] = (size_t)(qs + tl) * a.num_q_heads + (size_t)h * a.group + gi;
+    last[rt] = row < R ? c - nq + tl : -1;
+  }
+  if (key_begin >= c) {  // split past the context: an empty partial
+    if (kl == 0 && q4 == 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        if (last[rt] >= 0) a.ctx_lse[(size_t)split * a.total_q * a.num_q_heads + qrow[rt]] = neg_inf();
+    }
+    return;
+  }
+
+  // page ids of the split, one per lane (split_len <= 1024 keys = 64 pages)
+  const int npages = (c + kTile - 1) / kTile;
+  const int pg_begin = key_begin / kTile;
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+  int pt = 0;
+  if (lane < a.ctx_split_len / kTile && pg_begin + lane < npages) pt = bt[pg_begin + lane];
+
+  u32x4 qf[RT][NCH];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) load_q_tile<T, D>(qf[rt], a.q, qrow[rt], last[rt] >= 0);
+  pt = min(max(pt, 0), a.num_blocks - 1);
+  RowState<D> st[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) st[rt].init();
+
+  const size_t page_stride = (size_t)a.num_kv_heads * kTile * D * E;
+  const char* kbase = static_cast<const char*>(a.ctx_k) + (size_t)h * kTile * D * E;
+  const char* vbase = static_cast<const char*>(a.ctx_v) + (size_t)h * D * kTile * E;
+  const int nsteps = (key_end - key_begin + kTile - 1) / kTile;
+
+  // step s is the split's page s
+  auto issue = [&](PageFrag<T, D>& f, int s) {
+    const int blk = __builtin_amdgcn_readlane(pt, s);
+    load_page<T, D>(f, kbase + (size_t)blk * page_stride, vbase + (size_t)blk * page_stride, r16);
+  };
+  auto run = [&](PageFrag<T, D>& f, int s) {
+    compute_page<T, D, RT, true>(f, qf, st, key_begin + s * kTile + 4 * q4, c, last, a.scale_log2);
+  };
+  stream_steps<PF, WK, PageFrag<T, D>>(kl, nsteps, issue, run);
+  merge_key_lanes<D, RT, WK>(st, kl, lds);
+
+  if (kl == 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float* orow = nullptr;
+      float* lrow = nullptr;
+      if (last[rt] >= 0) {
+        const size_t r = (size_t)split * a.total_q * a.num_q_heads + qrow[rt];
+        orow = a.ctx_o + r * D;
+        lrow = a.ctx_lse + r;
+      }
+      store_row_tile(st[rt], orow, lrow);
+    }
+  }
+}
+
+template <int D, int RT, int WK>
+constexpr size_t units_lds_bytes() {
+  return WK > 1 ? sizeof(float) * (size_t)(WK / 2) * kMergeSlot<D, RT> : 0;
+}
+
+// The kernels are persistent: the grid is sized to what the GPU holds at once and
+// workgroup g takes units g, g + gridDim.x, ...; no workgroup waits to be dispatched
+// and every unit's setup latency overlaps other workgroups' streaming.
+// (Barriers inside a unit are reached by every wave of the workgroup: the unit loop
+// depends on blockIdx only.)
+
+// The system-attention step alone (at most 64 stacked rows: row tiles as units).
+template <typename T, int D, int WK, bool PF>
+__global__ __launch_bounds__(kWave* WK) void sys_attn_kernel(UnitArgs a) {
+  extern __shared__ float lds[];
+  for (int u = blockIdx.x; u < a.n_sys_units; u += gridDim.x) sys_unit<T, D, WK, PF>(a, u, lds);
+}
+
+// The context-attention step alone.
+template <typename T, int D, int RT, int WK, bool PF>
+__global__ __launch_bounds__(kWave* WK) void ctx_attn_kernel(UnitArgs a) {
+  extern __shared__ float lds[];
+  for (int u = blockIdx.x; u < a.n_ctx_units; u += gridDim.x) ctx_unit<T, D, RT, WK, PF>(a, u, lds);
+}
+
+// Both steps in one launch: units [0, n_sys_units) are system units (the longest,
+// taken first), the rest context units.
+template <typename T, int D, int RT, int WK, bool PF>
+__global__ __launch_bounds__(kWave* WK) void sys_ctx_attn_kernel(UnitArgs a) {
+  extern __shared__ float lds[];
+  const int total = a.n_sys_units + a.n_ctx_units;
+  for (int u = blockIdx.x; u < total; u += gridDim.x) {
+    if (u < a.n_sys_units) sys_unit<T, D, WK, PF>(a, u, lds);
+    else ctx_unit<T, D, RT, WK, PF>(a, u - a.n_sys_units, lds);
+  }
+}
+
+// Workgroups of kernel `k` that one CU holds at once.
+static int blocks_per_cu(const void* k, int threads, size_t lds) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, threads, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  return per_cu;
+}
+
+template <typename T, int D, int RT, int WK, bool PF>
+static hipError_t launch_units_t(const UnitArgs& a, int what, hipStream_t s) {
+  constexpr size_t lds = units_lds_bytes<D, RT, WK>();
+  static_assert(lds <= 64 * 1024, "LDS budget");
+  const void* k;
+  int units;
+  if (what == kUnitsSys) {
+    k = reinterpret_cast<const void*>(&sys_attn_kernel<T, D, WK, PF>);
+    units = a.n_sys_units;
+  } else if (what == kUnitsCtx) {
+    k = reinterpret_cast<const void*>(&ctx_attn_kernel<T, D, RT, WK, PF>);
+    units = a.n_ctx_units;
+  } else {
+    k = reinterpret_cast<const void*>(&sys_ctx_attn_kernel<T, D, RT, WK, PF>);
+    units = a.n_sys_units + a.n_ctx_units;
+  }
+  static const int per_cu = blocks_per_cu(k, kWave * WK, lds);  // once per kernel instance
+  const long long cap = 256LL * per_cu;
+  int grid = a.grid > 0 ? a.grid : (int)(units < cap ? units : cap);
+  if (grid > units) grid = units;
+  if (grid < 1) grid = 1;
+  if (what == kUnitsSys)
+    hipLaunchKernelGGL((sys_attn_kernel<T, D, WK, PF>), dim3(grid), dim3(kWave * WK), lds, s, a);
+  else if (what == kUnitsCtx)
+    hipLaunchKernelGGL((ctx_attn_kernel<T, D, RT, WK, PF>), dim3(grid), dim3(kWave * WK), lds, s, a);
+  else
+    hipLaunchKernelGGL((sys_ctx_attn_kernel<T, D, RT, WK, PF>), dim3(grid), dim3(kWave * WK), lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int RT>
+static hipError_t launch_units_w(const UnitArgs& a, int what, hipStream_t s) {
+  if constexpr (RT > 1) {  // two row tiles: at most 4 key lanes (LDS merge budget)
+    if (a.key_lanes == 1) return a.prefetch ? launch_units_t<T, D, RT, 1, true>(a, what, s)
+                                             : launch_units_t<T, D, RT, 1, false>(a, what, s);
+    return a.prefetch ? launch_units_t<T, D, RT, 4, true>(a, what, s)
+                      : launch_units_t<T, D, RT, 4, false>(a, what, s);
+  } else {
+    switch (a.key_lanes * 2 + a.prefetch) {
+      case 2: return launch_units_t<T, D, RT, 1, false>(a, what, s);
+      case 3: return launch_units_t<T, D, RT, 1, true>(a, what, s);
+      case 8: return launch_units_t<T, D, RT, 4, false>(a, what, s);
+      case 9: return launch_units_t<T, D, RT, 4, true>(a, what, s);
+      case 16: return launch_units_t<T, D, RT, 8, false>(a, what, s);
+      default: return launch_units_t<T, D, RT, 8, true>(a, what, s);
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_units_d(const UnitArgs& a, int rt, int what, hipStream_t s) {
+  return rt == 1 ? launch_units_w<T, D, 1>(a, what, s) : launch_units_w<T, D, 2>(a, what, s);
+}
+
+hipError_t launch_attn_units(const UnitArgs& a, int ctx_rt, int what, int in_dtype, int head_dim,
+                             hipStream_t stream) {
+  if (a.key_lanes != 1 && a.key_lanes != 4 && a.key_lanes != 8) return hipErrorInvalidValue;
+  if (in_dtype == 1) {
+    return head_dim == 64 ? launch_units_d<bf16_t, 64>(a, ctx_rt, what, stream)
+                          : launch_units_d<bf16_t, 128>(a, ctx_rt, what, stream);
+  }
+  return head_dim == 64 ? launch_units_d<float, 64>(a, ctx_rt, what, stream)
+                        : launch_units_d<float, 128>(a, ctx_rt, what, stream);
+}
+
+}  // namespace relay

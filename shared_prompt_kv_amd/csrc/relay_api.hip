@@ -11,8 +11,6 @@
 
 namespace {
 
-using relay::CtxArgs;
-using relay::CtxConfig;
 using relay::FuseArgs;
 using relay::SysArgs;
 using relay::SysConfig;
@@ -45,11 +43,11 @@ int round_up32(long long x) { return (int)(((x + 31) / 32) * 32); }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Plan {
-  SysConfig sc;
+  int sys_mode = 0;  // 0: no system step, 1: single-wave units, 2: tiled kernel
+  SysConfig sc{};
   int sys_chunks = 0, sys_chunk_len = 0, sys_row_blocks = 0, sys_wgs = 0, xcd_remap = 0;
-  CtxConfig cc;
-  int ctx_split_len = 0, ctx_max_splits = 0, ctx_row_blocks = 0, ctx_wgs = 0;
-  int fuse_wgs = 0;
+  int ctx_rt = 1, ctx_split_len = 0, ctx_max_splits = 0, ctx_row_blocks = 0, ctx_wgs = 0;
+  int fuse_wgs = 0, launches = 0;
   size_t off_sys_o = 0, off_sys_lse = 0, off_ctx_o = 0, off_ctx_lse = 0, ws_bytes = 0;
 };
 
@@ -83,41 +81,51 @@ int check_dims(const relay_dims* d, int32_t sys_len) {
   return RELAY_OK;
 }
 
+int clamp_int(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
 void make_plan(const relay_dims* d, int32_t sys_len, Plan* p) {
   const int g = d->num_q_heads / d->num_kv_heads;
   const long long rows = (long long)d->total_q * d->num_q_heads;
   // ---- system step
   const int M = d->total_q * g;
-  p->sc = relay::sys_config(M);
-  const int rows_per_wg = p->sc.wr * p->sc.rt * 16;
-  p->sys_row_blocks = ceil_div(M, rows_per_wg);
   if (sys_len > 0) {
-    const int target = env_int("RELAY_SYS_TARGET_WGS", 2 * kNumCUs);
-    int chunk = env_int("RELAY_SYS_CHUNK", 0);
-    if (chunk <= 0) {
-      const long long per = (long long)sys_len * d->num_kv_heads * p->sys_row_blocks / target;
-      chunk = round_up32(per < 1 ? 1 : per);
-      const int min_chunk = 32 * p->sc.wk;
-      if (chunk < min_chunk) chunk = min_chunk;
+    if (M <= relay::kUnitMaxRows) {
+      p->sys_mode = 1;
+      const int chunk = round_up32(clamp_int(env_int("RELAY_SYS_CHUNK", 512), 32, 1 << 20));
+      p->sys_chunk_len = chunk;
+      p->sys_chunks = ceil_div(sys_len, chunk);
+      p->sys_row_blocks = ceil_div(M, 16);
+      const long long groups = (long long)d->num_kv_heads * p->sys_chunks;
+      p->sys_wgs = (int)(8LL * p->sys_row_blocks * ((groups + 7) / 8));
+    } else {
+      p->sys_mode = 2;
+      p->sc = relay::sys_config(M);
+      p->sys_row_blocks = ceil_div(M, p->sc.wr * p->sc.rt * 16);
+      const int target = env_int("RELAY_SYS_TARGET_WGS", 2 * kNumCUs);
+      int chunk = env_int("RELAY_SYS_CHUNK", 0);
+      if (chunk <= 0) {
+        const long long per = (long long)sys_len * d->num_kv_heads * p->sys_row_blocks / target;
+        chunk = round_up32(per < 1 ? 1 : per);
+        if (chunk < 32 * p->sc.wk) chunk = 32 * p->sc.wk;
+      }
+      p->sys_chunk_len = round_up32(chunk);
+      p->sys_chunks = ceil_div(sys_len, p->sys_chunk_len);
+      p->sys_wgs = p->sys_row_blocks * p->sys_chunks * d->num_kv_heads;
+      p->xcd_remap = (p->sys_row_blocks > 1 && p->sys_wgs % 8 == 0) ? 1 : 0;
     }
-    chunk = round_up32(chunk);
-    p->sys_chunk_len = chunk;
-    p->sys_chunks = ceil_div(sys_len, chunk);
-    p->sys_wgs = p->sys_row_blocks * p->sys_chunks * d->num_kv_heads;
-    p->xcd_remap = (p->sys_row_blocks > 1 && p->sys_wgs % 8 == 0) ? 1 : 0;
   }
   // ---- context step
   const int R = d->max_q_len * g;
-  p->cc = relay::ctx_config(R);
-  p->ctx_row_blocks = ceil_div(R, p->cc.wr * p->cc.rt * 16);
-  int split = env_int("RELAY_CTX_SPLIT", 0);
-  if (split <= 0) split = (R <= 16) ? 128 : 512;
-  split = round_up32(split);
-  p->ctx_split_len = split;
-  p->ctx_max_splits = ceil_div(d->max_ctx_len, split);
-  p->ctx_wgs = p->ctx_row_blocks * p->ctx_max_splits * d->num_kv_heads * d->batch;
+  p->ctx_rt = relay::ctx_rt_for(R);
+  p->ctx_row_blocks = ceil_div(R, 16 * p->ctx_rt);
+  const int split = env_int("RELAY_CTX_SPLIT", R <= 16 ? 256 : 512);
+  p->ctx_split_len = round_up32(clamp_int(split, 32, 1024));
+  p->ctx_max_splits = ceil_div(d->max_ctx_len, p->ctx_split_len);
+  const long long cgroups = (long long)p->ctx_max_splits * d->num_kv_heads * d->batch;
+  p->ctx_wgs = (int)(8LL * p->ctx_row_blocks * ((cgroups + 7) / 8));
   // ---- fusion
   p->fuse_wgs = ceil_div(rows, 1024 / d->head_dim);
+  p->launches = (p->sys_mode == 2 ? 3 : 2);
   // ---- workspace
   size_t off = 0;
   p->off_sys_o = off;
@@ -137,8 +145,8 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(RELAY_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-int launch_sys(const relay_dims* d, const Plan& p, const void* q, const void* sys_k,
-               const void* sys_v, int32_t sys_len, char* ws, hipStream_t s) {
+int launch_sys_tiled(const relay_dims* d, const Plan& p, const void* q, const void* sys_k,
+                     const void* sys_v, int32_t sys_len, char* ws, hipStream_t s) {
   if (!grid_ok(p.sys_wgs)) return fail(RELAY_ERR_INVALID, "system grid too large");
   SysArgs a;
   a.q = q;
@@ -155,36 +163,55 @@ int launch_sys(const relay_dims* d, const Plan& p, const void* q, const void* sy
   a.row_blocks = p.sys_row_blocks;
   a.xcd_remap = p.xcd_remap;
   a.scale_log2 = d->scale * kLog2e;
-  hipError_t e = relay::launch_sys_attn(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s);
-  return e == hipSuccess ? RELAY_OK : hip_fail(e, "sys_attn launch");
+  hipError_t e = relay::launch_sys_attn_tiled(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s);
+  return e == hipSuccess ? RELAY_OK : hip_fail(e, "sys_attn_tiled launch");
 }
 
-int launch_ctx(const relay_dims* d, const Plan& p, const void* q, const void* ck, const void* cv,
-               const int32_t* bt, const int32_t* cl, const int32_t* cu, char* ws, hipStream_t s) {
-  if (!grid_ok(p.ctx_wgs)) return fail(RELAY_ERR_INVALID, "context grid too large");
-  CtxArgs a;
+// Launches single-wave units: what = relay::kUnitsSys / kUnitsCtx / kUnitsBoth.
+int launch_units(const relay_dims* d, const Plan& p, int what, const void* q, const void* sys_k,
+                 const void* sys_v, int32_t sys_len, const void* ck, const void* cv, const int32_t* bt,
+                 const int32_t* cl, const int32_t* cu, char* ws, hipStream_t s) {
+  relay::UnitArgs a{};
   a.q = q;
-  a.ctx_k = ck;
-  a.ctx_v = cv;
-  a.block_tables = bt;
-  a.ctx_lens = cl;
-  a.cu_q_lens = cu;
-  a.o_part = reinterpret_cast<float*>(ws + p.off_ctx_o);
-  a.lse_part = reinterpret_cast<float*>(ws + p.off_ctx_lse);
-  a.batch = d->batch;
   a.total_q = d->total_q;
   a.num_q_heads = d->num_q_heads;
   a.num_kv_heads = d->num_kv_heads;
   a.group = d->num_q_heads / d->num_kv_heads;
-  a.num_blocks = d->num_blocks;
-  a.max_blocks_per_seq = d->max_blocks_per_seq;
-  a.max_ctx_len = d->max_ctx_len;
-  a.split_len = p.ctx_split_len;
-  a.max_splits = p.ctx_max_splits;
-  a.row_blocks = p.ctx_row_blocks;
   a.scale_log2 = d->scale * kLog2e;
-  hipError_t e = relay::launch_ctx_attn(a, p.cc, d->in_dtype, d->head_dim, p.ctx_wgs, s);
-  return e == hipSuccess ? RELAY_OK : hip_fail(e, "ctx_attn launch");
+  a.prefetch = env_int("RELAY_PREFETCH", 1) == 1 ? 1 : 0;
+  a.key_lanes = env_int("RELAY_KEY_LANES", 4);
+  a.grid = env_int("RELAY_GRID", 0);
+  if (what & relay::kUnitsSys) {
+    a.sys_k = sys_k;
+    a.sys_v = sys_v;
+    a.sys_o = reinterpret_cast<float*>(ws + p.off_sys_o);
+    a.sys_lse = reinterpret_cast<float*>(ws + p.off_sys_lse);
+    a.sys_len = sys_len;
+    a.sys_chunk_len = p.sys_chunk_len;
+    a.sys_chunks = p.sys_chunks;
+    a.sys_row_tiles = p.sys_row_blocks;
+    a.n_sys_units = p.sys_wgs;
+  }
+  if (what & relay::kUnitsCtx) {
+    a.ctx_k = ck;
+    a.ctx_v = cv;
+    a.block_tables = bt;
+    a.ctx_lens = cl;
+    a.cu_q_lens = cu;
+    a.ctx_o = reinterpret_cast<float*>(ws + p.off_ctx_o);
+    a.ctx_lse = reinterpret_cast<float*>(ws + p.off_ctx_lse);
+    a.batch = d->batch;
+    a.num_blocks = d->num_blocks;
+    a.max_blocks_per_seq = d->max_blocks_per_seq;
+    a.max_ctx_len = d->max_ctx_len;
+    a.ctx_split_len = p.ctx_split_len;
+    a.ctx_max_splits = p.ctx_max_splits;
+    a.ctx_row_blocks = p.ctx_row_blocks;
+    a.n_ctx_units = p.ctx_wgs;
+  }
+  if (!grid_ok((long long)a.n_sys_units + a.n_ctx_units)) return fail(RELAY_ERR_INVALID, "grid too large");
+  hipError_t e = relay::launch_attn_units(a, p.ctx_rt, what, d->in_dtype, d->head_dim, s);
+  return e == hipSuccess ? RELAY_OK : hip_fail(e, "attention units launch");
 }
 
 int launch_fuse(FuseArgs& a, int head_dim, hipStream_t s) {
@@ -258,6 +285,8 @@ int relay_get_plan(const relay_dims* dims, int32_t sys_len, relay_plan* out) {
   out->ctx_row_blocks = p.ctx_row_blocks;
   out->ctx_wgs = p.ctx_wgs;
   out->fuse_wgs = p.fuse_wgs;
+  out->sys_mode = p.sys_mode;
+  out->launches = p.launches;
   return RELAY_OK;
 }
 
@@ -281,26 +310,27 @@ static int decode_impl(const relay_dims* dims, const void* q, const void* sys_k,
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if ((rc = record(events, 0, s)) != RELAY_OK) return rc;
-  if (sys_len > 0 && (rc = launch_sys(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
+  int units = relay::kUnitsCtx;
+  if (p.sys_mode == 2) {
+    if ((rc = launch_sys_tiled(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
+  } else if (p.sys_mode == 1) {
+    units = relay::kUnitsBoth;  // both steps in one launch
+  }
   if ((rc = record(events, 1, s)) != RELAY_OK) return rc;
-  if ((rc = launch_ctx(dims, p, q, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens, ws, s)) != RELAY_OK)
+  if ((rc = launch_units(dims, p, units, q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables,
+                         ctx_lens, cu_q_lens, ws, s)) != RELAY_OK)
     return rc;
   if ((rc = record(events, 2, s)) != RELAY_OK) return rc;
   FuseArgs f{};
   f.a_o = reinterpret_cast<const float*>(ws + p.off_sys_o);
   f.a_lse = reinterpret_cast<const float*>(ws + p.off_sys_lse);
-  f.a_count = sys_len > 0 ? p.sys_chunks : 0;
+  f.a_count = p.sys_chunks;
   f.b_o = reinterpret_cast<const float*>(ws + p.off_ctx_o);
   f.b_lse = reinterpret_cast<const float*>(ws + p.off_ctx_lse);
   f.b_count = p.ctx_max_splits;
-  f.b_split_len = p.ctx_split_len;
-  f.ctx_lens = ctx_lens;
-  f.cu_q_lens = cu_q_lens;
   f.out = out;
   f.lse_out = nullptr;
   f.n_rows = (long long)dims->total_q * dims->num_q_heads;
-  f.num_q_heads = dims->num_q_heads;
-  f.batch = dims->batch;
   f.out_bf16 = dims->out_dtype == RELAY_BF16;
   if ((rc = launch_fuse(f, dims->head_dim, s)) != RELAY_OK) return rc;
   return record(events, 3, s);
@@ -342,16 +372,17 @@ int relay_sys_attn(const relay_dims* dims, const void* q, const void* sys_k, con
   if ((rc = check_ws(p, workspace, workspace_bytes)) != RELAY_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  if (sys_len > 0 && (rc = launch_sys(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
+  if (p.sys_mode == 2 && (rc = launch_sys_tiled(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
+  if (p.sys_mode == 1 && (rc = launch_units(dims, p, relay::kUnitsSys, q, sys_k, sys_v, sys_len, nullptr, nullptr,
+                                            nullptr, nullptr, nullptr, ws, s)) != RELAY_OK)
+    return rc;
   FuseArgs f{};
   f.a_o = reinterpret_cast<const float*>(ws + p.off_sys_o);
   f.a_lse = reinterpret_cast<const float*>(ws + p.off_sys_lse);
-  f.a_count = sys_len > 0 ? p.sys_chunks : 0;
+  f.a_count = p.sys_chunks;
   f.out = o_sys;
   f.lse_out = lse_sys;
   f.n_rows = (long long)dims->total_q * dims->num_q_heads;
-  f.num_q_heads = dims->num_q_heads;
-  f.batch = dims->batch;
   return launch_fuse(f, dims->head_dim, s);
 }
 
@@ -371,20 +402,16 @@ int relay_ctx_attn(const relay_dims* dims, const void* q, const void* ctx_k_page
   if ((rc = check_ws(p, workspace, workspace_bytes)) != RELAY_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  if ((rc = launch_ctx(dims, p, q, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens, ws, s)) != RELAY_OK)
+  if ((rc = launch_units(dims, p, relay::kUnitsCtx, q, nullptr, nullptr, 0, ctx_k_pages, ctx_v_pages,
+                         block_tables, ctx_lens, cu_q_lens, ws, s)) != RELAY_OK)
     return rc;
   FuseArgs f{};
   f.b_o = reinterpret_cast<const float*>(ws + p.off_ctx_o);
   f.b_lse = reinterpret_cast<const float*>(ws + p.off_ctx_lse);
   f.b_count = p.ctx_max_splits;
-  f.b_split_len = p.ctx_split_len;
-  f.ctx_lens = ctx_lens;
-  f.cu_q_lens = cu_q_lens;
   f.out = o_ctx;
   f.lse_out = lse_ctx;
   f.n_rows = (long long)dims->total_q * dims->num_q_heads;
-  f.num_q_heads = dims->num_q_heads;
-  f.batch = dims->batch;
   return launch_fuse(f, dims->head_dim, s);
 }
 
@@ -407,12 +434,9 @@ int relay_fuse(int64_t n_rows, int32_t head_dim, const float* o_sys, const float
   f.b_o = o_ctx;
   f.b_lse = lse_ctx;
   f.b_count = 1;
-  f.b_split_len = 0;
   f.out = out;
   f.lse_out = lse_out;
   f.n_rows = n_rows;
-  f.num_q_heads = 1;
-  f.batch = 1;
   f.out_bf16 = out_dtype == RELAY_BF16;
   return launch_fuse(f, head_dim, static_cast<hipStream_t>(stream));
 }

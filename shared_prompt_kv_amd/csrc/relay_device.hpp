@@ -58,16 +58,31 @@ __device__ inline float neg_inf() { return -__builtin_inff(); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ inline float xor_max(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, kWave));
+// The values of lanes l and l^32 (permlane32 swap) and of l and l^16 (permlane16
+// swap), exchanged in VALU without going through LDS (gfx950).
+__device__ inline void swap32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ inline void swap16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
 }
 
 // Max / sum over the four lane groups (lanes l, l^16, l^32, l^48) that hold the same row.
-__device__ inline float row_max4(float v) { return xor_max(xor_max(v, 16), 32); }
+__device__ inline float row_max4(float v) {
+  float a, b;
+  swap32(v, a, b);
+  swap16(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
 __device__ inline float row_sum4(float v) {
-  v += __shfl_xor(v, 16, kWave);
-  v += __shfl_xor(v, 32, kWave);
-  return v;
+  float a, b;
+  swap32(v, a, b);
+  swap16(a + b, a, b);
+  return a + b;
 }
 
 // ---- matrix-core primitives ---------------------------------------------------------
@@ -207,20 +222,20 @@ struct RowState {
   }
 };
 
-// Folds 8 scores (log2 domain, -inf = masked) into the state and returns their
+// Folds N scores (log2 domain, -inf = masked) into the state and returns their
 // probabilities relative to the new running max.
-template <int D>
-__device__ inline void softmax_step(RowState<D>& st, float (&s)[8]) {
+template <int D, int N>
+__device__ inline void softmax_step(RowState<D>& st, float (&s)[N]) {
   float mx = s[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+  for (int i = 1; i < N; ++i) mx = fmaxf(mx, s[i]);
   mx = row_max4(mx);
   const float m_new = fmaxf(st.m, mx);
   const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
   const float alpha = fast_exp2(st.m - m_use);
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < N; ++i) {
     s[i] = fast_exp2(s[i] - m_use);
     sum += s[i];
   }
@@ -243,6 +258,49 @@ __device__ inline void merge_state(RowState<D>& a, float mb, float lb, const f32
   a.m = m_new;
 }
 
+// Floats of LDS one wave's RT row states occupy in a key-lane merge.
+template <int D, int RT>
+constexpr int kMergeSlot = kWave * RT * (2 + D / 4);
+
+// Merges the row states of WK waves (key lanes kl = 0..WK-1) that processed
+// disjoint keys of the same rows, in a fixed tree order (deterministic); key lane 0
+// ends with the merged state.  lds: (WK/2) * kMergeSlot<D, RT> floats for this group
+// of waves.  Every wave of the workgroup must call it (it holds barriers).
+template <int D, int RT, int WK>
+__device__ inline void merge_key_lanes(RowState<D> (&st)[RT], int kl, float* lds) {
+  if constexpr (WK > 1) {
+    const int lane = lane_id();
+    for (int half = WK / 2; half >= 1; half /= 2) {
+      __syncthreads();
+      if (kl >= half && kl < 2 * half) {
+        float* slot = lds + (size_t)(kl - half) * kMergeSlot<D, RT>;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          float* p = slot + rt * kWave * (2 + D / 4);
+          p[lane] = st[rt].m;
+          p[kWave + lane] = st[rt].l;
+#pragma unroll
+          for (int t = 0; t < D / 16; ++t)
+            *reinterpret_cast<f32x4*>(p + 2 * kWave + (t * kWave + lane) * 4) = st[rt].o[t];
+        }
+      }
+      __syncthreads();
+      if (kl < half) {
+        const float* slot = lds + (size_t)kl * kMergeSlot<D, RT>;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const float* p = slot + rt * kWave * (2 + D / 4);
+          f32x4 ob[D / 16];
+#pragma unroll
+          for (int t = 0; t < D / 16; ++t)
+            ob[t] = *reinterpret_cast<const f32x4*>(p + 2 * kWave + (t * kWave + lane) * 4);
+          merge_state(st[rt], p[lane], p[kWave + lane], ob);
+        }
+      }
+    }
+  }
+}
+
 // Writes a finished row tile: O = acc / l (0 when the row saw no key) and the
 // natural-log LSE (-inf when empty).  o_row: this lane's row, or nullptr when the
 // row is padding.
@@ -259,6 +317,130 @@ __device__ inline void store_row_tile(const RowState<D>& st, float* o_row, float
     *reinterpret_cast<f32x4*>(o_row + 16 * t + 4 * q) = v;
   }
   if (q == 0) *lse_row = empty ? neg_inf() : (st.m + __builtin_amdgcn_logf(l)) * kLn2;
+}
+
+// ---- one 16-key step of the streaming units ------------------------------------------
+//
+// A step is one 16-key block (a context page, or a 16-key system tile) with a
+// wave-uniform base address.  The score tile S^T = K Q^T gives lane group q the
+// scores of keys 4q..4q+3, which are its reduction slice in O^T = V^T P^T
+// (v_mfma_f32_16x16x16_bf16: 4 keys per lane group); V^T for them is 4 contiguous
+// keys of the block's dimension-major tile.
+
+// V^T[dim][4q..4q+3] of one block.
+template <typename T> struct VFrag4;
+template <> struct VFrag4<bf16_t> {
+  uint2 c;  // 4 bf16
+};
+template <> struct VFrag4<float> {
+  u32x4 c;  // 4 fp32
+};
+
+template <typename T, int D>
+struct PageFrag {
+  static constexpr int NCH = D * Elem<T>::kBytes / 64;
+  u32x4 k[NCH];          // this lane's K row, 16 bytes at 64*kk + 16*(l/16)
+  VFrag4<T> v[D / 16];   // V^T fragments, one per 16-dimension output tile
+};
+
+__device__ inline void load_v4(VFrag4<bf16_t>& f, const char* p) { f.c = *reinterpret_cast<const uint2*>(p); }
+__device__ inline void load_v4(VFrag4<float>& f, const char* p) { f.c = ld16(p); }
+
+// Zeroes the value elements of keys that do not exist (the first n of the four exist).
+__device__ inline void mask_v4(VFrag4<bf16_t>& f, int n) {
+  f.c.x = keep_bf16_pair(f.c.x, 0, n);
+  f.c.y = keep_bf16_pair(f.c.y, 2, n);
+}
+__device__ inline void mask_v4(VFrag4<float>& f, int n) {
+  f.c.x = 0 < n ? f.c.x : 0u;
+  f.c.y = 1 < n ? f.c.y : 0u;
+  f.c.z = 2 < n ? f.c.z : 0u;
+  f.c.w = 3 < n ? f.c.w : 0u;
+}
+
+// P for this lane's row and the lane group's 4 keys, as the output product's B operand.
+template <typename T> struct PFrag4;
+template <> struct PFrag4<bf16_t> {
+  uint2 c, lo;  // bf16 P and its rounding residual
+};
+template <> struct PFrag4<float> {
+  float p[4];
+};
+
+template <bool SPLIT>
+__device__ inline void make_p4(PFrag4<bf16_t>& f, const float (&p)[4]) {
+  f.c.x = pack_bf16x2(p[0], p[1]);
+  f.c.y = pack_bf16x2(p[2], p[3]);
+  if constexpr (SPLIT) {
+    f.lo.x = pack_bf16x2(p[0] - bf16_lo_as_float(f.c.x), p[1] - bf16_hi_as_float(f.c.x));
+    f.lo.y = pack_bf16x2(p[2] - bf16_lo_as_float(f.c.y), p[3] - bf16_hi_as_float(f.c.y));
+  }
+}
+template <bool SPLIT>
+__device__ inline void make_p4(PFrag4<float>& f, const float (&p)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.p[i] = p[i];
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <bool SPLIT>
+__device__ inline void mfma_pv4(f32x4& acc, const VFrag4<bf16_t>& v, const PFrag4<bf16_t>& p) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v.c), __builtin_bit_cast(s16x4, p.c),
+                                                  acc, 0, 0, 0);
+  if constexpr (SPLIT)
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v.c),
+                                                    __builtin_bit_cast(s16x4, p.lo), acc, 0, 0, 0);
+}
+template <bool SPLIT>
+__device__ inline void mfma_pv4(f32x4& acc, const VFrag4<float>& v, const PFrag4<float>& p) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c.x), p.p[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c.y), p.p[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c.z), p.p[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c.w), p.p[3], acc, 0, 0, 0);
+}
+
+// Issues the loads of one block.  kp: base of its 16 K rows; vp: base of its
+// dimension-major V^T tile; krow: the K row this lane reads (its A-operand row,
+// clamped where the block is short).
+template <typename T, int D>
+__device__ inline void load_page(PageFrag<T, D>& f, const char* kp, const char* vp, int krow) {
+  constexpr int E = Elem<T>::kBytes;
+  const int q4 = lane_id() >> 4, r16 = lane_id() & 15;
+  const char* kr = kp + krow * D * E + 16 * q4;
+#pragma unroll
+  for (int kk = 0; kk < PageFrag<T, D>::NCH; ++kk) f.k[kk] = ld16(kr + 64 * kk);
+  const char* vr = vp + r16 * kTile * E + 4 * q4 * E;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) load_v4(f.v[t], vr + 16 * t * kTile * E);
+}
+
+// Folds one loaded block into the row states.  keyq: index of this lane group's
+// first key (keys keyq..keyq+3); kv_len: keys that exist (values of the others are
+// zeroed); last[rt]: last key index the rows of tile rt may see (causal bound; -1
+// sees nothing).  PSPLIT: bf16 P as hi + lo.
+template <typename T, int D, int RT, bool PSPLIT>
+__device__ inline void compute_page(PageFrag<T, D>& f, const u32x4 (&qf)[RT][PageFrag<T, D>::NCH],
+                                    RowState<D> (&st)[RT], int keyq, int kv_len, const int (&last)[RT],
+                                    float scale_log2) {
+  if (keyq + 4 > kv_len) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) mask_v4(f.v[t], kv_len - keyq);
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < PageFrag<T, D>::NCH; ++kk) mfma_chunk(sa, f.k[kk], qf[rt][kk], T{});
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = (keyq + i <= last[rt]) ? sa[i] * scale_log2 : neg_inf();
+    softmax_step(st[rt], sc);
+    PFrag4<T> pf;
+    make_p4<PSPLIT>(pf, sc);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) mfma_pv4<PSPLIT>(st[rt].o[t], f.v[t], pf);
+  }
 }
 
 }  // namespace relay

@@ -10,7 +10,8 @@
 // pass: one read of every partial row, one write of the output.
 //
 // Layout: D/4 lanes per row, each owning four consecutive dimensions (one 16-byte
-// load per partial); 256 threads per workgroup.  HBM-bound.
+// load per partial); 256 threads per workgroup.  HBM-bound; the loads of a row's
+// partials are issued in batches of four so a row costs few memory latencies.
 #include "relay_device.hpp"
 #include "relay_internal.hpp"
 
@@ -24,41 +25,45 @@ __global__ __launch_bounds__(256) void relay_fuse_kernel(FuseArgs a) {
   if (row >= a.n_rows) return;
   const int c4 = threadIdx.x % LPR;
 
-  int nb = a.b_count;
-  if (a.b_split_len > 0) {
-    const int t = (int)(row / a.num_q_heads);
-    int b = t;
-    if (a.cu_q_lens) {  // last request whose first token is <= t
-      int lo = 0, hi = a.batch - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (a.cu_q_lens[mid] <= t) lo = mid;
-        else hi = mid - 1;
-      }
-      b = lo;
-    }
-    const int c = max(a.ctx_lens[b], 0);
-    nb = min((c + a.b_split_len - 1) / a.b_split_len, a.b_count);
-  }
-
+  // partial i < a_count is system chunk i, the rest are context splits
+  const int n = a.a_count + a.b_count;
+  auto lse_at = [&](int i) -> const float* {
+    return i < a.a_count ? a.a_lse + (size_t)i * a.n_rows + row
+                         : a.b_lse + (size_t)(i - a.a_count) * a.n_rows + row;
+  };
+  auto o_at = [&](int i) -> const f32x4* {
+    const float* base = i < a.a_count ? a.a_o + ((size_t)i * a.n_rows + row) * D
+                                      : a.b_o + ((size_t)(i - a.a_count) * a.n_rows + row) * D;
+    return reinterpret_cast<const f32x4*>(base + 4 * c4);
+  };
+  // Batches of 4 partials: all loads of a batch are issued before any is used.
   float m = neg_inf();
-  for (int i = 0; i < a.a_count; ++i) m = fmaxf(m, a.a_lse[(size_t)i * a.n_rows + row]);
-  for (int i = 0; i < nb; ++i) m = fmaxf(m, a.b_lse[(size_t)i * a.n_rows + row]);
-
+  for (int i0 = 0; i0 < n; i0 += 4) {
+    float l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) l[j] = (i0 + j < n) ? *lse_at(i0 + j) : neg_inf();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = fmaxf(m, l[j]);
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float z = 0.f;
   if (m != neg_inf()) {
-    for (int i = 0; i < a.a_count; ++i) {
-      const size_t r = (size_t)i * a.n_rows + row;
-      const float w = fast_exp2((a.a_lse[r] - m) * kLog2e);
-      z += w;
-      acc += w * *reinterpret_cast<const f32x4*>(a.a_o + r * D + 4 * c4);
-    }
-    for (int i = 0; i < nb; ++i) {
-      const size_t r = (size_t)i * a.n_rows + row;
-      const float w = fast_exp2((a.b_lse[r] - m) * kLog2e);
-      z += w;
-      acc += w * *reinterpret_cast<const f32x4*>(a.b_o + r * D + 4 * c4);
+    for (int i0 = 0; i0 < n; i0 += 4) {
+      float l[4];
+      f32x4 o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = i0 + j < n;
+        l[j] = ok ? *lse_at(i0 + j) : neg_inf();
+        o[j] = ok ? *o_at(i0 + j) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool live = l[j] != neg_inf();  // an empty partial's O may be unwritten
+        const float w = live ? fast_exp2((l[j] - m) * kLog2e) : 0.f;
+        z += w;
+        acc += w * (live ? o[j] : f32x4{0.f, 0.f, 0.f, 0.f});
+      }
     }
     acc *= 1.f / z;
   }

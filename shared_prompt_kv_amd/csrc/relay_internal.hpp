@@ -7,7 +7,7 @@
 
 namespace relay {
 
-// sys_attn: one launch over (row block, chunk, KV head) workgroups.
+// sys_attn_tiled (large M): one launch over (row block, chunk, KV head) workgroups.
 struct SysArgs {
   const void* q;        // [T_q, H_q, d]
   const void* sys_k;    // [H_kv, L_s, d]
@@ -31,7 +31,11 @@ struct SysConfig {
   int rt, wk, wr;
 };
 
-// The configuration used for M = T_q * g stacked query rows per KV head.
+// Up to this many stacked query rows per KV head the system step runs as
+// single-wave units (HBM-bound); above it as the tiled kernel (matrix-core-bound).
+constexpr int kUnitMaxRows = 64;
+
+// The tiled configuration used for M = T_q * g stacked query rows per KV head.
 inline SysConfig sys_config(int M) {
   if (M <= 16) return {1, 8, 1};
   if (M <= 32) return {2, 4, 1};
@@ -39,69 +43,73 @@ inline SysConfig sys_config(int M) {
   return {2, 1, 4};
 }
 
-// ctx_attn: one launch over (row block, split, KV head, request) workgroups.
-struct CtxArgs {
-  const void* q;             // [T_q, H_q, d]
-  const void* ctx_k;         // [num_blocks, H_kv, 16, d]
-  const void* ctx_v;         // [num_blocks, H_kv, d, 16]
-  const int32_t* block_tables;
-  const int32_t* ctx_lens;
-  const int32_t* cu_q_lens;  // NULL: one query per request
-  float* o_part;             // [max_splits, T_q, H_q, d]
-  float* lse_part;           // [max_splits, T_q, H_q]
-  int batch;
+// Single-wavefront units (attn_units.hip): system units over 16-row tiles and
+// context units, launched alone or together.
+struct UnitArgs {
+  const void* q;       // [T_q, H_q, d]
   int total_q;
   int num_q_heads;
   int num_kv_heads;
   int group;
+  float scale_log2;
+  // system units: n_sys_units = 8 * sys_row_tiles * ceil(H_kv * sys_chunks / 8), or 0
+  const void* sys_k;   // [H_kv, L_s, d]
+  const void* sys_v;   // [H_kv, ceil(L_s/16), d, 16]
+  float* sys_o;        // [sys_chunks, T_q, H_q, d]
+  float* sys_lse;      // [sys_chunks, T_q, H_q]
+  int sys_len;
+  int sys_chunk_len;   // multiple of 32
+  int sys_chunks;
+  int sys_row_tiles;   // ceil(T_q * g / 16)
+  int n_sys_units;
+  // context units: n_ctx_units = 8 * ctx_row_blocks * ceil(max_splits * H_kv * B / 8), or 0
+  const void* ctx_k;   // [num_blocks, H_kv, 16, d]
+  const void* ctx_v;   // [num_blocks, H_kv, d, 16]
+  const int32_t* block_tables;
+  const int32_t* ctx_lens;
+  const int32_t* cu_q_lens;  // NULL: one query per request
+  float* ctx_o;        // [max_splits, T_q, H_q, d]
+  float* ctx_lse;      // [max_splits, T_q, H_q]
+  int batch;
   int num_blocks;
   int max_blocks_per_seq;
-  int max_ctx_len;           // clamp for c_b (keeps splits inside the workspace)
-  int split_len;             // keys per split, multiple of 32
-  int max_splits;
-  int row_blocks;            // ceil(max_q_len * g / rows per workgroup)
-  float scale_log2;
+  int max_ctx_len;     // clamp for c_b (keeps splits inside the workspace)
+  int ctx_split_len;   // multiple of 32, at most 1024
+  int ctx_max_splits;
+  int ctx_row_blocks;  // ceil(max_q_len * g / (16 * ctx_rt))
+  int n_ctx_units;
+  int key_lanes;       // waves per unit: 1, 4 or 8 (two row tiles: at most 4)
+  int prefetch;        // 1: double-buffered steps
+  int grid;            // > 0: workgroups of the persistent launch; 0: as many as fit
 };
 
-struct CtxConfig {
-  int rt, wr;  // row tiles per wave, waves (row groups) per workgroup
-};
+constexpr int kUnitsSys = 1, kUnitsCtx = 2, kUnitsBoth = 3;
 
-inline CtxConfig ctx_config(int rows_per_request) {
-  if (rows_per_request <= 16) return {1, 1};
-  if (rows_per_request <= 32) return {2, 1};
-  if (rows_per_request <= 64) return {2, 2};
-  return {2, 4};
-}
+// Row tiles per context unit for up to R query rows per request.
+inline int ctx_rt_for(int rows_per_request) { return rows_per_request <= 16 ? 1 : 2; }
 
-// relay_fuse: LSE-weighted merge of two groups of partials per row.
-//   group A (system): a_count partials, partial i of row r at a_o[i*rows + r].
-//   group B (context): per-request count ceil(c_b / b_split_len) (capped at
-//   b_count) when b_split_len > 0, else b_count.
+// relay_fuse: LSE-weighted merge of two groups of partials per row: group A
+// (system chunks) a_count partials, partial i of row r at a_o[i*rows + r]; group B
+// (context splits) likewise with b_count.  A partial with LSE = -inf is empty: its
+// weight is 0 and its O is never used (it may be unwritten).
 struct FuseArgs {
   const float* a_o;
   const float* a_lse;
   const float* b_o;
   const float* b_lse;
-  const int32_t* ctx_lens;
-  const int32_t* cu_q_lens;
   void* out;
   float* lse_out;  // may be NULL
   long long n_rows;
-  int num_q_heads;
-  int batch;
   int a_count;
   int b_count;
-  int b_split_len;
   int out_bf16;
 };
 
-hipError_t launch_sys_attn(const SysArgs& a, const SysConfig& c, int in_dtype, int head_dim,
-                           int nwg, hipStream_t stream);
-hipError_t launch_ctx_attn(const CtxArgs& a, const CtxConfig& c, int in_dtype, int head_dim,
-                           int nwg, hipStream_t stream);
+hipError_t launch_sys_attn_tiled(const SysArgs& a, const SysConfig& c, int in_dtype, int head_dim,
+                                 int nwg, hipStream_t stream);
+hipError_t launch_attn_units(const UnitArgs& a, int ctx_rt, int what, int in_dtype, int head_dim,
+                             hipStream_t stream);
 hipError_t launch_relay_fuse(const FuseArgs& a, int head_dim, int nwg, hipStream_t stream);
 
-constexpr int kFuseRowsPerWg = 8;  // 256 threads, 32 lanes per row at d = 128
 
 }  // namespace relay

@@ -1,4 +1,5 @@
-// sys_attn: RelayAttention's system-attention step on gfx950.
+// sys_attn_tiled: RelayAttention's system-attention step on gfx950 for many stacked
+// query rows (matrix-core-bound: large batch x GQA group).
 //
 // Every query row of the batch attends to the shared system KV cache alone
 // (RelayAttention paper, abstract; atyun.com article, section "RelayAttention": the
@@ -22,7 +23,7 @@
 namespace relay {
 
 template <typename T, int D, int RT, int WK, int WR, bool PSPLIT>
-__global__ __launch_bounds__(kWave* WK* WR) void sys_attn_kernel(SysArgs a) {
+__global__ __launch_bounds__(kWave* WK* WR) void sys_attn_tiled_kernel(SysArgs a) {
   constexpr int NCH = D * Elem<T>::kBytes / 64;  // 16-byte chunks per lane per row
   constexpr int E = Elem<T>::kBytes;
   const int lane = lane_id();
@@ -179,7 +180,7 @@ template <typename T, int D, int RT, int WK, int WR, bool PSPLIT>
 static hipError_t launch_sys_t(const SysArgs& a, int nwg, hipStream_t stream) {
   constexpr size_t lds = (WK > 1) ? sizeof(float) * (size_t)WR * (WK / 2) * kWave * RT * (2 + D / 4) : 0;
   static_assert(lds <= 64 * 1024, "LDS budget");
-  hipLaunchKernelGGL((sys_attn_kernel<T, D, RT, WK, WR, PSPLIT>), dim3(nwg), dim3(kWave * WK * WR), lds,
+  hipLaunchKernelGGL((sys_attn_tiled_kernel<T, D, RT, WK, WR, PSPLIT>), dim3(nwg), dim3(kWave * WK * WR), lds,
                      stream, a);
   return hipGetLastError();
 }
@@ -198,7 +199,7 @@ static hipError_t launch_sys_d(const SysArgs& a, const SysConfig& c, int nwg, hi
   return launch_sys_t<T, D, 2, 1, 4, false>(a, nwg, s);
 }
 
-hipError_t launch_sys_attn(const SysArgs& a, const SysConfig& c, int in_dtype, int head_dim,
+hipError_t launch_sys_attn_tiled(const SysArgs& a, const SysConfig& c, int in_dtype, int head_dim,
                            int nwg, hipStream_t stream) {
   if (in_dtype == 1) {
     return head_dim == 64 ? launch_sys_d<bf16_t, 64>(a, c, nwg, stream)

@@ -42,7 +42,7 @@ class relay_dims(ctypes.Structure):
 class relay_plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "sys_chunks", "sys_chunk_len", "sys_row_blocks", "sys_wgs", "ctx_split_len",
-        "ctx_max_splits", "ctx_row_blocks", "ctx_wgs", "fuse_wgs")]
+        "ctx_max_splits", "ctx_row_blocks", "ctx_wgs", "fuse_wgs", "sys_mode", "launches")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -114,6 +114,9 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 
 def _stream(stream) -> ctypes.c_void_p:
+    """hipStream_t of a torch stream, a raw handle (int), or the current stream."""
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
 
@@ -163,7 +166,7 @@ def relay_get_plan(dims: relay_dims, sys_len: int) -> dict:
 
 def workspace(dims: relay_dims, sys_len: int, device) -> torch.Tensor:
     n = max(relay_workspace_size(dims, sys_len), 256)
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def relay_attn_decode(q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens,
@@ -286,6 +289,48 @@ def decode_workload(t: dict, out_dtype=torch.float32, workspace_buf=None, stream
                              t["ctx_v_pages"], t["block_tables"], t["ctx_lens"], t["cu_q_lens"], out,
                              scale=t["scale"], max_ctx_len=t["max_ctx_len"], max_q_len=t["max_q_len"],
                              out_dtype=out_dtype, workspace_buf=workspace_buf, stream=stream)
+
+
+class DecodeCall:
+    """A relay_attn_decode call with its arguments marshalled once.
+
+    Checks and converts every argument at construction; calling it is one ctypes
+    call (on ``stream``, or on the stream current at call time when stream is None),
+    cheap enough that the host keeps ahead of the GPU and usable inside HIP graph
+    capture.  The tensors must stay alive and unmoved while the object is used.
+    """
+
+    def __init__(self, t: dict, out: torch.Tensor, workspace_buf: torch.Tensor, out_dtype=torch.float32,
+                 timed_events=None):
+        _require_device(t["q"], t["sys_k"], t["sys_v"], t["ctx_k_pages"], t["ctx_v_pages"],
+                        t["block_tables"], t["ctx_lens"], t["cu_q_lens"], out, workspace_buf)
+        self.dims = dims_of(t, out_dtype)
+        need = relay_workspace_size(self.dims, t["sys_len"])
+        if workspace_buf.numel() < need:
+            raise ValueError(f"workspace has {workspace_buf.numel()} bytes, needs {need}")
+        lib = load_library()
+        self._keep = (t, out, workspace_buf)
+        self._args = [ctypes.byref(self.dims), _ptr(t["q"]), _ptr(t["sys_k"]), _ptr(t["sys_v"]),
+                      int(t["sys_len"]), _ptr(t["ctx_k_pages"]), _ptr(t["ctx_v_pages"]),
+                      _ptr(t["block_tables"]), _ptr(t["ctx_lens"]), _ptr(t["cu_q_lens"]), _ptr(out),
+                      _ptr(workspace_buf), workspace_buf.numel()]
+        self._fn = lib.relay_attn_decode
+        self._timed = lib.relay_attn_decode_timed
+        self.out = out
+
+    def __call__(self, stream=None):
+        rc = self._fn(*self._args, _stream(stream))
+        if rc != RELAY_OK:
+            _check(rc)
+        return self.out
+
+    def timed(self, events, stream=None):
+        """The same call, recording 4 raw hipEvent_t handles between the kernels."""
+        ev = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) if e else None for e in events])
+        rc = self._timed(*self._args, _stream(stream), ev)
+        if rc != RELAY_OK:
+            _check(rc)
+        return self.out
 
 
 def dims_of(t: dict, out_dtype=torch.float32) -> relay_dims:

@@ -131,8 +131,16 @@ def test_plan_for_each_config(lib, cfg, sweep):
     assert plan["sys_chunks"] * plan["sys_chunk_len"] >= spec.sys_len
     assert (plan["sys_chunks"] - 1) * plan["sys_chunk_len"] < spec.sys_len
     M = s["total_q"] * spec.group
-    assert plan["sys_wgs"] == plan["sys_row_blocks"] * plan["sys_chunks"] * spec.num_kv_heads
-    assert plan["sys_row_blocks"] * 16 >= M or plan["sys_row_blocks"] * 128 >= M
+    if M <= 64:   # single-wave system units, launched together with the context units
+        assert plan["sys_mode"] == 1 and plan["launches"] == 2
+        assert plan["sys_row_blocks"] == -(-M // 16)
+        groups = spec.num_kv_heads * plan["sys_chunks"]
+        assert plan["sys_wgs"] == 8 * plan["sys_row_blocks"] * (-(-groups // 8))
+    else:         # tiled system kernel
+        assert plan["sys_mode"] == 2 and plan["launches"] == 3
+        assert plan["sys_wgs"] == plan["sys_row_blocks"] * plan["sys_chunks"] * spec.num_kv_heads
+        assert plan["sys_row_blocks"] * 128 >= M
+    assert plan["ctx_split_len"] <= 1024
     assert 0 < plan["ctx_wgs"] < 2**31 and 0 < plan["sys_wgs"] < 2**31
 
 

@@ -255,3 +255,35 @@ def test_decode_matches_oracle_full_size(cfg, sweep, n_rows):
         check(out[rows], ref, spec.dtype, "out")
     del t
     torch.cuda.empty_cache()
+
+
+def test_graph_replay_matches_eager():
+    """The decode call captured in a HIP graph: every replay (with eager work and
+    synchronisations between replays) equals the eager result bitwise."""
+    spec = W.config_spec(2).replace(batch=6, sys_len=300, ctx_lo=16, ctx_hi=140)
+    say(f"[parity] graph replay {spec}")
+    w = workload(spec)
+    t = upload(w)
+    dims = R.dims_of(t)
+    ws = R.workspace(dims, t["sys_len"], "cuda")
+    ref = R.decode_workload(t, workspace_buf=ws).clone()
+    out = torch.empty_like(ref)
+    call = R.DecodeCall(t, out, ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    other = upload(workload(W.config_spec(1)))
+    for rep in range(4):
+        out.fill_(float("nan"))
+        R.decode_workload(other)            # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep} differs"
+    expect, _ = oracle.Problem(w).attention()
+    check(out.cpu().numpy(), expect, "bf16", "graph out")
