@@ -44,7 +44,46 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the oracle sample in CPU-seconds (wall time x threads)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (for counter runs, which serialise dispatches)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run torch's device copy of COPY_BYTES, 10 times (scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes)")
     return ap.parse_args()
+
+
+COPY_BYTES = 512 * 2**20
+
+
+def copy_calibration(torch):
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "dispatches": 10}), flush=True)
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3
+    counter summary, or None when there is none or the library's sources have
+    changed since it was taken."""
+    from shared_prompt_kv_amd import build as B
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("library_sources_sha256") != B.source_digest():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 # ---------------------------------------------------------------------------------------
@@ -121,7 +160,7 @@ def clone_set(torch, t):
     return {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
 
 
-def measure(torch, relay, w, steps, warmup, per_kernel=True):
+def measure(torch, relay, w, steps, warmup, per_kernel=True, graph=True):
     """Times decode steps over rotating input copies.
 
     graph: the steps captured in one HIP graph (a full rotation over the copies)
@@ -153,30 +192,9 @@ def measure(torch, relay, w, steps, warmup, per_kernel=True):
     torch.cuda.synchronize()
     res["eager_ms_per_step"] = e0.elapsed_time(e1) / steps
 
-    # HIP graph of one rotation (n_sets steps), replayed
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for c in calls:
-            c()
-    torch.cuda.current_stream().wait_stream(side)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for c in calls:
-            c()
-    reps = max(1, steps // n_sets)
-    for _ in range(2):
-        graph.replay()
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    res["graph_ms_per_step"] = e0.elapsed_time(e1) / (reps * n_sets)
-    res["graph_steps"] = reps * n_sets
-    res["ms_per_step"] = res["graph_ms_per_step"]
-    del graph
+    res["ms_per_step"] = res["eager_ms_per_step"]
+    if graph:
+        _time_graph(torch, calls, n_sets, steps, res)
 
     if per_kernel:
         he = HipEvents(torch)
@@ -198,6 +216,44 @@ def measure(torch, relay, w, steps, warmup, per_kernel=True):
     del calls, sets, outs, ws
     torch.cuda.empty_cache()
     return res
+
+
+def _time_graph(torch, calls, n_sets, steps, res):
+    """HIP graphs of the decode step, replayed for exactly `steps` steps: one graph
+    holds a full rotation over the input copies, a second the first steps % n_sets
+    calls of it."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(side)
+    reps, rest = divmod(steps, n_sets)
+    full = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(full):
+        for c in calls:
+            c()
+    part = None
+    if rest:
+        part = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(part):
+            for c in calls[:rest]:
+                c()
+    for _ in range(2):
+        full.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        full.replay()
+    if part is not None:
+        part.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    res["graph_ms_per_step"] = e0.elapsed_time(e1) / steps
+    res["ms_per_step"] = res["graph_ms_per_step"]
+    del full, part
 
 
 def cpu_baseline(w, budget_cpu_s):
@@ -237,10 +293,13 @@ def main():
     from shared_prompt_kv_amd import relay, workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     relay.load_library()
     spec = workloads.config_spec(args.config, args.sweep_index)
     w = workloads.generate(spec)
-    r = measure(torch, relay, w, args.steps, args.warmup)
+    r = measure(torch, relay, w, args.steps, args.warmup, graph=not args.no_graph)
     work = r["work"]
     ms = r["ms_per_step"]
     value = w.total_q / (ms * 1e-3)
@@ -258,7 +317,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
-        "timing": "HIP graph replay of the decode step (eager launch: %.5f ms/step)" % r["eager_ms_per_step"],
+        "timing": ("eager launches" if args.no_graph else
+                   "HIP graph replay of the decode step (eager launch: %.5f ms/step)" % r["eager_ms_per_step"]),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -276,7 +336,7 @@ def main():
         "plan": r["plan"],
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "bytes_alg_per_launch": work[dom], "traffic": None},
+                     "bytes_alg_per_launch": work[dom], "traffic": stored_traffic(dom, spec.name)},
     }
     if not args.no_sweep and args.config == 2:
         sweep = []
