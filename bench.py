@@ -256,6 +256,17 @@ def _time_graph(torch, calls, n_sets, steps, res):
     del full, part
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip() + f" ({os.cpu_count()} logical CPUs visible)"
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_cpu_s):
     """The oracle (unchanged) on the host cores, request by request through the
     workload (cycling), until about budget_cpu_s CPU-seconds have been spent."""
@@ -276,10 +287,32 @@ def cpu_baseline(w, budget_cpu_s):
         n += 1
         elapsed = time.perf_counter() - start
     return {"value": round(tokens / elapsed, 3), "unit": "query-tokens/s/layer", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"exact fp64 causal attention (all {Hq} heads) for {n} requests taken in order, "
                       f"cycling over the {w.spec.batch} requests of the same workload: {tokens} query "
                       f"tokens in {elapsed:.2f} s wall on {cores} threads"}
+
+
+def point(torch, relay, spec, args):
+    """One workload measured like the main line (fewer steps): throughput and
+    roofline fractions."""
+    w = workloads_generate(spec)
+    rr = measure(torch, relay, w, min(args.steps, 50), min(args.warmup, 10))
+    print(f"[bench] {spec.name}: {1000 * rr['ms_per_step']:.2f} us/step", file=sys.stderr, flush=True)
+    m = rr["ms_per_step"]
+    work = rr["work"]
+    peak = (BF16_PEAK_TFLOPS if spec.dtype == "bf16" else FP32_PEAK_TFLOPS) * 1e12
+    return {"workload": spec.name, "qtok_s": round(w.total_q / (m * 1e-3), 1),
+            "us_per_step": round(1000 * m, 2), "eager_us_per_step": round(1000 * rr["eager_ms_per_step"], 2),
+            "hbm_frac": round(work["step_bytes"] / (m * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+            "mfma_frac": round(work["step_flops"] / (m * 1e-3) / peak, 4),
+            "kernel_us": {k: round(v, 2) for k, v in rr["kernel_us"].items()},
+            "sys_mode": rr["plan"]["sys_mode"]}
+
+
+def workloads_generate(spec):
+    from shared_prompt_kv_amd import workloads
+    return workloads.generate(spec)
 
 
 def main():
@@ -300,6 +333,7 @@ def main():
     spec = workloads.config_spec(args.config, args.sweep_index)
     w = workloads.generate(spec)
     r = measure(torch, relay, w, args.steps, args.warmup, graph=not args.no_graph)
+    print(f"[bench] {spec.name}: {1000 * r['ms_per_step']:.2f} us/step", file=sys.stderr, flush=True)
     work = r["work"]
     ms = r["ms_per_step"]
     value = w.total_q / (ms * 1e-3)
@@ -339,17 +373,10 @@ def main():
                      "bytes_alg_per_launch": work[dom], "traffic": stored_traffic(dom, spec.name)},
     }
     if not args.no_sweep and args.config == 2:
-        sweep = []
-        for i, Ls in enumerate(workloads.CONFIG3_SYS_LENS):
-            ws_ = workloads.generate(workloads.config_spec(3, i))
-            rr = measure(torch, relay, ws_, min(args.steps, 50), min(args.warmup, 10), per_kernel=True)
-            m = rr["ms_per_step"]
-            sweep.append({"sys_len": Ls, "qtok_s": round(ws_.total_q / (m * 1e-3), 1),
-                          "us_per_step": round(1000 * m, 2), "eager_us_per_step": round(1000 * rr["eager_ms_per_step"], 2),
-                          "hbm_frac": round(rr["work"]["step_bytes"] / (m * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-                          "kernel_us": {k: round(v, 2) for k, v in rr["kernel_us"].items()}})
-            del ws_
-        line["sweep"] = {"workload": "llama30b_mha (batch 32, 52 heads, ctx 128)", "points": sweep}
+        line["sweep"] = {"workload": "llama30b_mha (batch 32, 52 heads, ctx 128)",
+                         "points": [dict(sys_len=Ls, **point(torch, relay, workloads.config_spec(3, i), args))
+                                    for i, Ls in enumerate(workloads.CONFIG3_SYS_LENS)]}
+        line["other_configs"] = [point(torch, relay, workloads.config_spec(c, 0), args) for c in (1, 4, 5)]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

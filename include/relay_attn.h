@@ -11,11 +11,11 @@
  *      system KV cache alone; the cache is read from HBM once for the whole batch
  *      by stacking all query rows into one matrix-matrix product;
  *   2. context attention - each request attends to its own paged context KV alone;
- *   3. relay fusion      - the final output is a convex combination of the two
- *      intermediate outputs.  The pages name only "convex combination"; the weights
- *      here are alpha_sys = e^LSE_sys / (e^LSE_sys + e^LSE_ctx), alpha_ctx =
- *      1 - alpha_sys, the only convex weights for which the result equals exact
- *      causal attention over [system; context].
+ *   3. relay fusion      - the final output is a weighted average of the two
+ *      intermediate outputs with non-negative weights that sum to one.  The pages
+ *      fix nothing more about the weights; here they are alpha_sys = e^LSE_sys /
+ *      (e^LSE_sys + e^LSE_ctx) and alpha_ctx = 1 - alpha_sys, the only such weights
+ *      for which the result equals exact causal attention over [system; context].
  *
  * The system KV cache is separate from the context cache and filled before
  * serving; context positions follow the system prompt (atyun.com article, section
@@ -153,8 +153,11 @@ int relay_get_plan(const relay_dims* dims, int32_t sys_len, relay_plan* plan);
  * The whole RelayAttention decode step: system attention (skipped when
  * sys_len == 0), context attention and relay fusion, written to out.
  * Equals exact causal attention of each query row over its visible
- * [system; context] keys.  Three kernels are enqueued on `stream`:
- * sys_attn, ctx_attn and relay_fuse.  workspace must hold
+ * [system; context] keys.  Enqueued on `stream`: when at most 64 query rows
+ * share a KV head, one launch that runs the system and context steps together,
+ * then relay_fuse (2 launches); otherwise the matrix-core system kernel, the
+ * context step and relay_fuse (3 launches).  relay_get_plan() says which.
+ * workspace must hold
  * relay_workspace_size(dims, sys_len) bytes (256-byte aligned); its contents on
  * entry are irrelevant and on return unspecified.
  */

@@ -26,11 +26,12 @@
  *   context part (attention over the request's own visible context alone) is
  *   [L_s, L_s + p + 1).  An empty range gives out = 0, LSE = -inf.
  *
- *   oracle_relay_fuse() is the relay-fusion step: the final output is a convex
- *   combination of the two intermediate outputs (atyun.com article, section
- *   "RelayAttention").  The pages state only "convex combination"; the weights
- *   used are alpha_s = e^LSE_s / (e^LSE_s + e^LSE_c), alpha_c = 1 - alpha_s, the
- *   only convex weights for which the result equals exact attention.
+ *   oracle_relay_fuse() is the relay-fusion step: the final output is a weighted
+ *   average of the two intermediate outputs, with non-negative weights summing to
+ *   one (atyun.com article, section "RelayAttention").  The pages fix nothing more
+ *   about the weights; those used are alpha_s = e^LSE_s / (e^LSE_s + e^LSE_c),
+ *   alpha_c = 1 - alpha_s, the only such weights for which the result equals
+ *   exact attention.
  *   oracle_merge() is the same identity over k partial results.
  *
  * Sums over keys use Neumaier compensation so that the split-equals-unsplit

@@ -63,7 +63,7 @@ __device__ inline void load_q_tile(u32x4* qf, const void* q, size_t row_index, b
 }
 
 template <typename T, int D, int WK, bool PF>
-__device__ void sys_unit(const UnitArgs& a, int u, float* lds) {
+__device__ __forceinline__ void sys_unit(const UnitArgs& a, int u, float* lds) {
   constexpr int E = Elem<T>::kBytes;
   const int lane = lane_id();
   const int kl = threadIdx.x / kWave;
@@ -121,20 +121,24 @@ __device__ void sys_unit(const UnitArgs& a, int u, float* lds) {
 }
 
 template <typename T, int D, int RT, int WK, bool PF>
-__device__ void ctx_unit(const UnitArgs& a, int v, float* lds) {
+__device__ __forceinline__ void ctx_unit(const UnitArgs& a, int v, float* lds) {
   constexpr int E = Elem<T>::kBytes;
   constexpr int NCH = PageFrag<T, D>::NCH;
   const int lane = lane_id();
   const int kl = threadIdx.x / kWave;
   const int q4 = lane >> 4, r16 = lane & 15;
+  // unit id -> (row block, group): the row blocks of one (request, head, split) are
+  // 8 ids apart (same XCD).  Groups are split-major: with a grid-stride schedule,
+  // every workgroup's first units are first splits (the longest, present for every
+  // request), and no workgroup is tied to one split index.
   const int slot = v >> 3;
   const int rb = slot % a.ctx_row_blocks;
-  int grp = (v & 7) + 8 * (slot / a.ctx_row_blocks);
-  const int split = grp % a.ctx_max_splits;
-  grp /= a.ctx_max_splits;
+  const int grp = (v & 7) + 8 * (slot / a.ctx_row_blocks);
+  const int per_split = a.batch * a.num_kv_heads;
+  const int split = grp / per_split;
   const int h = grp % a.num_kv_heads;
-  const int b = grp / a.num_kv_heads;
-  if (b >= a.batch) return;  // padding unit
+  const int b = (grp % per_split) / a.num_kv_heads;
+  if (split >= a.ctx_max_splits) return;  // padding unit
 
   // Clamped per-request sizes: bad inputs cannot move an access out of bounds.
   const int cap = min(a.max_ctx_len, a.max_blocks_per_seq * kTile);
@@ -219,24 +223,31 @@ constexpr size_t units_lds_bytes() {
   return WK > 1 ? sizeof(float) * (size_t)(WK / 2) * kMergeSlot<D, RT> : 0;
 }
 
-// The kernels are persistent: the grid is sized to what the GPU holds at once and
-// workgroup g takes units g, g + gridDim.x, ...; no workgroup waits to be dispatched
-// and every unit's setup latency overlaps other workgroups' streaming.
-// (Barriers inside a unit are reached by every wave of the workgroup: the unit loop
-// depends on blockIdx only.)
+// The kernels are persistent: the grid is sized to what the GPU holds at once, so
+// no workgroup waits to be dispatched and every unit's setup latency overlaps other
+// workgroups' streaming.  Round k hands units [kG, kG + G) to the G workgroups,
+// rotated by 8k: workgroup w takes unit kG + (w + 8k) mod G.  Each round is a
+// bijection, the unit's XCD (unit mod 8 when G is a multiple of 8) stays that of
+// the workgroup, and no workgroup is tied to one row block or split for the whole
+// launch.  (Barriers inside a unit are reached by every wave of the workgroup: the
+// unit sequence depends on blockIdx only.)
+#define RELAY_FOR_EACH_UNIT(u, total)                                                   \
+  for (int base_ = 0, off_ = (int)blockIdx.x, u = off_; base_ < (total);                \
+       base_ += (int)gridDim.x, off_ = (off_ + 8) % (int)gridDim.x, u = base_ + off_)  \
+    if (u < (total))
 
 // The system-attention step alone (at most 64 stacked rows: row tiles as units).
 template <typename T, int D, int WK, bool PF>
 __global__ __launch_bounds__(kWave* WK) void sys_attn_kernel(UnitArgs a) {
   extern __shared__ float lds[];
-  for (int u = blockIdx.x; u < a.n_sys_units; u += gridDim.x) sys_unit<T, D, WK, PF>(a, u, lds);
+  RELAY_FOR_EACH_UNIT(u, a.n_sys_units) sys_unit<T, D, WK, PF>(a, u, lds);
 }
 
 // The context-attention step alone.
 template <typename T, int D, int RT, int WK, bool PF>
 __global__ __launch_bounds__(kWave* WK) void ctx_attn_kernel(UnitArgs a) {
   extern __shared__ float lds[];
-  for (int u = blockIdx.x; u < a.n_ctx_units; u += gridDim.x) ctx_unit<T, D, RT, WK, PF>(a, u, lds);
+  RELAY_FOR_EACH_UNIT(u, a.n_ctx_units) ctx_unit<T, D, RT, WK, PF>(a, u, lds);
 }
 
 // Both steps in one launch: units [0, n_sys_units) are system units (the longest,
@@ -245,7 +256,7 @@ template <typename T, int D, int RT, int WK, bool PF>
 __global__ __launch_bounds__(kWave* WK) void sys_ctx_attn_kernel(UnitArgs a) {
   extern __shared__ float lds[];
   const int total = a.n_sys_units + a.n_ctx_units;
-  for (int u = blockIdx.x; u < total; u += gridDim.x) {
+  RELAY_FOR_EACH_UNIT(u, total) {
     if (u < a.n_sys_units) sys_unit<T, D, WK, PF>(a, u, lds);
     else ctx_unit<T, D, RT, WK, PF>(a, u - a.n_sys_units, lds);
   }

@@ -1,7 +1,8 @@
 // relay_fuse: RelayAttention's relay-fusion step on gfx950.
 //
-// The final output is a convex combination of the system-attention and
-// context-attention outputs (atyun.com article, section "RelayAttention"; a single
+// The final output is a weighted average, with non-negative weights summing to one,
+// of the system-attention and context-attention outputs (atyun.com article, section
+// "RelayAttention"; a single
 // fused elementwise kernel in the linnk.ai summary, section "Abstract").  With
 // LSE_i = ln sum_{j in part i} e^{s_j}, the weights e^{LSE_i} / sum_k e^{LSE_k} are
 // non-negative, sum to one, and make the result equal attention over the union of

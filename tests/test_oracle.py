@@ -6,8 +6,8 @@
   the CPU over the dense gathered [K_s; K_c] with an explicit causal mask;
 * closed forms: q = 0, one key, two keys, constant V, V shifted by a constant;
 * the relay identity (RelayAttention abstract: exact reformulation; atyun.com
-  article, section "RelayAttention": convex combination of two intermediate
-  outputs): weights non-negative and summing to 1, split == unsplit, split-point
+  article, section "RelayAttention": the output is a weighted average of the two
+  intermediate outputs): weights non-negative and summing to 1, split == unsplit, split-point
   invariance, k-way == 2-way, sys_len = 0 and empty-context reductions;
 * paging invariances: page relabelling, GQA->MHA expansion, batch permutation,
   poison never reaching an output.
