@@ -46,6 +46,9 @@ def parse():
                     help="budget of the oracle sample in CPU-seconds (wall time x threads)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (for counter runs, which serialise dispatches)")
+    ap.add_argument("--sys-scaling", action="store_true",
+                    help="only run the system-attention step over batch sweeps of the Llama2-7B and "
+                         "Llama-3-8B shapes (for counters: system-KV bytes read vs batch size)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run torch's device copy of COPY_BYTES, 10 times (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -62,6 +65,46 @@ def copy_calibration(torch):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": COPY_BYTES, "dispatches": 10}), flush=True)
+
+
+SYS_SCALING = (("llama2_7b_mha", 2, (1, 4, 8, 16, 32)), ("llama3_8b_gqa", 4, (1, 4, 16, 64, 256)))
+
+
+def sys_scaling(torch, relay, steps):
+    """relay_sys_attn alone (system kernel + chunk merge) for each batch size: 3
+    untimed calls then `steps` timed ones.  Prints one JSON line per case; under
+    rocprofv3 the system kernel's dispatches come in the same order, 3 + steps per
+    case."""
+    from shared_prompt_kv_amd import workloads
+    for name, cfg, batches in SYS_SCALING:
+        for B in batches:
+            spec = workloads.config_spec(cfg, 0).replace(batch=B)
+            w = workloads.generate(spec)
+            t = relay.to_device(w, "cuda")
+            dims = relay.dims_of(t)
+            ws = relay.workspace(dims, t["sys_len"], "cuda")
+            call = lambda: relay.relay_sys_attn(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], dims,
+                                                workspace_buf=ws)
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            plan = relay.relay_get_plan(dims, t["sys_len"])
+            E = 2 if spec.dtype == "bf16" else 4
+            print(json.dumps({"shape": name, "batch": B, "sys_len": spec.sys_len,
+                              "rows_per_kv_head": w.total_q * spec.group,
+                              "kernel": "sys_attn" if plan["sys_mode"] == 1 else "sys_attn_tiled",
+                              "dispatches": 3 + steps,
+                              "sys_kv_bytes": 2 * spec.num_kv_heads * spec.head_dim * E * spec.sys_len,
+                              "us_per_call": round(1000 * e0.elapsed_time(e1) / steps, 2)}), flush=True)
+            del t, ws, w
+            torch.cuda.empty_cache()
 
 
 def stored_traffic(kernel, workload):
@@ -328,6 +371,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.sys_scaling:
+        relay.load_library()
+        sys_scaling(torch, relay, min(args.steps, 20))
         return
     relay.load_library()
     spec = workloads.config_spec(args.config, args.sweep_index)

@@ -23,6 +23,8 @@
 // writes one partial (O, LSE) per row.  sys_ctx_attn_kernel carries both kinds of
 // unit in one launch (system units first: they are the longest), so the two steps
 // overlap and the machine fills even when one step alone could not.
+#include <atomic>
+
 #include "relay_device.hpp"
 #include "relay_internal.hpp"
 
@@ -120,8 +122,42 @@ __device__ __forceinline__ void sys_unit(const UnitArgs& a, int u, float* lds) {
   }
 }
 
+// Where a context unit's work is, read before the unit starts: the next unit's
+// metadata loads are issued while the current unit streams, so a unit begins with
+// its context length, query range and page ids already in registers.
+struct CtxMeta {
+  int c;    // context length (clamped)
+  int qs;   // first query token of the request
+  int nq;   // query tokens of the request
+  int pt;   // this lane's page id (lane s holds the split's page s)
+};
+
+// Issues the metadata loads of context unit v (values are consumed later).
+__device__ __forceinline__ CtxMeta ctx_meta(const UnitArgs& a, int v) {
+  CtxMeta m{0, 0, 0, 0};
+  const int slot = v >> 3;
+  const int grp = (v & 7) + 8 * (slot / a.ctx_row_blocks);
+  const int per_split = a.batch * a.num_kv_heads;
+  const int split = grp / per_split;
+  if (split >= a.ctx_max_splits) return m;  // padding unit
+  const int b = (grp % per_split) / a.num_kv_heads;
+  m.c = a.ctx_lens[b];
+  m.qs = b;
+  m.nq = 1;
+  if (a.cu_q_lens) {
+    m.qs = a.cu_q_lens[b];
+    m.nq = a.cu_q_lens[b + 1];  // the end for now; ctx_unit makes it a count
+  }
+  // table entries of the split; entries past the context are read but never used
+  const int pg_begin = split * (a.ctx_split_len / kTile);
+  const int lane = lane_id();
+  if (lane < a.ctx_split_len / kTile && pg_begin + lane < a.max_blocks_per_seq)
+    m.pt = a.block_tables[(size_t)b * a.max_blocks_per_seq + pg_begin + lane];
+  return m;
+}
+
 template <typename T, int D, int RT, int WK, bool PF>
-__device__ __forceinline__ void ctx_unit(const UnitArgs& a, int v, float* lds) {
+__device__ __forceinline__ void ctx_unit(const UnitArgs& a, int v, CtxMeta m, float* lds) {
   constexpr int E = Elem<T>::kBytes;
   constexpr int NCH = PageFrag<T, D>::NCH;
   const int lane = lane_id();
@@ -137,16 +173,15 @@ __device__ __forceinline__ void ctx_unit(const UnitArgs& a, int v, float* lds) {
   const int per_split = a.batch * a.num_kv_heads;
   const int split = grp / per_split;
   const int h = grp % a.num_kv_heads;
-  const int b = (grp % per_split) / a.num_kv_heads;
   if (split >= a.ctx_max_splits) return;  // padding unit
 
   // Clamped per-request sizes: bad inputs cannot move an access out of bounds.
   const int cap = min(a.max_ctx_len, a.max_blocks_per_seq * kTile);
-  const int c = min(max(a.ctx_lens[b], 0), cap);
-  int qs = b, nq = 1;
+  const int c = min(max(m.c, 0), cap);
+  int qs = m.qs, nq = 1;
   if (a.cu_q_lens) {
-    qs = min(max(a.cu_q_lens[b], 0), a.total_q);
-    nq = min(max(a.cu_q_lens[b + 1] - qs, 0), a.total_q - qs);
+    qs = min(max(m.qs, 0), a.total_q);
+    nq = min(max(m.nq - qs, 0), a.total_q - qs);
   }
   const int R = nq * a.group;
   const int row0 = rb * RT * 16;
@@ -172,13 +207,7 @@ __device__ __forceinline__ void ctx_unit(const UnitArgs& a, int v, float* lds) {
     return;
   }
 
-  // page ids of the split, one per lane (split_len <= 1024 keys = 64 pages)
-  const int npages = (c + kTile - 1) / kTile;
-  const int pg_begin = key_begin / kTile;
-  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-  int pt = 0;
-  if (lane < a.ctx_split_len / kTile && pg_begin + lane < npages) pt = bt[pg_begin + lane];
-
+  int pt = m.pt;
   u32x4 qf[RT][NCH];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) load_q_tile<T, D>(qf[rt], a.q, qrow[rt], last[rt] >= 0);
@@ -223,43 +252,68 @@ constexpr size_t units_lds_bytes() {
   return WK > 1 ? sizeof(float) * (size_t)(WK / 2) * kMergeSlot<D, RT> : 0;
 }
 
-// The kernels are persistent: the grid is sized to what the GPU holds at once, so
-// no workgroup waits to be dispatched and every unit's setup latency overlaps other
-// workgroups' streaming.  Round k hands units [kG, kG + G) to the G workgroups,
-// rotated by 8k: workgroup w takes unit kG + (w + 8k) mod G.  Each round is a
-// bijection, the unit's XCD (unit mod 8 when G is a multiple of 8) stays that of
-// the workgroup, and no workgroup is tied to one row block or split for the whole
-// launch.  (Barriers inside a unit are reached by every wave of the workgroup: the
-// unit sequence depends on blockIdx only.)
-#define RELAY_FOR_EACH_UNIT(u, total)                                                   \
-  for (int base_ = 0, off_ = (int)blockIdx.x, u = off_; base_ < (total);                \
-       base_ += (int)gridDim.x, off_ = (off_ + 8) % (int)gridDim.x, u = base_ + off_)  \
-    if (u < (total))
+// ---- scheduling ---------------------------------------------------------------------
+//
+// The kernels are persistent: the grid is sized to what the GPU holds at once, so no
+// workgroup waits to be dispatched.  Units are numbered with system units first (the
+// longest), then context units split-major.  Round k hands units [kG, kG + G) to the
+// G workgroups rotated by 8k: workgroup w takes kG + (w + 8k) mod G.  Each round is a
+// bijection, each unit stays on its workgroup's XCD (unit mod 8, G a multiple of 8),
+// and no workgroup is tied to one row block or split for the whole launch.  The
+// sequence is known in advance, so the next context unit's metadata loads are issued
+// while the current unit streams.  (Barriers inside a unit are reached by every wave
+// of the workgroup: the sequence depends on blockIdx only.)
+
+constexpr int kNoUnit = 0x7fffffff;
+
+// Metadata of unit u when it is a context unit (else nothing is loaded).
+template <int WHAT>
+__device__ __forceinline__ CtxMeta meta_for(const UnitArgs& a, int u, int ns, int total) {
+  if ((WHAT & kUnitsCtx) && u >= ns && u < total) return ctx_meta(a, u - ns);
+  return CtxMeta{0, 0, 0, 0};
+}
+
+template <typename T, int D, int RT, int WK, bool PF, int WHAT>
+__device__ __forceinline__ void run_units(const UnitArgs& a, float* lds) {
+  const int ns = (WHAT & kUnitsSys) ? a.n_sys_units : 0;
+  const int total = ns + ((WHAT & kUnitsCtx) ? a.n_ctx_units : 0);
+  const int G = gridDim.x;
+  int u = blockIdx.x < total ? (int)blockIdx.x : kNoUnit;
+  int soff = (int)((blockIdx.x + 8) % G);
+  int sbase = G;
+  int un = sbase + soff < total ? sbase + soff : kNoUnit;
+  CtxMeta m = meta_for<WHAT>(a, u, ns, total);
+  while (u != kNoUnit) {
+    const CtxMeta mn = meta_for<WHAT>(a, un, ns, total);
+    if ((WHAT & kUnitsSys) && u < ns) sys_unit<T, D, WK, PF>(a, u, lds);
+    else if (WHAT & kUnitsCtx) ctx_unit<T, D, RT, WK, PF>(a, u - ns, m, lds);
+    sbase += G;
+    soff = (soff + 8) % G;
+    u = un;
+    un = sbase + soff < total ? sbase + soff : kNoUnit;
+    m = mn;
+  }
+}
 
 // The system-attention step alone (at most 64 stacked rows: row tiles as units).
 template <typename T, int D, int WK, bool PF>
 __global__ __launch_bounds__(kWave* WK) void sys_attn_kernel(UnitArgs a) {
   extern __shared__ float lds[];
-  RELAY_FOR_EACH_UNIT(u, a.n_sys_units) sys_unit<T, D, WK, PF>(a, u, lds);
+  run_units<T, D, 1, WK, PF, kUnitsSys>(a, lds);
 }
 
 // The context-attention step alone.
 template <typename T, int D, int RT, int WK, bool PF>
 __global__ __launch_bounds__(kWave* WK) void ctx_attn_kernel(UnitArgs a) {
   extern __shared__ float lds[];
-  RELAY_FOR_EACH_UNIT(u, a.n_ctx_units) ctx_unit<T, D, RT, WK, PF>(a, u, lds);
+  run_units<T, D, RT, WK, PF, kUnitsCtx>(a, lds);
 }
 
-// Both steps in one launch: units [0, n_sys_units) are system units (the longest,
-// taken first), the rest context units.
+// Both steps in one launch.
 template <typename T, int D, int RT, int WK, bool PF>
 __global__ __launch_bounds__(kWave* WK) void sys_ctx_attn_kernel(UnitArgs a) {
   extern __shared__ float lds[];
-  const int total = a.n_sys_units + a.n_ctx_units;
-  RELAY_FOR_EACH_UNIT(u, total) {
-    if (u < a.n_sys_units) sys_unit<T, D, WK, PF>(a, u, lds);
-    else ctx_unit<T, D, RT, WK, PF>(a, u - a.n_sys_units, lds);
-  }
+  run_units<T, D, RT, WK, PF, kUnitsBoth>(a, lds);
 }
 
 // Workgroups of kernel `k` that one CU holds at once.
@@ -286,17 +340,24 @@ static hipError_t launch_units_t(const UnitArgs& a, int what, hipStream_t s) {
     k = reinterpret_cast<const void*>(&sys_ctx_attn_kernel<T, D, RT, WK, PF>);
     units = a.n_sys_units + a.n_ctx_units;
   }
-  static const int per_cu = blocks_per_cu(k, kWave * WK, lds);  // once per kernel instance
+  // occupancy of each kernel, queried once
+  static std::atomic<int> cached[4];
+  int per_cu = cached[what].load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    per_cu = blocks_per_cu(k, kWave * WK, lds);
+    cached[what].store(per_cu, std::memory_order_relaxed);
+  }
   const long long cap = 256LL * per_cu;
-  int grid = a.grid > 0 ? a.grid : (int)(units < cap ? units : cap);
+  long long grid = a.grid > 0 ? a.grid : (units < cap ? units : cap);
   if (grid > units) grid = units;
   if (grid < 1) grid = 1;
+  const dim3 g((unsigned)grid), b(kWave * WK);
   if (what == kUnitsSys)
-    hipLaunchKernelGGL((sys_attn_kernel<T, D, WK, PF>), dim3(grid), dim3(kWave * WK), lds, s, a);
+    hipLaunchKernelGGL((sys_attn_kernel<T, D, WK, PF>), g, b, lds, s, a);
   else if (what == kUnitsCtx)
-    hipLaunchKernelGGL((ctx_attn_kernel<T, D, RT, WK, PF>), dim3(grid), dim3(kWave * WK), lds, s, a);
+    hipLaunchKernelGGL((ctx_attn_kernel<T, D, RT, WK, PF>), g, b, lds, s, a);
   else
-    hipLaunchKernelGGL((sys_ctx_attn_kernel<T, D, RT, WK, PF>), dim3(grid), dim3(kWave * WK), lds, s, a);
+    hipLaunchKernelGGL((sys_ctx_attn_kernel<T, D, RT, WK, PF>), g, b, lds, s, a);
   return hipGetLastError();
 }
 

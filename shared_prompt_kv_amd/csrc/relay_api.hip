@@ -181,6 +181,7 @@ int launch_units(const relay_dims* d, const Plan& p, int what, const void* q, co
   a.prefetch = env_int("RELAY_PREFETCH", 1) == 1 ? 1 : 0;
   a.key_lanes = env_int("RELAY_KEY_LANES", 4);
   a.grid = env_int("RELAY_GRID", 0);
+
   if (what & relay::kUnitsSys) {
     a.sys_k = sys_k;
     a.sys_v = sys_v;

@@ -287,3 +287,41 @@ def test_graph_replay_matches_eager():
         assert torch.equal(out, ref), f"replay {rep} differs"
     expect, _ = oracle.Problem(w).attention()
     check(out.cpu().numpy(), expect, "bf16", "graph out")
+
+
+# ------------------------------------------------------------------------------------------
+# the unit schedule at other shapes; a workspace full of garbage
+
+SCHED_SPECS = [
+    W.config_spec(2).replace(batch=12, sys_len=1100, ctx_lo=16, ctx_hi=700),
+    W.config_spec(4).replace(batch=40, sys_len=700, ctx_median=200, ctx_cap=1500),
+    W.config_spec(5).replace(batch=6, sys_len=900, ctx_lo=64, ctx_hi=1200),
+]
+
+
+@pytest.mark.parametrize("spec", SCHED_SPECS, ids=[s.name for s in SCHED_SPECS])
+def test_multi_split_shapes(spec):
+    """Several context splits and row blocks per request, grids smaller than the unit
+    count: every unit runs once (oracle parity, deterministic bits)."""
+    say(f"[parity] multi-split {spec}")
+    w = workload(spec)
+    t = upload(w)
+    a = R.decode_workload(t).cpu()
+    b = R.decode_workload(t).cpu()
+    assert torch.equal(a, b)
+    expect, _ = oracle.Problem(w).attention()
+    check(a.numpy(), expect, spec.dtype, "multi-split")
+
+
+def test_garbage_workspace():
+    """Whatever the workspace held (here random bytes), a call gives the same bits."""
+    spec = SCHED_SPECS[0]
+    say(f"[parity] garbage workspace {spec}")
+    t = upload(workload(spec))
+    dims = R.dims_of(t)
+    ws = R.workspace(dims, t["sys_len"], "cuda")
+    ref = R.decode_workload(t, workspace_buf=ws).clone()
+    g = torch.Generator(device="cuda").manual_seed(7)
+    for _ in range(3):
+        ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda", generator=g).view(ws.dtype))
+        assert torch.equal(R.decode_workload(t, workspace_buf=ws), ref)
