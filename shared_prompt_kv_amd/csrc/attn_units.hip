@@ -30,29 +30,11 @@
 
 namespace relay {
 
-// Runs the steps kl, kl+WK, ... < nsteps.  PF: double-buffered, the loads of the
-// next step are issued before the current one is computed; otherwise one step's
-// loads at a time (fewer registers, more resident waves).
-template <bool PF, int WK, class Frag, class Issue, class Run>
-__device__ inline void stream_steps(int kl, int nsteps, Issue&& issue, Run&& run) {
-  if constexpr (PF) {
-    Frag f0, f1;
-    if (kl < nsteps) issue(f0, kl);
-    for (int s = kl; s < nsteps; s += 2 * WK) {
-      if (s + WK < nsteps) issue(f1, s + WK);
-      run(f0, s);
-      if (s + WK >= nsteps) break;
-      if (s + 2 * WK < nsteps) issue(f0, s + 2 * WK);
-      run(f1, s + WK);
-    }
-  } else {
-    Frag f;
-    for (int s = kl; s < nsteps; s += WK) {
-      issue(f, s);
-      run(f, s);
-    }
-  }
-}
+// Units shorter than this many keys compute P.V with P split into bf16 hi + lo (two
+// products): there single probabilities can be large and bf16 rounding of P alone
+// would cost up to 2^-9 of the output.  Longer units spread their weight over many
+// keys and round P once.
+constexpr int kPSplitBelow = 256;
 
 template <typename T, int D>
 __device__ inline void load_q_tile(u32x4* qf, const void* q, size_t row_index, bool valid) {
@@ -60,11 +42,11 @@ __device__ inline void load_q_tile(u32x4* qf, const void* q, size_t row_index, b
   const int q4 = lane_id() >> 4;
   const char* qp = static_cast<const char*>(q) + row_index * D * E;
 #pragma unroll
-  for (int kk = 0; kk < PageFrag<T, D>::NCH; ++kk)
+  for (int kk = 0; kk < StepK<T, D>::NCH; ++kk)
     qf[kk] = valid ? ld16(qp + 64 * kk + 16 * q4) : u32x4{0u, 0u, 0u, 0u};
 }
 
-template <typename T, int D, int WK, bool PF>
+template <typename T, int D, int WK>
 __device__ __forceinline__ void sys_unit(const UnitArgs& a, int u, float* lds) {
   constexpr int E = Elem<T>::kBytes;
   const int lane = lane_id();
@@ -83,7 +65,7 @@ __device__ __forceinline__ void sys_unit(const UnitArgs& a, int u, float* lds) {
   const int row = rt * 16 + r16;
   const int t = row / a.group, gi = row % a.group;
   const size_t qrow = (size_t)t * a.num_q_heads + (size_t)h * a.group + gi;
-  u32x4 qf[1][PageFrag<T, D>::NCH];
+  u32x4 qf[1][StepK<T, D>::NCH];
   load_q_tile<T, D>(qf[0], a.q, qrow, row < M);
   RowState<D> st[1];
   st[0].init();
@@ -92,22 +74,30 @@ __device__ __forceinline__ void sys_unit(const UnitArgs& a, int u, float* lds) {
   const int Ls = a.sys_len;
   const int key_begin = chunk * a.sys_chunk_len;
   const int key_end = min(key_begin + a.sys_chunk_len, Ls);
-  const int nsteps = (key_end - key_begin + kTile - 1) / kTile;
   const int ntile = (Ls + kTile - 1) / kTile;
   const char* kbase = static_cast<const char*>(a.sys_k) + (size_t)h * Ls * D * E;
   const char* vbase = static_cast<const char*>(a.sys_v) + (size_t)h * ntile * D * kTile * E;
 
-  // step s is system tile key_begin/16 + s; K rows past the end of the keys are
-  // clamped (their scores are masked, their values zeroed)
-  auto issue = [&](PageFrag<T, D>& f, int s) {
-    const int key0 = key_begin + s * kTile;
-    load_page<T, D>(f, kbase + (size_t)key0 * D * E, vbase + (size_t)(key0 / kTile) * D * kTile * E,
-                    min(r16, Ls - 1 - key0));
+  // step s covers system tiles key_begin/16 + 2s and + 2s + 1; a page past the end of
+  // the keys re-reads the first (its keys are masked), K rows past the end are clamped
+  const int npages = (key_end - key_begin + kTile - 1) / kTile;
+  const int nsteps = (npages + 1) / 2;
+  auto addr = [&](int st_) {
+    const int ka = key_begin + 2 * kTile * st_;
+    const int kb = ka + kTile < Ls ? ka + kTile : ka;
+    StepAddr r;
+    r.ka = kbase + (size_t)ka * D * E;
+    r.kb = kbase + (size_t)kb * D * E;
+    r.ra = min(r16, Ls - 1 - ka);
+    r.rb = min(r16, Ls - 1 - kb);
+    r.va = vbase + (size_t)(ka / kTile) * D * kTile * E;
+    r.vb = vbase + (size_t)(kb / kTile) * D * kTile * E;
+    return r;
   };
-  auto run = [&](PageFrag<T, D>& f, int s) {
-    compute_page<T, D, 1, true>(f, qf, st, key_begin + s * kTile + 4 * q4, Ls, last, a.scale_log2);
-  };
-  stream_steps<PF, WK, PageFrag<T, D>>(kl, nsteps, issue, run);
+  if (key_end - key_begin < kPSplitBelow)
+    stream_pipelined<T, D, 1, WK, true>(kl, nsteps, qf, st, key_begin, key_end, last, a.scale_log2, addr);
+  else
+    stream_pipelined<T, D, 1, WK, false>(kl, nsteps, qf, st, key_begin, key_end, last, a.scale_log2, addr);
   merge_key_lanes<D, 1, WK>(st, kl, lds);
 
   if (kl == 0) {
@@ -126,40 +116,39 @@ __device__ __forceinline__ void sys_unit(const UnitArgs& a, int u, float* lds) {
 // metadata loads are issued while the current unit streams, so a unit begins with
 // its context length, query range and page ids already in registers.
 struct CtxMeta {
-  int c;    // context length (clamped)
-  int qs;   // first query token of the request
-  int nq;   // query tokens of the request
+  int raw;  // lane 0: context length; lanes 1, 2: the request's query-token range
+            // (when cu_q_lens is given)
   int pt;   // this lane's page id (lane s holds the split's page s)
 };
 
-// Issues the metadata loads of context unit v (values are consumed later).
+// Issues the metadata loads of context unit v (values are consumed later).  They are
+// per-lane vector loads (lanes 0..2 read the request's length and query range), so
+// their wait is the first use in the next unit, not the issue point.
 __device__ __forceinline__ CtxMeta ctx_meta(const UnitArgs& a, int v) {
-  CtxMeta m{0, 0, 0, 0};
+  CtxMeta m{0, 0};
   const int slot = v >> 3;
   const int grp = (v & 7) + 8 * (slot / a.ctx_row_blocks);
   const int per_split = a.batch * a.num_kv_heads;
   const int split = grp / per_split;
   if (split >= a.ctx_max_splits) return m;  // padding unit
   const int b = (grp % per_split) / a.num_kv_heads;
-  m.c = a.ctx_lens[b];
-  m.qs = b;
-  m.nq = 1;
-  if (a.cu_q_lens) {
-    m.qs = a.cu_q_lens[b];
-    m.nq = a.cu_q_lens[b + 1];  // the end for now; ctx_unit makes it a count
-  }
+  // every lane loads (one vector load, in-bounds lane-dependent addresses): lane 0
+  // the context length, lanes 1 and 2 the query range when there is one
+  const int lane = lane_id();
+  const int32_t* src = a.cu_q_lens ? (lane == 0 ? a.ctx_lens + b : a.cu_q_lens + min(b + lane - 1, a.batch))
+                                   : a.ctx_lens + min(b + lane, a.batch - 1);
+  m.raw = *src;
   // table entries of the split; entries past the context are read but never used
   const int pg_begin = split * (a.ctx_split_len / kTile);
-  const int lane = lane_id();
   if (lane < a.ctx_split_len / kTile && pg_begin + lane < a.max_blocks_per_seq)
     m.pt = a.block_tables[(size_t)b * a.max_blocks_per_seq + pg_begin + lane];
   return m;
 }
 
-template <typename T, int D, int RT, int WK, bool PF>
+template <typename T, int D, int RT, int WK>
 __device__ __forceinline__ void ctx_unit(const UnitArgs& a, int v, CtxMeta m, float* lds) {
   constexpr int E = Elem<T>::kBytes;
-  constexpr int NCH = PageFrag<T, D>::NCH;
+  constexpr int NCH = StepK<T, D>::NCH;
   const int lane = lane_id();
   const int kl = threadIdx.x / kWave;
   const int q4 = lane >> 4, r16 = lane & 15;
@@ -177,11 +166,12 @@ __device__ __forceinline__ void ctx_unit(const UnitArgs& a, int v, CtxMeta m, fl
 
   // Clamped per-request sizes: bad inputs cannot move an access out of bounds.
   const int cap = min(a.max_ctx_len, a.max_blocks_per_seq * kTile);
-  const int c = min(max(m.c, 0), cap);
-  int qs = m.qs, nq = 1;
+  const int c = min(max(__builtin_amdgcn_readlane(m.raw, 0), 0), cap);
+  const int b = (grp % per_split) / a.num_kv_heads;
+  int qs = b, nq = 1;
   if (a.cu_q_lens) {
-    qs = min(max(m.qs, 0), a.total_q);
-    nq = min(max(m.nq - qs, 0), a.total_q - qs);
+    qs = min(max(__builtin_amdgcn_readlane(m.raw, 1), 0), a.total_q);
+    nq = min(max(__builtin_amdgcn_readlane(m.raw, 2) - qs, 0), a.total_q - qs);
   }
   const int R = nq * a.group;
   const int row0 = rb * RT * 16;
@@ -219,17 +209,25 @@ __device__ __forceinline__ void ctx_unit(const UnitArgs& a, int v, CtxMeta m, fl
   const size_t page_stride = (size_t)a.num_kv_heads * kTile * D * E;
   const char* kbase = static_cast<const char*>(a.ctx_k) + (size_t)h * kTile * D * E;
   const char* vbase = static_cast<const char*>(a.ctx_v) + (size_t)h * D * kTile * E;
-  const int nsteps = (key_end - key_begin + kTile - 1) / kTile;
-
-  // step s is the split's page s
-  auto issue = [&](PageFrag<T, D>& f, int s) {
-    const int blk = __builtin_amdgcn_readlane(pt, s);
-    load_page<T, D>(f, kbase + (size_t)blk * page_stride, vbase + (size_t)blk * page_stride, r16);
+  // step s covers the split's pages 2s and 2s + 1 (page ids broadcast from lane 2s,
+  // 2s + 1); a page past the split's end re-reads the last one (its keys are masked)
+  const int npages = (key_end - key_begin + kTile - 1) / kTile;
+  const int nsteps = (npages + 1) / 2;
+  auto addr = [&](int st_) {
+    const int ba = __builtin_amdgcn_readlane(pt, 2 * st_);
+    const int bb = __builtin_amdgcn_readlane(pt, min(2 * st_ + 1, npages - 1));
+    StepAddr r;
+    r.ka = kbase + (size_t)ba * page_stride;
+    r.kb = kbase + (size_t)bb * page_stride;
+    r.va = vbase + (size_t)ba * page_stride;
+    r.vb = vbase + (size_t)bb * page_stride;
+    r.ra = r.rb = r16;
+    return r;
   };
-  auto run = [&](PageFrag<T, D>& f, int s) {
-    compute_page<T, D, RT, true>(f, qf, st, key_begin + s * kTile + 4 * q4, c, last, a.scale_log2);
-  };
-  stream_steps<PF, WK, PageFrag<T, D>>(kl, nsteps, issue, run);
+  if (key_end - key_begin < kPSplitBelow)
+    stream_pipelined<T, D, RT, WK, true>(kl, nsteps, qf, st, key_begin, key_end, last, a.scale_log2, addr);
+  else
+    stream_pipelined<T, D, RT, WK, false>(kl, nsteps, qf, st, key_begin, key_end, last, a.scale_log2, addr);
   merge_key_lanes<D, RT, WK>(st, kl, lds);
 
   if (kl == 0) {
@@ -270,10 +268,10 @@ constexpr int kNoUnit = 0x7fffffff;
 template <int WHAT>
 __device__ __forceinline__ CtxMeta meta_for(const UnitArgs& a, int u, int ns, int total) {
   if ((WHAT & kUnitsCtx) && u >= ns && u < total) return ctx_meta(a, u - ns);
-  return CtxMeta{0, 0, 0, 0};
+  return CtxMeta{0, 0};
 }
 
-template <typename T, int D, int RT, int WK, bool PF, int WHAT>
+template <typename T, int D, int RT, int WK, int WHAT>
 __device__ __forceinline__ void run_units(const UnitArgs& a, float* lds) {
   const int ns = (WHAT & kUnitsSys) ? a.n_sys_units : 0;
   const int total = ns + ((WHAT & kUnitsCtx) ? a.n_ctx_units : 0);
@@ -285,8 +283,8 @@ __device__ __forceinline__ void run_units(const UnitArgs& a, float* lds) {
   CtxMeta m = meta_for<WHAT>(a, u, ns, total);
   while (u != kNoUnit) {
     const CtxMeta mn = meta_for<WHAT>(a, un, ns, total);
-    if ((WHAT & kUnitsSys) && u < ns) sys_unit<T, D, WK, PF>(a, u, lds);
-    else if (WHAT & kUnitsCtx) ctx_unit<T, D, RT, WK, PF>(a, u - ns, m, lds);
+    if ((WHAT & kUnitsSys) && u < ns) sys_unit<T, D, WK>(a, u, lds);
+    else if (WHAT & kUnitsCtx) ctx_unit<T, D, RT, WK>(a, u - ns, m, lds);
     sbase += G;
     soff = (soff + 8) % G;
     u = un;
@@ -296,24 +294,24 @@ __device__ __forceinline__ void run_units(const UnitArgs& a, float* lds) {
 }
 
 // The system-attention step alone (at most 64 stacked rows: row tiles as units).
-template <typename T, int D, int WK, bool PF>
-__global__ __launch_bounds__(kWave* WK) void sys_attn_kernel(UnitArgs a) {
+template <typename T, int D, int WK>
+__global__ __launch_bounds__(kWave* WK, (stream_depth<T, 1>())) void sys_attn_kernel(UnitArgs a) {
   extern __shared__ float lds[];
-  run_units<T, D, 1, WK, PF, kUnitsSys>(a, lds);
+  run_units<T, D, 1, WK, kUnitsSys>(a, lds);
 }
 
 // The context-attention step alone.
-template <typename T, int D, int RT, int WK, bool PF>
-__global__ __launch_bounds__(kWave* WK) void ctx_attn_kernel(UnitArgs a) {
+template <typename T, int D, int RT, int WK>
+__global__ __launch_bounds__(kWave* WK, (stream_depth<T, RT>())) void ctx_attn_kernel(UnitArgs a) {
   extern __shared__ float lds[];
-  run_units<T, D, RT, WK, PF, kUnitsCtx>(a, lds);
+  run_units<T, D, RT, WK, kUnitsCtx>(a, lds);
 }
 
 // Both steps in one launch.
-template <typename T, int D, int RT, int WK, bool PF>
-__global__ __launch_bounds__(kWave* WK) void sys_ctx_attn_kernel(UnitArgs a) {
+template <typename T, int D, int RT, int WK>
+__global__ __launch_bounds__(kWave* WK, (stream_depth<T, RT>())) void sys_ctx_attn_kernel(UnitArgs a) {
   extern __shared__ float lds[];
-  run_units<T, D, RT, WK, PF, kUnitsBoth>(a, lds);
+  run_units<T, D, RT, WK, kUnitsBoth>(a, lds);
 }
 
 // Workgroups of kernel `k` that one CU holds at once.
@@ -324,20 +322,20 @@ static int blocks_per_cu(const void* k, int threads, size_t lds) {
   return per_cu;
 }
 
-template <typename T, int D, int RT, int WK, bool PF>
+template <typename T, int D, int RT, int WK>
 static hipError_t launch_units_t(const UnitArgs& a, int what, hipStream_t s) {
   constexpr size_t lds = units_lds_bytes<D, RT, WK>();
   static_assert(lds <= 64 * 1024, "LDS budget");
   const void* k;
   int units;
   if (what == kUnitsSys) {
-    k = reinterpret_cast<const void*>(&sys_attn_kernel<T, D, WK, PF>);
+    k = reinterpret_cast<const void*>(&sys_attn_kernel<T, D, WK>);
     units = a.n_sys_units;
   } else if (what == kUnitsCtx) {
-    k = reinterpret_cast<const void*>(&ctx_attn_kernel<T, D, RT, WK, PF>);
+    k = reinterpret_cast<const void*>(&ctx_attn_kernel<T, D, RT, WK>);
     units = a.n_ctx_units;
   } else {
-    k = reinterpret_cast<const void*>(&sys_ctx_attn_kernel<T, D, RT, WK, PF>);
+    k = reinterpret_cast<const void*>(&sys_ctx_attn_kernel<T, D, RT, WK>);
     units = a.n_sys_units + a.n_ctx_units;
   }
   // occupancy of each kernel, queried once
@@ -353,31 +351,21 @@ static hipError_t launch_units_t(const UnitArgs& a, int what, hipStream_t s) {
   if (grid < 1) grid = 1;
   const dim3 g((unsigned)grid), b(kWave * WK);
   if (what == kUnitsSys)
-    hipLaunchKernelGGL((sys_attn_kernel<T, D, WK, PF>), g, b, lds, s, a);
+    hipLaunchKernelGGL((sys_attn_kernel<T, D, WK>), g, b, lds, s, a);
   else if (what == kUnitsCtx)
-    hipLaunchKernelGGL((ctx_attn_kernel<T, D, RT, WK, PF>), g, b, lds, s, a);
+    hipLaunchKernelGGL((ctx_attn_kernel<T, D, RT, WK>), g, b, lds, s, a);
   else
-    hipLaunchKernelGGL((sys_ctx_attn_kernel<T, D, RT, WK, PF>), g, b, lds, s, a);
+    hipLaunchKernelGGL((sys_ctx_attn_kernel<T, D, RT, WK>), g, b, lds, s, a);
   return hipGetLastError();
 }
 
+// Instantiated: 4 key lanes (8 for one row tile).
 template <typename T, int D, int RT>
 static hipError_t launch_units_w(const UnitArgs& a, int what, hipStream_t s) {
-  if constexpr (RT > 1) {  // two row tiles: at most 4 key lanes (LDS merge budget)
-    if (a.key_lanes == 1) return a.prefetch ? launch_units_t<T, D, RT, 1, true>(a, what, s)
-                                             : launch_units_t<T, D, RT, 1, false>(a, what, s);
-    return a.prefetch ? launch_units_t<T, D, RT, 4, true>(a, what, s)
-                      : launch_units_t<T, D, RT, 4, false>(a, what, s);
-  } else {
-    switch (a.key_lanes * 2 + a.prefetch) {
-      case 2: return launch_units_t<T, D, RT, 1, false>(a, what, s);
-      case 3: return launch_units_t<T, D, RT, 1, true>(a, what, s);
-      case 8: return launch_units_t<T, D, RT, 4, false>(a, what, s);
-      case 9: return launch_units_t<T, D, RT, 4, true>(a, what, s);
-      case 16: return launch_units_t<T, D, RT, 8, false>(a, what, s);
-      default: return launch_units_t<T, D, RT, 8, true>(a, what, s);
-    }
+  if constexpr (RT == 1) {
+    if (a.key_lanes == 8) return launch_units_t<T, D, RT, 8>(a, what, s);
   }
+  return launch_units_t<T, D, RT, 4>(a, what, s);
 }
 
 template <typename T, int D>
@@ -387,7 +375,7 @@ static hipError_t launch_units_d(const UnitArgs& a, int rt, int what, hipStream_
 
 hipError_t launch_attn_units(const UnitArgs& a, int ctx_rt, int what, int in_dtype, int head_dim,
                              hipStream_t stream) {
-  if (a.key_lanes != 1 && a.key_lanes != 4 && a.key_lanes != 8) return hipErrorInvalidValue;
+  if (a.key_lanes != 4 && a.key_lanes != 8) return hipErrorInvalidValue;
   if (in_dtype == 1) {
     return head_dim == 64 ? launch_units_d<bf16_t, 64>(a, ctx_rt, what, stream)
                           : launch_units_d<bf16_t, 128>(a, ctx_rt, what, stream);

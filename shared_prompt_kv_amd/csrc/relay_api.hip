@@ -178,7 +178,6 @@ int launch_units(const relay_dims* d, const Plan& p, int what, const void* q, co
   a.num_kv_heads = d->num_kv_heads;
   a.group = d->num_q_heads / d->num_kv_heads;
   a.scale_log2 = d->scale * kLog2e;
-  a.prefetch = env_int("RELAY_PREFETCH", 1) == 1 ? 1 : 0;
   a.key_lanes = env_int("RELAY_KEY_LANES", 4);
   a.grid = env_int("RELAY_GRID", 0);
 

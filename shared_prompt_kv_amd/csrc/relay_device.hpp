@@ -33,6 +33,7 @@ namespace relay {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kStep = 32;   // keys per step
@@ -330,7 +331,7 @@ __device__ inline void store_row_tile(const RowState<D>& st, float* o_row, float
 // V^T[dim][4q..4q+3] of one block.
 template <typename T> struct VFrag4;
 template <> struct VFrag4<bf16_t> {
-  uint2 c;  // 4 bf16
+  u32x2 c;  // 4 bf16
 };
 template <> struct VFrag4<float> {
   u32x4 c;  // 4 fp32
@@ -343,7 +344,7 @@ struct PageFrag {
   VFrag4<T> v[D / 16];   // V^T fragments, one per 16-dimension output tile
 };
 
-__device__ inline void load_v4(VFrag4<bf16_t>& f, const char* p) { f.c = *reinterpret_cast<const uint2*>(p); }
+__device__ inline void load_v4(VFrag4<bf16_t>& f, const char* p) { f.c = *reinterpret_cast<const u32x2*>(p); }
 __device__ inline void load_v4(VFrag4<float>& f, const char* p) { f.c = ld16(p); }
 
 // Zeroes the value elements of keys that do not exist (the first n of the four exist).
@@ -361,7 +362,7 @@ __device__ inline void mask_v4(VFrag4<float>& f, int n) {
 // P for this lane's row and the lane group's 4 keys, as the output product's B operand.
 template <typename T> struct PFrag4;
 template <> struct PFrag4<bf16_t> {
-  uint2 c, lo;  // bf16 P and its rounding residual
+  u32x2 c, lo;  // bf16 P and its rounding residual
 };
 template <> struct PFrag4<float> {
   float p[4];
@@ -440,6 +441,257 @@ __device__ inline void compute_page(PageFrag<T, D>& f, const u32x4 (&qf)[RT][Pag
     make_p4<PSPLIT>(pf, sc);
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) mfma_pv4<PSPLIT>(st[rt].o[t], f.v[t], pf);
+  }
+}
+
+// ---- two-page steps (32 keys) ----------------------------------------------------------
+//
+// A step covers pages a (keys k0..k0+15) and b (k0+16..k0+31).  Lane group q holds
+// the scores of keys 4q..4q+3 of each page (the score accumulator layout), i.e. 8
+// keys per lane: the k slots 8q..8q+7 of one v_mfma_f32_16x16x32_bf16 for P.V are
+// {a: 4q..4q+3, b: 4q..4q+3}, and V^T supplies the same keys, 8 bytes from each
+// page's dimension-major tile.  One softmax update serves 32 keys.
+//
+// K and V are issued separately so a step can be pipelined with a single set of
+// registers: once the score products have read K, the next step's K loads go out;
+// once P.V has read V, the next step's V loads go out.
+
+template <typename T, int D>
+struct StepK {
+  static constexpr int NCH = D * Elem<T>::kBytes / 64;
+  u32x4 a[NCH], b[NCH];  // this lane's K rows of pages a and b
+};
+template <typename T, int D>
+struct StepV {
+  VFrag4<T> a[D / 16], b[D / 16];  // V^T fragments of pages a and b
+};
+
+// P of one row tile for a step: bf16 hi (+ residual lo) in the k-slot order above,
+// or the 8 fp32 values.
+template <typename T> struct PStep;
+template <> struct PStep<bf16_t> {
+  u32x4 c, lo;
+};
+template <> struct PStep<float> {
+  float p[8];
+};
+
+template <bool SPLIT>
+__device__ __forceinline__ void make_pstep(PStep<bf16_t>& f, const float (&p)[8]) {
+  f.c.x = pack_bf16x2(p[0], p[1]);
+  f.c.y = pack_bf16x2(p[2], p[3]);
+  f.c.z = pack_bf16x2(p[4], p[5]);
+  f.c.w = pack_bf16x2(p[6], p[7]);
+  if constexpr (SPLIT) {
+    f.lo.x = pack_bf16x2(p[0] - bf16_lo_as_float(f.c.x), p[1] - bf16_hi_as_float(f.c.x));
+    f.lo.y = pack_bf16x2(p[2] - bf16_lo_as_float(f.c.y), p[3] - bf16_hi_as_float(f.c.y));
+    f.lo.z = pack_bf16x2(p[4] - bf16_lo_as_float(f.c.z), p[5] - bf16_hi_as_float(f.c.z));
+    f.lo.w = pack_bf16x2(p[6] - bf16_lo_as_float(f.c.w), p[7] - bf16_hi_as_float(f.c.w));
+  }
+}
+template <bool SPLIT>
+__device__ __forceinline__ void make_pstep(PStep<float>& f, const float (&p)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.p[i] = p[i];
+}
+
+template <bool SPLIT>
+__device__ __forceinline__ void mfma_pstep(f32x4& acc, const VFrag4<bf16_t>& va, const VFrag4<bf16_t>& vb,
+                                           const PStep<bf16_t>& p) {
+  const u32x4 v = {va.c.x, va.c.y, vb.c.x, vb.c.y};
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), __builtin_bit_cast(bf16x8, p.c),
+                                                acc, 0, 0, 0);
+  if constexpr (SPLIT)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), __builtin_bit_cast(bf16x8, p.lo),
+                                                  acc, 0, 0, 0);
+}
+template <bool SPLIT>
+__device__ __forceinline__ void mfma_pstep(f32x4& acc, const VFrag4<float>& va, const VFrag4<float>& vb,
+                                           const PStep<float>& p) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(va.c.x), p.p[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(va.c.y), p.p[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(va.c.z), p.p[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(va.c.w), p.p[3], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb.c.x), p.p[4], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb.c.y), p.p[5], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb.c.z), p.p[6], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb.c.w), p.p[7], acc, 0, 0, 0);
+}
+
+// Issues the K loads of a step: kpa/kpb are the bases of the two pages' 16 K rows,
+// krow_a/krow_b the row this lane reads (clamped where a page is short).
+template <typename T, int D>
+__device__ __forceinline__ void issue_k(StepK<T, D>& f, const char* kpa, const char* kpb, int krow_a, int krow_b) {
+  constexpr int E = Elem<T>::kBytes;
+  const int q4 = lane_id() >> 4;
+  const char* ra = kpa + krow_a * D * E + 16 * q4;
+  const char* rb = kpb + krow_b * D * E + 16 * q4;
+#pragma unroll
+  for (int kk = 0; kk < StepK<T, D>::NCH; ++kk) {
+    f.a[kk] = ld16(ra + 64 * kk);
+    f.b[kk] = ld16(rb + 64 * kk);
+  }
+}
+
+// Issues the V loads of a step from the two pages' dimension-major tiles.
+template <typename T, int D>
+__device__ __forceinline__ void issue_v(StepV<T, D>& f, const char* vpa, const char* vpb) {
+  constexpr int E = Elem<T>::kBytes;
+  const int q4 = lane_id() >> 4, r16 = lane_id() & 15;
+  const int off = r16 * kTile * E + 4 * q4 * E;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    load_v4(f.a[t], vpa + off + 16 * t * kTile * E);
+    load_v4(f.b[t], vpb + off + 16 * t * kTile * E);
+  }
+}
+
+// Rows whose running maximum grew by more than this (log2 units) rescale their
+// accumulators; otherwise probabilities are taken against the older, smaller
+// reference and may reach 2^kLazyRescale.  The result is the same real number either
+// way (the reference cancels in O = sum p v / sum p and in LSE = m + log2 l).
+constexpr float kLazyRescale = 8.f;
+
+template <int D, int N>
+__device__ __forceinline__ void softmax_lazy(RowState<D>& st, float (&s)[N]) {
+  float mx = s[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) mx = fmaxf(mx, s[i]);
+  mx = row_max4(mx);
+  const bool grow = mx > st.m + kLazyRescale;  // also true for the first live key (m = -inf)
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
+    const float m_new = grow ? mx : st.m;
+    const float alpha = grow ? fast_exp2(st.m - m_new) : 1.f;
+    st.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < RowState<D>::kDT; ++t) st.o[t] *= alpha;
+    st.m = m_new;
+  }
+  const float m_use = (st.m == neg_inf()) ? 0.f : st.m;
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    s[i] = fast_exp2(s[i] - m_use);
+    sum += s[i];
+  }
+  st.l += sum;
+}
+
+// Scores of a step for every row tile, folded into the row states; P out.  keyq: key
+// index of this lane group's first key of page a (page b: keyq + 16); keys at or past
+// kv_len do not exist; last[rt]: the last key the rows of tile rt may see.
+template <typename T, int D, int RT, bool PSPLIT>
+__device__ __forceinline__ void step_scores(const StepK<T, D>& k, const u32x4 (&qf)[RT][StepK<T, D>::NCH],
+                                            RowState<D> (&st)[RT], int keyq, int kv_len, const int (&last)[RT],
+                                            float scale_log2, PStep<T> (&p)[RT]) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < StepK<T, D>::NCH; ++kk) {
+      mfma_chunk(sa, k.a[kk], qf[rt][kk], T{});
+      mfma_chunk(sb, k.b[kk], qf[rt][kk], T{});
+    }
+    const int lim = min(last[rt], kv_len - 1);
+    float sc[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = (keyq + i <= lim) ? sa[i] * scale_log2 : neg_inf();
+      sc[4 + i] = (keyq + 16 + i <= lim) ? sb[i] * scale_log2 : neg_inf();
+    }
+    softmax_lazy(st[rt], sc);
+    make_pstep<PSPLIT>(p[rt], sc);
+  }
+}
+
+// P.V of a step into every row tile's accumulators (values of keys at or past kv_len
+// are zeroed first: poisoned padding must not reach an output through 0 * NaN).
+template <typename T, int D, int RT, bool PSPLIT>
+__device__ __forceinline__ void step_pv(StepV<T, D>& v, int keyq, int kv_len, RowState<D> (&st)[RT],
+                                        const PStep<T> (&p)[RT]) {
+  if (keyq + 4 > kv_len) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) mask_v4(v.a[t], kv_len - keyq);
+  }
+  if (keyq + 20 > kv_len) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) mask_v4(v.b[t], kv_len - keyq - 16);
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) mfma_pstep<PSPLIT>(st[rt].o[t], v.a[t], v.b[t], p[rt]);
+  }
+}
+
+// Steps held in registers while streaming: 2 (the next step's loads are in flight
+// while one computes) where it fits two waves per SIMD in 256 registers, bf16 with
+// one row tile; else 1 (a single step whose K and V are reloaded as soon as read).
+template <typename T, int RT>
+constexpr int stream_depth() {
+  return (Elem<T>::kBytes == 2 && RT == 1) ? 2 : 1;
+}
+
+// Page addresses of one step: K row bases and rows for pages a and b, V tile bases.
+struct StepAddr {
+  const char* ka;
+  const char* kb;
+  const char* va;
+  const char* vb;
+  int ra, rb;
+};
+
+// Streams steps kl, kl + WK, ... < nsteps: K(s) -> scores -> issue K(next) ->
+// V(s) -> P.V -> issue V(next).  addr(s) gives a step's page addresses.
+template <typename T, int D, int RT, int WK, bool PSPLIT, class Addr>
+__device__ __forceinline__ void stream_pipelined(int kl, int nsteps, const u32x4 (&qf)[RT][StepK<T, D>::NCH],
+                                                 RowState<D> (&st)[RT], int key0, int kv_len,
+                                                 const int (&last)[RT], float scale_log2, Addr&& addr) {
+  if (kl >= nsteps) return;
+  const int q4 = lane_id() >> 4;
+  auto issue = [&](StepK<T, D>& k, StepV<T, D>& v, int s) {
+    const StepAddr ad = addr(s);
+    issue_k(k, ad.ka, ad.kb, ad.ra, ad.rb);
+    issue_v(v, ad.va, ad.vb);
+  };
+  auto run = [&](StepK<T, D>& k, StepV<T, D>& v, int s) {
+    const int keyq = key0 + 32 * s + 4 * q4;
+    PStep<T> p[RT];
+    step_scores<T, D, RT, PSPLIT>(k, qf, st, keyq, kv_len, last, scale_log2, p);
+    step_pv<T, D, RT, PSPLIT>(v, keyq, kv_len, st, p);
+  };
+  if constexpr (stream_depth<T, RT>() == 2) {
+    // two steps in registers: the loads of step s + WK are in flight while s computes
+    StepK<T, D> k0, k1;
+    StepV<T, D> v0, v1;
+    issue(k0, v0, kl);
+    if (kl + WK < nsteps) issue(k1, v1, kl + WK);
+    for (int s = kl; s < nsteps; s += 2 * WK) {
+      run(k0, v0, s);
+      if (s + 2 * WK < nsteps) issue(k0, v0, s + 2 * WK);
+      if (s + WK >= nsteps) break;
+      run(k1, v1, s + WK);
+      if (s + 3 * WK < nsteps) issue(k1, v1, s + 3 * WK);
+    }
+  } else {
+    // one step in registers: K of the next step goes out once the scores have read K,
+    // V once P.V has read V
+    StepK<T, D> k;
+    StepV<T, D> v;
+    issue(k, v, kl);
+    for (int s = kl; s < nsteps; s += WK) {
+      const int sn = s + WK;
+      const int keyq = key0 + 32 * s + 4 * q4;
+      PStep<T> p[RT];
+      step_scores<T, D, RT, PSPLIT>(k, qf, st, keyq, kv_len, last, scale_log2, p);
+      StepAddr ad;
+      if (sn < nsteps) {
+        ad = addr(sn);
+        issue_k(k, ad.ka, ad.kb, ad.ra, ad.rb);
+      }
+      step_pv<T, D, RT, PSPLIT>(v, keyq, kv_len, st, p);
+      if (sn < nsteps) issue_v(v, ad.va, ad.vb);
+    }
   }
 }
 

@@ -78,8 +78,7 @@ struct UnitArgs {
   int ctx_max_splits;
   int ctx_row_blocks;  // ceil(max_q_len * g / (16 * ctx_rt))
   int n_ctx_units;
-  int key_lanes;       // waves per unit: 1, 4 or 8 (two row tiles: at most 4)
-  int prefetch;        // 1: double-buffered steps
+  int key_lanes;       // waves per unit: 4, or 8 with one row tile
   int grid;            // > 0: workgroups of the persistent launch; 0: as many as fit
 };
 
