@@ -43,7 +43,8 @@ int round_up32(long long x) { return (int)(((x + 31) / 32) * 32); }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Plan {
-  int sys_mode = 0;  // 0: no system step, 1: single-wave units, 2: tiled kernel
+  int sys_mode = 0;  // 0: no system step, 1: streaming units, 2: matrix-core kernel
+  int sys_mfma = 0;  // sys_mode 2: 1 = sys_attn_mfma (bf16, d = 128), 0 = sys_attn_tiled
   SysConfig sc{};
   int sys_chunks = 0, sys_chunk_len = 0, sys_row_blocks = 0, sys_wgs = 0, xcd_remap = 0;
   int ctx_rt = 1, ctx_split_len = 0, ctx_max_splits = 0, ctx_row_blocks = 0, ctx_wgs = 0;
@@ -97,6 +98,33 @@ void make_plan(const relay_dims* d, int32_t sys_len, Plan* p) {
       p->sys_row_blocks = ceil_div(M, 16);
       const long long groups = (long long)d->num_kv_heads * p->sys_chunks;
       p->sys_wgs = (int)(8LL * p->sys_row_blocks * ((groups + 7) / 8));
+    } else if (d->in_dtype == RELAY_BF16 && d->head_dim == 128) {
+      p->sys_mode = 2;
+      p->sys_mfma = 1;
+      p->sys_row_blocks = ceil_div(M, relay::kSysMfmaRows);
+      // chunks: the count that fills the resident workgroup slots best (whole rounds),
+      // then the fewest (each chunk adds a partial per row to the fusion)
+      const long long groups = (long long)p->sys_row_blocks * d->num_kv_heads;
+      int best_c = 1;
+      double best_eff = -1.0;
+      const int forced = env_int("RELAY_SYS_CHUNK", 0);
+      for (int c = 1; c <= 64; ++c) {
+        const int len = ((ceil_div(sys_len, c) + 63) / 64) * 64;
+        if (c > 1 && len < 256) break;
+        const int cact = ceil_div(sys_len, len);
+        const long long total = groups * cact;
+        const long long rounds = (total + relay::kSysMfmaSlots - 1) / relay::kSysMfmaSlots;
+        const double eff = (double)total / (double)(rounds * relay::kSysMfmaSlots);
+        if (eff > best_eff + 1e-9) {
+          best_eff = eff;
+          best_c = c;
+        }
+      }
+      int len = forced > 0 ? forced : ceil_div(sys_len, best_c);
+      p->sys_chunk_len = ((len + 63) / 64) * 64;
+      p->sys_chunks = ceil_div(sys_len, p->sys_chunk_len);
+      p->sys_wgs = p->sys_row_blocks * p->sys_chunks * d->num_kv_heads;
+      p->xcd_remap = (p->sys_row_blocks > 1 && p->sys_wgs % 8 == 0) ? 1 : 0;
     } else {
       p->sys_mode = 2;
       p->sc = relay::sys_config(M);
@@ -163,8 +191,9 @@ int launch_sys_tiled(const relay_dims* d, const Plan& p, const void* q, const vo
   a.row_blocks = p.sys_row_blocks;
   a.xcd_remap = p.xcd_remap;
   a.scale_log2 = d->scale * kLog2e;
-  hipError_t e = relay::launch_sys_attn_tiled(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s);
-  return e == hipSuccess ? RELAY_OK : hip_fail(e, "sys_attn_tiled launch");
+  hipError_t e = p.sys_mfma ? relay::launch_sys_attn_mfma(a, p.sys_wgs, s)
+                            : relay::launch_sys_attn_tiled(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s);
+  return e == hipSuccess ? RELAY_OK : hip_fail(e, "system attention launch");
 }
 
 // Launches single-wave units: what = relay::kUnitsSys / kUnitsCtx / kUnitsBoth.

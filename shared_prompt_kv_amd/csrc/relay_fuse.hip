@@ -37,33 +37,43 @@ __global__ __launch_bounds__(256) void relay_fuse_kernel(FuseArgs a) {
                                       : a.b_o + ((size_t)(i - a.a_count) * a.n_rows + row) * D;
     return reinterpret_cast<const f32x4*>(base + 4 * c4);
   };
-  // Batches of 4 partials: all loads of a batch are issued before any is used.
-  float m = neg_inf();
-  for (int i0 = 0; i0 < n; i0 += 4) {
-    float l[4];
+  // pass 1: the largest LSE and a live partial (16 loads in flight per batch)
+  constexpr int kL = 16;
+  float mx = neg_inf();
+  int live0 = -1;
+  for (int i0 = 0; i0 < n; i0 += kL) {
+    float l[kL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) l[j] = (i0 + j < n) ? *lse_at(i0 + j) : neg_inf();
+    for (int j = 0; j < kL; ++j) l[j] = *lse_at(min(i0 + j, n - 1));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m = fmaxf(m, l[j]);
+    for (int j = 0; j < kL; ++j) {
+      if (i0 + j < n && l[j] != neg_inf()) {
+        mx = fmaxf(mx, l[j]);
+        if (live0 < 0) live0 = i0 + j;
+      }
+    }
   }
+  // pass 2: the weighted sum, 8 output loads in flight per batch; an empty partial
+  // (LSE = -inf, its O possibly never written) reads the live one instead, weight 0
+  constexpr int kB = 8;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float z = 0.f;
-  if (m != neg_inf()) {
-    for (int i0 = 0; i0 < n; i0 += 4) {
-      float l[4];
-      f32x4 o[4];
+  if (live0 >= 0) {
+    for (int i0 = 0; i0 < n; i0 += kB) {
+      float l[kB], w[kB];
+      f32x4 o[kB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool ok = i0 + j < n;
-        l[j] = ok ? *lse_at(i0 + j) : neg_inf();
-        o[j] = ok ? *o_at(i0 + j) : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < kB; ++j) l[j] = *lse_at(min(i0 + j, n - 1));
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const bool live = i0 + j < n && l[j] != neg_inf();
+        w[j] = live ? fast_exp2((l[j] - mx) * kLog2e) : 0.f;
+        o[j] = *o_at(live ? i0 + j : live0);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool live = l[j] != neg_inf();  // an empty partial's O may be unwritten
-        const float w = live ? fast_exp2((l[j] - m) * kLog2e) : 0.f;
-        z += w;
-        acc += w * (live ? o[j] : f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int j = 0; j < kB; ++j) {
+        z += w[j];
+        acc += w[j] * o[j];
       }
     }
     acc *= 1.f / z;
@@ -75,7 +85,7 @@ __global__ __launch_bounds__(256) void relay_fuse_kernel(FuseArgs a) {
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + (size_t)row * D + 4 * c4) = acc;
   }
-  if (a.lse_out && c4 == 0) a.lse_out[row] = (m == neg_inf()) ? m : m + __builtin_amdgcn_logf(z) * kLn2;
+  if (a.lse_out && c4 == 0) a.lse_out[row] = (live0 < 0) ? neg_inf() : mx + __builtin_amdgcn_logf(z) * kLn2;
 }
 
 hipError_t launch_relay_fuse(const FuseArgs& a, int head_dim, int nwg, hipStream_t stream) {

@@ -106,6 +106,13 @@ struct FuseArgs {
 
 hipError_t launch_sys_attn_tiled(const SysArgs& a, const SysConfig& c, int in_dtype, int head_dim,
                                  int nwg, hipStream_t stream);
+
+// sys_attn_mfma (bf16, head_dim 128): workgroups of kSysMfmaRows query rows; designed
+// for two workgroups per CU (kSysMfmaSlots resident at once).  chunk_len: a multiple
+// of 64.
+constexpr int kSysMfmaRows = 128;
+constexpr int kSysMfmaSlots = 512;
+hipError_t launch_sys_attn_mfma(const SysArgs& a, int nwg, hipStream_t stream);
 hipError_t launch_attn_units(const UnitArgs& a, int ctx_rt, int what, int in_dtype, int head_dim,
                              hipStream_t stream);
 hipError_t launch_relay_fuse(const FuseArgs& a, int head_dim, int nwg, hipStream_t stream);

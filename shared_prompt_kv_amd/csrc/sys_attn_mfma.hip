@@ -1,0 +1,259 @@
+// sys_attn_mfma: RelayAttention's system-attention step on the matrix cores of gfx950
+// for many stacked query rows (bf16 inputs, head_dim 128).
+//
+// Every query row of the batch attends to the shared system KV cache alone, so for KV
+// head h the M = T_q * g rows that use it form one matrix multiplied against the
+// system keys (RelayAttention paper page, Abstract; atyun.com article, section
+// "RelayAttention": the system K/V leave HBM once per batch).  With M in the
+// thousands this is a dense contraction bound by the matrix cores.
+//
+// Workgroup = (128-row block, key chunk, KV head), 4 waves of 32 rows each.  The
+// chunk's keys stream through LDS in 64-key steps, double-buffered: the next step's
+// K and V tiles are fetched into registers while the current one is computed, then
+// written to the other LDS buffer; one barrier per step.  Every wave reads each tile
+// from LDS, so a tile leaves L2 once per workgroup.
+//
+// Matrix-core mapping (v_mfma_f32_32x32x16_bf16, 32x32 tiles):
+//   * scores transposed, S^T = K Q^T: A = 32 keys x 16 dims from LDS, B = 16 dims x 32
+//     query rows (registers).  Lane l then holds row l % 32 and keys
+//     8 (j / 4) + 4 (l / 32) + j % 4, j = 0..15, of the 32-key block;
+//   * outputs transposed, O^T = V^T P^T: B is P straight from the score
+//     accumulators, 16 keys per product: k slots 0..3 hold keys 4 (l/32) + 0..3, slots
+//     4..7 keys 8 + 4 (l/32) + 0..3 of the 16-key block; A is V^T with the same key
+//     order, two 8-byte reads from the dimension-major LDS tile.
+// LDS tiles are XOR-swizzled in 16-byte chunks (K: by key % 16, V: by dim % 8) so
+// those reads hit distinct banks.  Softmax uses a lazily moved reference (rows
+// rescale only when their maximum grows by more than 2^8).
+#include "relay_device.hpp"
+#include "relay_internal.hpp"
+
+namespace relay {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace mf {
+constexpr int D = 128;
+constexpr int kRowsPerWave = 32;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kKB = 64;                       // keys per step
+constexpr int kTileBytes = kKB * D * 2;       // one K or V tile (bf16)
+constexpr int kBufBytes = 2 * kTileBytes;     // K then V
+constexpr int kChunks = kTileBytes / 16 / kThreads;  // 16-byte chunks per thread per tile
+}  // namespace mf
+
+static_assert(kSysMfmaRows == mf::kRowsPerWave * mf::kWaves, "rows per workgroup");
+constexpr size_t kSysMfmaLds = 2 * (size_t)mf::kBufBytes;
+
+// Staging registers of one step's tiles.
+struct MfStage {
+  u32x4 k[mf::kChunks];
+  u32x4 v[mf::kChunks];
+};
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// Fetches the K / V tiles of the step whose first key is key0 into registers.  K rows
+// past the keys are clamped (their scores are masked); V tiles past the last are
+// clamped and the values of keys >= sys_len zeroed (padding must not reach an output
+// through 0 * NaN).
+__device__ __forceinline__ void mf_fetch(MfStage& st, const char* kbase, const char* vbase, int key0, int Ls,
+                                         int ntile) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < mf::kChunks; ++j) {
+    const int i = tid + mf::kThreads * j;
+    const int key = min(key0 + (i >> 4), Ls - 1);
+    st.k[j] = ld16(kbase + (size_t)key * mf::D * 2 + (i & 15) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < mf::kChunks; ++j) {
+    const int i = tid + mf::kThreads * j;
+    const int tile = key0 / kTile + (i >> 8);
+    const int d = (i & 255) >> 1, half = i & 1;
+    st.v[j] = ld16(vbase + (size_t)min(tile, ntile - 1) * (mf::D * kTile * 2) + d * (kTile * 2) + half * 16);
+    const int nvalid = Ls - (tile * kTile + half * 8);  // keys of this chunk that exist
+    if (nvalid < 8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t w = st.v[j][e];
+        if (2 * e >= nvalid) w &= 0xFFFF0000u;
+        if (2 * e + 1 >= nvalid) w &= 0x0000FFFFu;
+        st.v[j][e] = w;
+      }
+    }
+  }
+}
+
+// Writes staged tiles to an LDS buffer (swizzled).
+__device__ __forceinline__ void mf_store(const MfStage& st, char* buf) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < mf::kChunks; ++j) {
+    const int i = tid + mf::kThreads * j;
+    const int key = i >> 4, c = i & 15;
+    *reinterpret_cast<u32x4*>(buf + key * 256 + ((c ^ (key & 15)) << 4)) = st.k[j];
+  }
+#pragma unroll
+  for (int j = 0; j < mf::kChunks; ++j) {
+    const int i = tid + mf::kThreads * j;
+    const int tile = i >> 8, d = (i & 255) >> 1, half = i & 1;
+    const int c = 2 * tile + half;  // 8-key chunk of the 64-key row
+    *reinterpret_cast<u32x4*>(buf + mf::kTileBytes + d * 128 + ((c ^ (d & 7)) << 4)) = st.v[j];
+  }
+}
+
+__global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int r32 = lane & 31, hh = lane >> 5;
+
+  // workgroup -> (row block, chunk, KV head); the row blocks of one (head, chunk) run
+  // on one XCD (hardware places workgroup i on XCD i % 8) so the chunk's K/V are
+  // fetched from HBM once and from that XCD's L2 after
+  const int total = gridDim.x;
+  int li = blockIdx.x;
+  if (a.xcd_remap) li = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int rb = li % a.row_blocks;
+  const int grp = li / a.row_blocks;
+  const int chunk = grp % a.n_chunks;
+  const int h = grp / a.n_chunks;
+
+  const int Ls = a.sys_len;
+  const int M = a.total_q * a.group;
+  const int key_begin = chunk * a.chunk_len;
+  const int key_end = min(key_begin + a.chunk_len, Ls);
+  const int nsteps = (key_end - key_begin + mf::kKB - 1) / mf::kKB;
+  const int ntile = (Ls + kTile - 1) / kTile;
+  const char* kbase = static_cast<const char*>(a.sys_k) + (size_t)h * Ls * mf::D * 2;
+  const char* vbase = static_cast<const char*>(a.sys_v) + (size_t)h * ntile * mf::D * kTile * 2;
+
+  // this lane's query row (B operand of S^T: 8 consecutive dims of 16 per product)
+  const int m = rb * kSysMfmaRows + wave * mf::kRowsPerWave + r32;
+  const bool row_ok = m < M;
+  const int t = m / a.group, gi = m % a.group;
+  const size_t qrow = (size_t)t * a.num_q_heads + (size_t)h * a.group + gi;
+  u32x4 qf[mf::D / 16];
+  {
+    const char* qp = static_cast<const char*>(a.q) + qrow * mf::D * 2 + 16 * hh;
+#pragma unroll
+    for (int kk = 0; kk < mf::D / 16; ++kk) qf[kk] = row_ok ? ld16(qp + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  f32x16 o[mf::D / 32];
+#pragma unroll
+  for (int db = 0; db < mf::D / 32; ++db) o[db] = f32x16{};
+  float mrow = neg_inf(), lsum = 0.f;
+
+  MfStage stage;
+  mf_fetch(stage, kbase, vbase, key_begin, Ls, ntile);
+  mf_store(stage, lds_raw);
+  __syncthreads();
+
+  for (int s = 0; s < nsteps; ++s) {
+    const int key0 = key_begin + s * mf::kKB;
+    const char* buf = lds_raw + (s & 1) * mf::kBufBytes;
+    const bool more = s + 1 < nsteps;
+    if (more) mf_fetch(stage, kbase, vbase, key0 + mf::kKB, Ls, ntile);
+
+    // ---- scores of the 64 keys: two 32-key blocks
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      sacc[kb2] = f32x16{};
+      const int key = 32 * kb2 + r32;
+      const char* krow = buf + key * 256;
+#pragma unroll
+      for (int kk = 0; kk < mf::D / 16; ++kk) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(krow + (((2 * kk + hh) ^ (key & 15)) << 4));
+        sacc[kb2] = mfma32(ka, qf[kk], sacc[kb2]);
+      }
+    }
+    float sc[32];
+    const int lim = key_end - key0;  // keys [0, lim) of the step exist
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = 32 * kb2 + 8 * (j >> 2) + 4 * hh + (j & 3);
+        sc[16 * kb2 + j] = key < lim ? sacc[kb2][j] * a.scale_log2 : neg_inf();
+      }
+    }
+    // ---- online softmax (lanes l and l ^ 32 hold the same row)
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, sc[i]);
+    {
+      float x, y;
+      swap32(mx, x, y);
+      mx = fmaxf(x, y);
+    }
+    const bool grow = mx > mrow + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mx : mrow;
+      const float alpha = grow ? fast_exp2(mrow - m_new) : 1.f;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < mf::D / 32; ++db) o[db] *= alpha;
+      mrow = m_new;
+    }
+    const float m_use = (mrow == neg_inf()) ? 0.f : mrow;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      sc[i] = fast_exp2(sc[i] - m_use);
+      lsum += sc[i];
+    }
+    // ---- P (bf16) per 16-key block, then O^T += V^T P^T
+    u32x4 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const float* p = sc + 16 * (kb >> 1) + 8 * (kb & 1);
+      pb[kb] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                     pack_bf16x2(p[6], p[7])};
+    }
+    const char* vt = buf + mf::kTileBytes;
+#pragma unroll
+    for (int db = 0; db < mf::D / 32; ++db) {
+      const int d = 32 * db + r32;
+      const char* vrow = vt + d * 128 + 8 * hh;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow + (((2 * kb) ^ (d & 7)) << 4));
+        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + (((2 * kb + 1) ^ (d & 7)) << 4));
+        o[db] = mfma32(u32x4{v0.x, v0.y, v1.x, v1.y}, pb[kb], o[db]);
+      }
+    }
+    if (more) mf_store(stage, lds_raw + ((s + 1) & 1) * mf::kBufBytes);
+    __syncthreads();
+  }
+
+  // ---- this chunk's partial for the lane's row
+  float lo, hi;
+  swap32(lsum, lo, hi);
+  const float ltot = lo + hi;
+  if (!row_ok) return;
+  const size_t r = (size_t)chunk * a.total_q * a.num_q_heads + qrow;
+  const bool empty = !(ltot > 0.f);
+  const float inv = empty ? 0.f : 1.f / ltot;
+  float* orow = a.o_part + r * mf::D;
+#pragma unroll
+  for (int db = 0; db < mf::D / 32; ++db) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const f32x4 v = {o[db][4 * b] * inv, o[db][4 * b + 1] * inv, o[db][4 * b + 2] * inv, o[db][4 * b + 3] * inv};
+      *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * b + 4 * hh) = v;
+    }
+  }
+  if (hh == 0) a.lse_part[r] = empty ? neg_inf() : (mrow + __builtin_amdgcn_logf(ltot)) * kLn2;
+}
+
+hipError_t launch_sys_attn_mfma(const SysArgs& a, int nwg, hipStream_t stream) {
+  hipLaunchKernelGGL(sys_attn_mfma_kernel, dim3(nwg), dim3(mf::kThreads), kSysMfmaLds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace relay
