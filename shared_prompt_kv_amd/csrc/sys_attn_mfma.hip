@@ -9,9 +9,9 @@
 //
 // Workgroup = (128-row block, key chunk, KV head), 4 waves of 32 rows each.  The
 // chunk's keys stream through LDS in 64-key steps, double-buffered: the next step's
-// K and V tiles are fetched into registers while the current one is computed, then
-// written to the other LDS buffer; one barrier per step.  Every wave reads each tile
-// from LDS, so a tile leaves L2 once per workgroup.
+// K and V tiles load straight into the other LDS buffer (global_load_lds) while the
+// current one is computed; one wait and barrier per step.  Every wave reads each
+// tile from LDS, so a tile leaves L2 once per workgroup.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, 32x32 tiles):
 //   * scores transposed, S^T = K Q^T: A = 32 keys x 16 dims from LDS, B = 16 dims x 32
@@ -45,64 +45,47 @@ constexpr int kChunks = kTileBytes / 16 / kThreads;  // 16-byte chunks per threa
 static_assert(kSysMfmaRows == mf::kRowsPerWave * mf::kWaves, "rows per workgroup");
 constexpr size_t kSysMfmaLds = 2 * (size_t)mf::kBufBytes;
 
-// Staging registers of one step's tiles.
-struct MfStage {
-  u32x4 k[mf::kChunks];
-  u32x4 v[mf::kChunks];
-};
-
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
 }
 
-// Fetches the K / V tiles of the step whose first key is key0 into registers.  K rows
-// past the keys are clamped (their scores are masked); V tiles past the last are
-// clamped and the values of keys >= sys_len zeroed (padding must not reach an output
-// through 0 * NaN).
-__device__ __forceinline__ void mf_fetch(MfStage& st, const char* kbase, const char* vbase, int key0, int Ls,
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Issues the loads of the step whose first key is key0 straight into an LDS buffer:
+// lane i of a wave's load lands at the instruction's LDS base + 16 i, so each lane
+// fetches the global 16 bytes that belong at its position of the swizzled layout.  K
+// rows past the keys are clamped (their scores are masked); V tiles past the last are
+// clamped (mf_zero_tail clears values of keys that do not exist).
+__device__ __forceinline__ void mf_issue(char* buf, const char* kbase, const char* vbase, int key0, int Ls,
                                          int ntile) {
-  const int tid = threadIdx.x;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
 #pragma unroll
   for (int j = 0; j < mf::kChunks; ++j) {
-    const int i = tid + mf::kThreads * j;
-    const int key = min(key0 + (i >> 4), Ls - 1);
-    st.k[j] = ld16(kbase + (size_t)key * mf::D * 2 + (i & 15) * 16);
+    const int base = mf::kThreads * j + kWave * wave;  // first 16-byte position of this load
+    const int p = base + lane;
+    const int key = p >> 4, c = (p & 15) ^ (key & 15);
+    const char* src = kbase + (size_t)min(key0 + key, Ls - 1) * mf::D * 2 + c * 16;
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(buf + base * 16), 16, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < mf::kChunks; ++j) {
-    const int i = tid + mf::kThreads * j;
-    const int tile = key0 / kTile + (i >> 8);
-    const int d = (i & 255) >> 1, half = i & 1;
-    st.v[j] = ld16(vbase + (size_t)min(tile, ntile - 1) * (mf::D * kTile * 2) + d * (kTile * 2) + half * 16);
-    const int nvalid = Ls - (tile * kTile + half * 8);  // keys of this chunk that exist
-    if (nvalid < 8) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t w = st.v[j][e];
-        if (2 * e >= nvalid) w &= 0xFFFF0000u;
-        if (2 * e + 1 >= nvalid) w &= 0x0000FFFFu;
-        st.v[j][e] = w;
-      }
-    }
+    const int base = mf::kThreads * j + kWave * wave;
+    const int p = base + lane;
+    const int d = p >> 3, c = (p & 7) ^ (d & 7);  // row d, 8-key chunk c of the 64
+    const int tile = min(key0 / kTile + (c >> 1), ntile - 1);
+    const char* src = vbase + (size_t)tile * (mf::D * kTile * 2) + d * (kTile * 2) + (c & 1) * 16;
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(buf + mf::kTileBytes + base * 16), 16, 0, 0);
   }
 }
 
-// Writes staged tiles to an LDS buffer (swizzled).
-__device__ __forceinline__ void mf_store(const MfStage& st, char* buf) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < mf::kChunks; ++j) {
-    const int i = tid + mf::kThreads * j;
-    const int key = i >> 4, c = i & 15;
-    *reinterpret_cast<u32x4*>(buf + key * 256 + ((c ^ (key & 15)) << 4)) = st.k[j];
-  }
-#pragma unroll
-  for (int j = 0; j < mf::kChunks; ++j) {
-    const int i = tid + mf::kThreads * j;
-    const int tile = i >> 8, d = (i & 255) >> 1, half = i & 1;
-    const int c = 2 * tile + half;  // 8-key chunk of the 64-key row
-    *reinterpret_cast<u32x4*>(buf + mf::kTileBytes + d * 128 + ((c ^ (d & 7)) << 4)) = st.v[j];
+// Zeroes the V values of keys [nvalid, 64) of a landed step (values of keys past the
+// system prompt must not reach an output through 0 * NaN).
+__device__ __forceinline__ void mf_zero_tail(char* buf, int nvalid) {
+  for (int i = threadIdx.x; i < mf::D * mf::kKB; i += mf::kThreads) {
+    const int d = i / mf::kKB, k = i % mf::kKB;
+    if (k >= nvalid)
+      *reinterpret_cast<uint16_t*>(buf + mf::kTileBytes + d * 128 + (((k >> 3) ^ (d & 7)) << 4) + (k & 7) * 2) = 0;
   }
 }
 
@@ -149,16 +132,19 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
   for (int db = 0; db < mf::D / 32; ++db) o[db] = f32x16{};
   float mrow = neg_inf(), lsum = 0.f;
 
-  MfStage stage;
-  mf_fetch(stage, kbase, vbase, key_begin, Ls, ntile);
-  mf_store(stage, lds_raw);
+  mf_issue(lds_raw, kbase, vbase, key_begin, Ls, ntile);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int s = 0; s < nsteps; ++s) {
     const int key0 = key_begin + s * mf::kKB;
-    const char* buf = lds_raw + (s & 1) * mf::kBufBytes;
+    char* buf = lds_raw + (s & 1) * mf::kBufBytes;
+    if (key0 + mf::kKB > Ls) {  // the last step of the prompt: clear V past its end
+      mf_zero_tail(buf, Ls - key0);
+      __syncthreads();
+    }
     const bool more = s + 1 < nsteps;
-    if (more) mf_fetch(stage, kbase, vbase, key0 + mf::kKB, Ls, ntile);
+    if (more) mf_issue(lds_raw + ((s + 1) & 1) * mf::kBufBytes, kbase, vbase, key0 + mf::kKB, Ls, ntile);
 
     // ---- scores of the 64 keys: two 32-key blocks
     f32x16 sacc[2];
@@ -174,13 +160,18 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
       }
     }
     float sc[32];
-    const int lim = key_end - key0;  // keys [0, lim) of the step exist
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = 32 * kb2 + 8 * (j >> 2) + 4 * hh + (j & 3);
-        sc[16 * kb2 + j] = key < lim ? sacc[kb2][j] * a.scale_log2 : neg_inf();
+      for (int j = 0; j < 16; ++j) sc[16 * kb2 + j] = sacc[kb2][j] * a.scale_log2;
+    }
+    const int lim = key_end - key0;  // keys [0, lim) of the step exist
+    if (lim < mf::kKB) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (32 * kb2 + 8 * (j >> 2) + 4 * hh + (j & 3) >= lim) sc[16 * kb2 + j] = neg_inf();
       }
     }
     // ---- online softmax (lanes l and l ^ 32 hold the same row)
@@ -227,7 +218,7 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
         o[db] = mfma32(u32x4{v0.x, v0.y, v1.x, v1.y}, pb[kb], o[db]);
       }
     }
-    if (more) mf_store(stage, lds_raw + ((s + 1) & 1) * mf::kBufBytes);
+    if (more) __builtin_amdgcn_s_waitcnt(0);  // the next step's tiles have landed
     __syncthreads();
   }
 
