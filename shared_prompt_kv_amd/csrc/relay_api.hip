@@ -47,6 +47,7 @@ struct Plan {
   int sys_mfma = 0;  // sys_mode 2: 1 = sys_attn_mfma (bf16, d = 128), 0 = sys_attn_tiled
   SysConfig sc{};
   int sys_chunks = 0, sys_chunk_len = 0, sys_row_blocks = 0, sys_wgs = 0, xcd_remap = 0;
+  int sys_steps_per_head = 0, sys_total_steps = 0, sys_parts = 0;  // sys_attn_mfma
   int ctx_rt = 1, ctx_split_len = 0, ctx_max_splits = 0, ctx_row_blocks = 0, ctx_wgs = 0;
   int fuse_wgs = 0, launches = 0;
   size_t off_sys_o = 0, off_sys_lse = 0, off_ctx_o = 0, off_ctx_lse = 0, ws_bytes = 0;
@@ -77,7 +78,7 @@ int check_dims(const relay_dims* d, int32_t sys_len) {
   if (!(isfinite(d->scale))) return fail(RELAY_ERR_INVALID, "scale must be finite");
   if (sys_len < 0) return fail(RELAY_ERR_INVALID, "sys_len must be >= 0 (got %d)", sys_len);
   const long long rows = (long long)d->total_q * d->num_q_heads;
-  if (rows * d->head_dim > (1LL << 40) || (long long)d->total_q * (d->num_q_heads / d->num_kv_heads) > (1 << 30))
+  if (rows * d->head_dim > (1LL << 40) || (long long)sys_len * d->num_kv_heads > (1LL << 36) || (long long)d->total_q * (d->num_q_heads / d->num_kv_heads) > (1 << 30))
     return fail(RELAY_ERR_INVALID, "problem too large");
   return RELAY_OK;
 }
@@ -102,29 +103,30 @@ void make_plan(const relay_dims* d, int32_t sys_len, Plan* p) {
       p->sys_mode = 2;
       p->sys_mfma = 1;
       p->sys_row_blocks = ceil_div(M, relay::kSysMfmaRows);
-      // chunks: the count that fills the resident workgroup slots best (whole rounds),
-      // then the fewest (each chunk adds a partial per row to the fusion)
-      const long long groups = (long long)p->sys_row_blocks * d->num_kv_heads;
-      int best_c = 1;
-      double best_eff = -1.0;
-      const int forced = env_int("RELAY_SYS_CHUNK", 0);
-      for (int c = 1; c <= 64; ++c) {
-        const int len = ((ceil_div(sys_len, c) + 63) / 64) * 64;
-        if (c > 1 && len < 256) break;
-        const int cact = ceil_div(sys_len, len);
-        const long long total = groups * cact;
-        const long long rounds = (total + relay::kSysMfmaSlots - 1) / relay::kSysMfmaSlots;
-        const double eff = (double)total / (double)(rounds * relay::kSysMfmaSlots);
-        if (eff > best_eff + 1e-9) {
-          best_eff = eff;
-          best_c = c;
-        }
+      // the 64-key steps of all heads, cut into `parts` equal runs so the row blocks
+      // times the parts fill the resident workgroup slots once
+      p->sys_steps_per_head = ceil_div(sys_len, relay::kSysMfmaStep);
+      const long long S = (long long)p->sys_steps_per_head * d->num_kv_heads;
+      p->sys_total_steps = (int)S;
+      long long parts = relay::kSysMfmaSlots / p->sys_row_blocks;
+      const int forced = env_int("RELAY_SYS_PARTS", 0);
+      if (forced > 0) parts = forced;
+      if (parts < 1) parts = 1;
+      if (parts > S) parts = S;
+      p->sys_parts = (int)parts;
+      // slots: the most parts any one head is spread over
+      int slots = 1;
+      for (int h = 0; h < d->num_kv_heads; ++h) {
+        const long long x0 = (long long)h * p->sys_steps_per_head;
+        const long long x1 = x0 + p->sys_steps_per_head - 1;
+        const int n = relay::lean_part_of(x1, (int)S, (int)parts) - relay::lean_part_of(x0, (int)S, (int)parts) + 1;
+        if (n > slots) slots = n;
       }
-      int len = forced > 0 ? forced : ceil_div(sys_len, best_c);
-      p->sys_chunk_len = ((len + 63) / 64) * 64;
-      p->sys_chunks = ceil_div(sys_len, p->sys_chunk_len);
-      p->sys_wgs = p->sys_row_blocks * p->sys_chunks * d->num_kv_heads;
-      p->xcd_remap = (p->sys_row_blocks > 1 && p->sys_wgs % 8 == 0) ? 1 : 0;
+      p->sys_chunks = slots;
+      p->sys_chunk_len = (int)(((S + parts - 1) / parts) * relay::kSysMfmaStep);  // keys per part
+      const long long wgs = (long long)p->sys_row_blocks * parts;
+      p->sys_wgs = (int)((wgs + 7) / 8 * 8);
+      p->xcd_remap = 1;
     } else {
       p->sys_mode = 2;
       p->sc = relay::sys_config(M);
@@ -152,7 +154,7 @@ void make_plan(const relay_dims* d, int32_t sys_len, Plan* p) {
   const long long cgroups = (long long)p->ctx_max_splits * d->num_kv_heads * d->batch;
   p->ctx_wgs = (int)(8LL * p->ctx_row_blocks * ((cgroups + 7) / 8));
   // ---- fusion
-  p->fuse_wgs = ceil_div(rows, 1024 / d->head_dim);
+  p->fuse_wgs = ceil_div(rows, relay::fuse_rows_per_wg(d->head_dim));
   p->launches = (p->sys_mode == 2 ? 3 : 2);
   // ---- workspace
   size_t off = 0;
@@ -191,6 +193,9 @@ int launch_sys_tiled(const relay_dims* d, const Plan& p, const void* q, const vo
   a.row_blocks = p.sys_row_blocks;
   a.xcd_remap = p.xcd_remap;
   a.scale_log2 = d->scale * kLog2e;
+  a.steps_per_head = p.sys_steps_per_head;
+  a.total_steps = p.sys_total_steps;
+  a.parts = p.sys_parts;
   hipError_t e = p.sys_mfma ? relay::launch_sys_attn_mfma(a, p.sys_wgs, s)
                             : relay::launch_sys_attn_tiled(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s);
   return e == hipSuccess ? RELAY_OK : hip_fail(e, "system attention launch");
@@ -244,7 +249,8 @@ int launch_units(const relay_dims* d, const Plan& p, int what, const void* q, co
 }
 
 int launch_fuse(FuseArgs& a, int head_dim, hipStream_t s) {
-  const long long nwg = (a.n_rows + (1024 / head_dim) - 1) / (1024 / head_dim);
+  const long long per = relay::fuse_rows_per_wg(head_dim);
+  const long long nwg = (a.n_rows + per - 1) / per;
   if (!grid_ok(nwg)) return fail(RELAY_ERR_INVALID, "fusion grid too large");
   hipError_t e = relay::launch_relay_fuse(a, head_dim, (int)nwg, s);
   return e == hipSuccess ? RELAY_OK : hip_fail(e, "relay_fuse launch");

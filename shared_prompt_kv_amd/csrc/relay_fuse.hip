@@ -11,17 +11,21 @@
 // pass: one read of every partial row, one write of the output.
 //
 // Layout: D/4 lanes per row, each owning four consecutive dimensions (one 16-byte
-// load per partial); 256 threads per workgroup.  HBM-bound; the loads of a row's
-// partials are issued in batches of four so a row costs few memory latencies.
+// load per partial); one wave per workgroup, so even a few hundred rows spread over
+// the CUs.  HBM-bound.  One pass: the LSEs and outputs of a batch of partials are
+// loaded together (one memory latency per batch) and folded into a running
+// (max, weight sum, weighted sum) that is rescaled when the max grows.
 #include "relay_device.hpp"
 #include "relay_internal.hpp"
 
 namespace relay {
 
+constexpr int kFuseThreads = 64;
+
 template <int D>
-__global__ __launch_bounds__(256) void relay_fuse_kernel(FuseArgs a) {
-  constexpr int LPR = D / 4;         // lanes per row
-  constexpr int RPW = 256 / LPR;     // rows per workgroup
+__global__ __launch_bounds__(kFuseThreads) void relay_fuse_kernel(FuseArgs a) {
+  constexpr int LPR = D / 4;                // lanes per row
+  constexpr int RPW = kFuseThreads / LPR;   // rows per workgroup
   const long long row = (long long)blockIdx.x * RPW + threadIdx.x / LPR;
   if (row >= a.n_rows) return;
   const int c4 = threadIdx.x % LPR;
@@ -37,47 +41,40 @@ __global__ __launch_bounds__(256) void relay_fuse_kernel(FuseArgs a) {
                                       : a.b_o + ((size_t)(i - a.a_count) * a.n_rows + row) * D;
     return reinterpret_cast<const f32x4*>(base + 4 * c4);
   };
-  // pass 1: the largest LSE and a live partial (16 loads in flight per batch)
-  constexpr int kL = 16;
-  float mx = neg_inf();
-  int live0 = -1;
-  for (int i0 = 0; i0 < n; i0 += kL) {
-    float l[kL];
-#pragma unroll
-    for (int j = 0; j < kL; ++j) l[j] = *lse_at(min(i0 + j, n - 1));
-#pragma unroll
-    for (int j = 0; j < kL; ++j) {
-      if (i0 + j < n && l[j] != neg_inf()) {
-        mx = fmaxf(mx, l[j]);
-        if (live0 < 0) live0 = i0 + j;
-      }
-    }
-  }
-  // pass 2: the weighted sum, 8 output loads in flight per batch; an empty partial
-  // (LSE = -inf, its O possibly never written) reads the live one instead, weight 0
+  // running state in the log2 domain: m = max LSE so far, z = sum of 2^(LSE_i - m),
+  // acc = sum of 2^(LSE_i - m) O_i.  An empty partial (LSE = -inf) has weight 0 and
+  // its O, possibly never written, is selected away rather than multiplied by 0.
   constexpr int kB = 8;
+  float m = neg_inf(), z = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float z = 0.f;
-  if (live0 >= 0) {
-    for (int i0 = 0; i0 < n; i0 += kB) {
-      float l[kB], w[kB];
-      f32x4 o[kB];
+  for (int i0 = 0; i0 < n; i0 += kB) {
+    float l[kB];
+    f32x4 o[kB];
 #pragma unroll
-      for (int j = 0; j < kB; ++j) l[j] = *lse_at(min(i0 + j, n - 1));
-#pragma unroll
-      for (int j = 0; j < kB; ++j) {
-        const bool live = i0 + j < n && l[j] != neg_inf();
-        w[j] = live ? fast_exp2((l[j] - mx) * kLog2e) : 0.f;
-        o[j] = *o_at(live ? i0 + j : live0);
-      }
-#pragma unroll
-      for (int j = 0; j < kB; ++j) {
-        z += w[j];
-        acc += w[j] * o[j];
-      }
+    for (int j = 0; j < kB; ++j) {
+      const int i = min(i0 + j, n - 1);
+      l[j] = *lse_at(i) * kLog2e;
+      o[j] = *o_at(i);
     }
-    acc *= 1.f / z;
+    float bm = m;
+#pragma unroll
+    for (int j = 0; j < kB; ++j)
+      if (i0 + j < n) bm = fmaxf(bm, l[j]);
+    if (bm == neg_inf()) continue;  // nothing live yet
+    const float sc = fast_exp2(m - bm);  // 0 while m = -inf
+    z *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const bool live = i0 + j < n && l[j] != neg_inf();
+      const float w = live ? fast_exp2(l[j] - bm) : 0.f;
+      z += w;
+      const f32x4 wo = w * o[j];
+      acc += live ? wo : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    m = bm;
   }
+  acc *= (z > 0.f) ? 1.f / z : 0.f;
   if (a.out_bf16) {
     uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<char*>(a.out) + ((size_t)row * D + 4 * c4) * 2);
     o[0] = pack_bf16x2(acc.x, acc.y);
@@ -85,14 +82,14 @@ __global__ __launch_bounds__(256) void relay_fuse_kernel(FuseArgs a) {
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + (size_t)row * D + 4 * c4) = acc;
   }
-  if (a.lse_out && c4 == 0) a.lse_out[row] = (live0 < 0) ? neg_inf() : mx + __builtin_amdgcn_logf(z) * kLn2;
+  if (a.lse_out && c4 == 0) a.lse_out[row] = (z > 0.f) ? (m + __builtin_amdgcn_logf(z)) * kLn2 : neg_inf();
 }
 
 hipError_t launch_relay_fuse(const FuseArgs& a, int head_dim, int nwg, hipStream_t stream) {
   if (head_dim == 64)
-    hipLaunchKernelGGL((relay_fuse_kernel<64>), dim3(nwg), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((relay_fuse_kernel<64>), dim3(nwg), dim3(kFuseThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((relay_fuse_kernel<128>), dim3(nwg), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((relay_fuse_kernel<128>), dim3(nwg), dim3(kFuseThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -23,6 +23,13 @@ struct SysArgs {
   int row_blocks;       // ceil(T_q * g / rows per workgroup)
   int xcd_remap;        // 1: grid size is a multiple of 8 and ids are remapped per XCD
   float scale_log2;     // scale * log2(e)
+  // sys_attn_mfma only: the 64-key steps of all KV heads, head after head
+  // (total_steps = H_kv * steps_per_head), are cut into `parts` equal runs; workgroup
+  // (row block, part) streams its run, writing one partial per head it touches into
+  // slot (part - first part of that head) < n_chunks.
+  int steps_per_head;
+  int total_steps;
+  int parts;
 };
 
 // Tile configuration of sys_attn: rt row tiles (16 rows each) per wave, wk waves
@@ -108,13 +115,21 @@ hipError_t launch_sys_attn_tiled(const SysArgs& a, const SysConfig& c, int in_dt
                                  int nwg, hipStream_t stream);
 
 // sys_attn_mfma (bf16, head_dim 128): workgroups of kSysMfmaRows query rows; designed
-// for two workgroups per CU (kSysMfmaSlots resident at once).  chunk_len: a multiple
-// of 64.
+// for two workgroups per CU (kSysMfmaSlots resident at once).
 constexpr int kSysMfmaRows = 128;
 constexpr int kSysMfmaSlots = 512;
+constexpr int kSysMfmaStep = 64;
+
+// The part (of `parts` equal runs over `total` steps) that holds step x.
+inline __host__ __device__ int lean_part_of(long long x, int total, int parts) {
+  return (int)(((x + 1) * parts + total - 1) / total) - 1;
+}
 hipError_t launch_sys_attn_mfma(const SysArgs& a, int nwg, hipStream_t stream);
 hipError_t launch_attn_units(const UnitArgs& a, int ctx_rt, int what, int in_dtype, int head_dim,
                              hipStream_t stream);
+// relay_fuse workgroups hold fuse_rows_per_wg(head_dim) rows (one 64-lane wave, D/4
+// lanes per row).
+inline int fuse_rows_per_wg(int head_dim) { return 256 / head_dim; }
 hipError_t launch_relay_fuse(const FuseArgs& a, int head_dim, int nwg, hipStream_t stream);
 
 

@@ -7,8 +7,8 @@
 // "RelayAttention": the system K/V leave HBM once per batch).  With M in the
 // thousands this is a dense contraction bound by the matrix cores.
 //
-// Workgroup = (128-row block, key chunk, KV head), 4 waves of 32 rows each.  The
-// chunk's keys stream through LDS in 64-key steps, double-buffered: the next step's
+// Workgroup = (128-row block, part of the keys of all heads), 4 waves of 32 rows
+// each.  Its keys stream through LDS in 64-key steps, double-buffered: the next step's
 // K and V tiles load straight into the other LDS buffer (global_load_lds) while the
 // current one is computed; one wait and barrier per step.  Every wave reads each
 // tile from LDS, so a tile leaves L2 once per workgroup.
@@ -95,151 +95,177 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
   const int wave = threadIdx.x / kWave;
   const int r32 = lane & 31, hh = lane >> 5;
 
-  // workgroup -> (row block, chunk, KV head); the row blocks of one (head, chunk) run
-  // on one XCD (hardware places workgroup i on XCD i % 8) so the chunk's K/V are
-  // fetched from HBM once and from that XCD's L2 after
+  // workgroup -> (row block, part).  Part p streams the 64-key steps
+  // [p S / P, (p + 1) S / P) of the S = H_kv * steps_per_head steps of all heads
+  // (every workgroup the same amount of work, whatever the head and row-block counts),
+  // and every row block runs the same parts in step: the workgroups of one part are
+  // consecutive ids, placed on one XCD (hardware puts workgroup i on XCD i % 8, the
+  // remap gives each XCD a contiguous id range), so a K/V tile leaves HBM once and
+  // the other row blocks read it from that XCD's L2.
   const int total = gridDim.x;
   int li = blockIdx.x;
   if (a.xcd_remap) li = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
   const int rb = li % a.row_blocks;
-  const int grp = li / a.row_blocks;
-  const int chunk = grp % a.n_chunks;
-  const int h = grp / a.n_chunks;
+  const int part = li / a.row_blocks;
+  if (part >= a.parts) return;  // padding workgroup (whole workgroup)
+  const int S = a.total_steps, P = a.parts, sph = a.steps_per_head;
+  int sbeg = (int)((long long)part * S / P);
+  const int send = (int)((long long)(part + 1) * S / P);
 
   const int Ls = a.sys_len;
   const int M = a.total_q * a.group;
-  const int key_begin = chunk * a.chunk_len;
-  const int key_end = min(key_begin + a.chunk_len, Ls);
-  const int nsteps = (key_end - key_begin + mf::kKB - 1) / mf::kKB;
   const int ntile = (Ls + kTile - 1) / kTile;
-  const char* kbase = static_cast<const char*>(a.sys_k) + (size_t)h * Ls * mf::D * 2;
-  const char* vbase = static_cast<const char*>(a.sys_v) + (size_t)h * ntile * mf::D * kTile * 2;
-
-  // this lane's query row (B operand of S^T: 8 consecutive dims of 16 per product)
-  const int m = rb * kSysMfmaRows + wave * mf::kRowsPerWave + r32;
+  const int m = rb * kSysMfmaRows + wave * mf::kRowsPerWave + r32;  // this lane's stacked row
   const bool row_ok = m < M;
   const int t = m / a.group, gi = m % a.group;
-  const size_t qrow = (size_t)t * a.num_q_heads + (size_t)h * a.group + gi;
-  u32x4 qf[mf::D / 16];
-  {
-    const char* qp = static_cast<const char*>(a.q) + qrow * mf::D * 2 + 16 * hh;
+
+  // one segment per head the run touches: keys [ls0 * 64, min(ls1 * 64, Ls)) of head h
+  while (sbeg < send) {
+    const int h = sbeg / sph;
+    const int ls0 = sbeg % sph;
+    const int ls1 = min(sph, ls0 + (send - sbeg));
+    sbeg += ls1 - ls0;
+    const int key_begin = ls0 * mf::kKB;
+    const int key_end = min(ls1 * mf::kKB, Ls);
+    const int nsteps = ls1 - ls0;
+    const char* kbase = static_cast<const char*>(a.sys_k) + (size_t)h * Ls * mf::D * 2;
+    const char* vbase = static_cast<const char*>(a.sys_v) + (size_t)h * ntile * mf::D * kTile * 2;
+
+    // this lane's query row (B operand of S^T: 8 consecutive dims of 16 per product)
+    const size_t qrow = (size_t)t * a.num_q_heads + (size_t)h * a.group + gi;
+    u32x4 qf[mf::D / 16];
+    {
+      const char* qp = static_cast<const char*>(a.q) + qrow * mf::D * 2 + 16 * hh;
 #pragma unroll
-    for (int kk = 0; kk < mf::D / 16; ++kk) qf[kk] = row_ok ? ld16(qp + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
-  }
-
-  f32x16 o[mf::D / 32];
-#pragma unroll
-  for (int db = 0; db < mf::D / 32; ++db) o[db] = f32x16{};
-  float mrow = neg_inf(), lsum = 0.f;
-
-  mf_issue(lds_raw, kbase, vbase, key_begin, Ls, ntile);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int s = 0; s < nsteps; ++s) {
-    const int key0 = key_begin + s * mf::kKB;
-    char* buf = lds_raw + (s & 1) * mf::kBufBytes;
-    if (key0 + mf::kKB > Ls) {  // the last step of the prompt: clear V past its end
-      mf_zero_tail(buf, Ls - key0);
-      __syncthreads();
+      for (int kk = 0; kk < mf::D / 16; ++kk) qf[kk] = row_ok ? ld16(qp + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
     }
-    const bool more = s + 1 < nsteps;
-    if (more) mf_issue(lds_raw + ((s + 1) & 1) * mf::kBufBytes, kbase, vbase, key0 + mf::kKB, Ls, ntile);
 
-    // ---- scores of the 64 keys: two 32-key blocks
-    f32x16 sacc[2];
+    f32x16 o[mf::D / 32];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      sacc[kb2] = f32x16{};
-      const int key = 32 * kb2 + r32;
-      const char* krow = buf + key * 256;
-#pragma unroll
-      for (int kk = 0; kk < mf::D / 16; ++kk) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(krow + (((2 * kk + hh) ^ (key & 15)) << 4));
-        sacc[kb2] = mfma32(ka, qf[kk], sacc[kb2]);
+    for (int db = 0; db < mf::D / 32; ++db) o[db] = f32x16{};
+    float mrow = neg_inf(), lsum = 0.f;
+
+    mf_issue(lds_raw, kbase, vbase, key_begin, Ls, ntile);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int s = 0; s < nsteps; ++s) {
+      const int key0 = key_begin + s * mf::kKB;
+      char* buf = lds_raw + (s & 1) * mf::kBufBytes;
+      if (key0 + mf::kKB > Ls) {  // the last step of the prompt: clear V past its end
+        mf_zero_tail(buf, Ls - key0);
+        __syncthreads();
       }
-    }
-    float sc[32];
+      const bool more = s + 1 < nsteps;
+      if (more) mf_issue(lds_raw + ((s + 1) & 1) * mf::kBufBytes, kbase, vbase, key0 + mf::kKB, Ls, ntile);
+
+      // ---- scores of the 64 keys: two 32-key blocks
+      f32x16 sacc[2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        sacc[kb2] = f32x16{};
+        const int key = 32 * kb2 + r32;
+        const char* krow = buf + key * 256;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sc[16 * kb2 + j] = sacc[kb2][j] * a.scale_log2;
-    }
-    const int lim = key_end - key0;  // keys [0, lim) of the step exist
-    if (lim < mf::kKB) {
+        for (int kk = 0; kk < mf::D / 16; ++kk) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(krow + (((2 * kk + hh) ^ (key & 15)) << 4));
+          sacc[kb2] = mfma32(ka, qf[kk], sacc[kb2]);
+        }
+      }
+      float sc[32];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (32 * kb2 + 8 * (j >> 2) + 4 * hh + (j & 3) >= lim) sc[16 * kb2 + j] = neg_inf();
+        for (int j = 0; j < 16; ++j) sc[16 * kb2 + j] = sacc[kb2][j] * a.scale_log2;
       }
-    }
-    // ---- online softmax (lanes l and l ^ 32 hold the same row)
-    float mx = sc[0];
+      const int lim = key_end - key0;  // keys [0, lim) of the step exist
+      if (lim < mf::kKB) {
 #pragma unroll
-    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, sc[i]);
-    {
-      float x, y;
-      swap32(mx, x, y);
-      mx = fmaxf(x, y);
-    }
-    const bool grow = mx > mrow + kLazyRescale;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? mx : mrow;
-      const float alpha = grow ? fast_exp2(mrow - m_new) : 1.f;
-      lsum *= alpha;
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-      for (int db = 0; db < mf::D / 32; ++db) o[db] *= alpha;
-      mrow = m_new;
-    }
-    const float m_use = (mrow == neg_inf()) ? 0.f : mrow;
+          for (int j = 0; j < 16; ++j)
+            if (32 * kb2 + 8 * (j >> 2) + 4 * hh + (j & 3) >= lim) sc[16 * kb2 + j] = neg_inf();
+        }
+      }
+      // ---- online softmax (lanes l and l ^ 32 hold the same row)
+      float mx = sc[0];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      sc[i] = fast_exp2(sc[i] - m_use);
-      lsum += sc[i];
-    }
-    // ---- P (bf16) per 16-key block, then O^T += V^T P^T
-    u32x4 pb[4];
+      for (int i = 1; i < 32; ++i) mx = fmaxf(mx, sc[i]);
+      {
+        float x, y;
+        swap32(mx, x, y);
+        mx = fmaxf(x, y);
+      }
+      const bool grow = mx > mrow + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mx : mrow;
+        const float alpha = grow ? fast_exp2(mrow - m_new) : 1.f;
+        lsum *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const float* p = sc + 16 * (kb >> 1) + 8 * (kb & 1);
-      pb[kb] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                     pack_bf16x2(p[6], p[7])};
-    }
-    const char* vt = buf + mf::kTileBytes;
+        for (int db = 0; db < mf::D / 32; ++db) o[db] *= alpha;
+        mrow = m_new;
+      }
+      const float m_use = (mrow == neg_inf()) ? 0.f : mrow;
 #pragma unroll
-    for (int db = 0; db < mf::D / 32; ++db) {
-      const int d = 32 * db + r32;
-      const char* vrow = vt + d * 128 + 8 * hh;
+      for (int i = 0; i < 32; ++i) {
+        sc[i] = fast_exp2(sc[i] - m_use);
+        lsum += sc[i];
+      }
+      // ---- P (bf16) per 16-key block, then O^T += V^T P^T
+      u32x4 pb[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow + (((2 * kb) ^ (d & 7)) << 4));
-        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + (((2 * kb + 1) ^ (d & 7)) << 4));
-        o[db] = mfma32(u32x4{v0.x, v0.y, v1.x, v1.y}, pb[kb], o[db]);
+        const float* p = sc + 16 * (kb >> 1) + 8 * (kb & 1);
+        pb[kb] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                       pack_bf16x2(p[6], p[7])};
+      }
+      const char* vt = buf + mf::kTileBytes;
+#pragma unroll
+      for (int db = 0; db < mf::D / 32; ++db) {
+        const int d = 32 * db + r32;
+        const char* vrow = vt + d * 128 + 8 * hh;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow + (((2 * kb) ^ (d & 7)) << 4));
+          const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + (((2 * kb + 1) ^ (d & 7)) << 4));
+          o[db] = mfma32(u32x4{v0.x, v0.y, v1.x, v1.y}, pb[kb], o[db]);
+        }
+      }
+      if (more) __builtin_amdgcn_s_waitcnt(0);  // the next step's tiles have landed
+      __syncthreads();  // (also: the buffers are free for the next segment)
+    }
+
+    // ---- this segment's partial for the lane's row, in slot (part - first part of h);
+    // the workgroup holding the head's first step also marks the head's unused slots
+    // empty, so every slot < n_chunks of every row is written
+    float lo, hi;
+    swap32(lsum, lo, hi);
+    const float ltot = lo + hi;
+    if (row_ok) {
+      const int first = lean_part_of((long long)h * sph, S, P);
+      const size_t rows = (size_t)a.total_q * a.num_q_heads;
+      const size_t r = (size_t)(part - first) * rows + qrow;
+      const bool empty = !(ltot > 0.f);
+      const float inv = empty ? 0.f : 1.f / ltot;
+      float* orow = a.o_part + r * mf::D;
+#pragma unroll
+      for (int db = 0; db < mf::D / 32; ++db) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const f32x4 v = {o[db][4 * b] * inv, o[db][4 * b + 1] * inv, o[db][4 * b + 2] * inv,
+                           o[db][4 * b + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * b + 4 * hh) = v;
+        }
+      }
+      if (hh == 0) {
+        a.lse_part[r] = empty ? neg_inf() : (mrow + __builtin_amdgcn_logf(ltot)) * kLn2;
+        if (ls0 == 0) {
+          const int used = lean_part_of((long long)(h + 1) * sph - 1, S, P) - first + 1;
+          for (int sl = used; sl < a.n_chunks; ++sl) a.lse_part[(size_t)sl * rows + qrow] = neg_inf();
+        }
       }
     }
-    if (more) __builtin_amdgcn_s_waitcnt(0);  // the next step's tiles have landed
-    __syncthreads();
   }
-
-  // ---- this chunk's partial for the lane's row
-  float lo, hi;
-  swap32(lsum, lo, hi);
-  const float ltot = lo + hi;
-  if (!row_ok) return;
-  const size_t r = (size_t)chunk * a.total_q * a.num_q_heads + qrow;
-  const bool empty = !(ltot > 0.f);
-  const float inv = empty ? 0.f : 1.f / ltot;
-  float* orow = a.o_part + r * mf::D;
-#pragma unroll
-  for (int db = 0; db < mf::D / 32; ++db) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const f32x4 v = {o[db][4 * b] * inv, o[db][4 * b + 1] * inv, o[db][4 * b + 2] * inv, o[db][4 * b + 3] * inv};
-      *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * b + 4 * hh) = v;
-    }
-  }
-  if (hh == 0) a.lse_part[r] = empty ? neg_inf() : (mrow + __builtin_amdgcn_logf(ltot)) * kLn2;
 }
 
 hipError_t launch_sys_attn_mfma(const SysArgs& a, int nwg, hipStream_t stream) {

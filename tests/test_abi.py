@@ -128,18 +128,26 @@ def test_plan_for_each_config(lib, cfg, sweep):
                      -(-s["max_ctx"] // 16), 1000, s["total_q"], int(s["q_lens"].max()), s["max_ctx"],
                      spec.scale, 1 if spec.dtype == "bf16" else 0, 0)
     plan = R.relay_get_plan(d, spec.sys_len)
-    assert plan["sys_chunks"] * plan["sys_chunk_len"] >= spec.sys_len
-    assert (plan["sys_chunks"] - 1) * plan["sys_chunk_len"] < spec.sys_len
     M = s["total_q"] * spec.group
     if M <= 64:   # single-wave system units, launched together with the context units
+        assert plan["sys_chunks"] * plan["sys_chunk_len"] >= spec.sys_len
+        assert (plan["sys_chunks"] - 1) * plan["sys_chunk_len"] < spec.sys_len
         assert plan["sys_mode"] == 1 and plan["launches"] == 2
         assert plan["sys_row_blocks"] == -(-M // 16)
         groups = spec.num_kv_heads * plan["sys_chunks"]
         assert plan["sys_wgs"] == 8 * plan["sys_row_blocks"] * (-(-groups // 8))
-    else:         # tiled system kernel
+    else:         # matrix-core system kernel: (row block, run of 64-key steps) workgroups
         assert plan["sys_mode"] == 2 and plan["launches"] == 3
-        assert plan["sys_wgs"] == plan["sys_row_blocks"] * plan["sys_chunks"] * spec.num_kv_heads
         assert plan["sys_row_blocks"] * 128 >= M
+        steps = spec.num_kv_heads * -(-spec.sys_len // 64)
+        parts = min(max(512 // plan["sys_row_blocks"], 1), steps)
+        assert plan["sys_wgs"] == -(-plan["sys_row_blocks"] * parts // 8) * 8 <= max(512, plan["sys_wgs"])
+        assert plan["sys_chunk_len"] == -(-steps // parts) * 64
+        # slots: the most runs one head's steps fall into
+        part_of = lambda x: ((x + 1) * parts + steps - 1) // steps - 1
+        sph = steps // spec.num_kv_heads
+        assert plan["sys_chunks"] == max(part_of(h * sph + sph - 1) - part_of(h * sph) + 1
+                                         for h in range(spec.num_kv_heads))
     assert plan["ctx_split_len"] <= 1024
     assert 0 < plan["ctx_wgs"] < 2**31 and 0 < plan["sys_wgs"] < 2**31
 

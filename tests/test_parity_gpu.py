@@ -313,6 +313,27 @@ def test_multi_split_shapes(spec):
     check(a.numpy(), expect, spec.dtype, "multi-split")
 
 
+@pytest.mark.parametrize("parts", [1, 3, 7, 13])
+def test_system_runs_across_heads(parts, monkeypatch):
+    """Matrix-core system step with its key runs forced to cross KV-head boundaries
+    (each run one partial per head it touches, unused slots empty)."""
+    spec = W.config_spec(5).replace(batch=5, sys_len=290, ctx_lo=64, ctx_hi=300)
+    monkeypatch.setenv("RELAY_SYS_PARTS", str(parts))
+    say(f"[parity] system runs across heads, parts={parts} {spec}")
+    w = workload(spec)
+    t = upload(w)
+    plan = R.relay_get_plan(R.dims_of(t), t["sys_len"])
+    assert plan["sys_mode"] == 2
+    o, lse = R.relay_sys_attn(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], R.dims_of(t))
+    out = R.decode_workload(t)
+    torch.cuda.synchronize()
+    ro, rl = oracle.Problem(w).system_part()
+    check(o.cpu().numpy(), ro, spec.dtype, "o_sys")
+    check(lse.cpu().numpy(), rl, spec.dtype, "lse_sys")
+    ref, _ = oracle.Problem(w).attention()
+    check(out.cpu().numpy(), ref, spec.dtype, "out")
+
+
 def test_garbage_workspace():
     """Whatever the workspace held (here random bytes), a call gives the same bits."""
     spec = SCHED_SPECS[0]
