@@ -154,7 +154,7 @@ void make_plan(const relay_dims* d, int32_t sys_len, Plan* p) {
   const long long cgroups = (long long)p->ctx_max_splits * d->num_kv_heads * d->batch;
   p->ctx_wgs = (int)(8LL * p->ctx_row_blocks * ((cgroups + 7) / 8));
   // ---- fusion
-  p->fuse_wgs = ceil_div(rows, relay::fuse_rows_per_wg(d->head_dim));
+  p->fuse_wgs = ceil_div(rows, relay::fuse_rows_per_wg(d->head_dim, rows));
   p->launches = (p->sys_mode == 2 ? 3 : 2);
   // ---- workspace
   size_t off = 0;
@@ -249,7 +249,7 @@ int launch_units(const relay_dims* d, const Plan& p, int what, const void* q, co
 }
 
 int launch_fuse(FuseArgs& a, int head_dim, hipStream_t s) {
-  const long long per = relay::fuse_rows_per_wg(head_dim);
+  const long long per = relay::fuse_rows_per_wg(head_dim, a.n_rows);
   const long long nwg = (a.n_rows + per - 1) / per;
   if (!grid_ok(nwg)) return fail(RELAY_ERR_INVALID, "fusion grid too large");
   hipError_t e = relay::launch_relay_fuse(a, head_dim, (int)nwg, s);

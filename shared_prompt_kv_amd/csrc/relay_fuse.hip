@@ -11,8 +11,8 @@
 // pass: one read of every partial row, one write of the output.
 //
 // Layout: D/4 lanes per row, each owning four consecutive dimensions (one 16-byte
-// load per partial); one wave per workgroup, so even a few hundred rows spread over
-// the CUs.  HBM-bound.  One pass: the LSEs and outputs of a batch of partials are
+// load per partial); one wave per workgroup when there are few rows, so a few hundred
+// rows still spread over the CUs, four when there are many.  HBM-bound.  One pass: the LSEs and outputs of a batch of partials are
 // loaded together (one memory latency per batch) and folded into a running
 // (max, weight sum, weighted sum) that is rescaled when the max grows.
 #include "relay_device.hpp"
@@ -20,12 +20,10 @@
 
 namespace relay {
 
-constexpr int kFuseThreads = 64;
-
-template <int D>
-__global__ __launch_bounds__(kFuseThreads) void relay_fuse_kernel(FuseArgs a) {
-  constexpr int LPR = D / 4;                // lanes per row
-  constexpr int RPW = kFuseThreads / LPR;   // rows per workgroup
+template <int D, int THREADS>
+__global__ __launch_bounds__(THREADS) void relay_fuse_kernel(FuseArgs a) {
+  constexpr int LPR = D / 4;           // lanes per row
+  constexpr int RPW = THREADS / LPR;   // rows per workgroup
   const long long row = (long long)blockIdx.x * RPW + threadIdx.x / LPR;
   if (row >= a.n_rows) return;
   const int c4 = threadIdx.x % LPR;
@@ -86,10 +84,14 @@ __global__ __launch_bounds__(kFuseThreads) void relay_fuse_kernel(FuseArgs a) {
 }
 
 hipError_t launch_relay_fuse(const FuseArgs& a, int head_dim, int nwg, hipStream_t stream) {
-  if (head_dim == 64)
-    hipLaunchKernelGGL((relay_fuse_kernel<64>), dim3(nwg), dim3(kFuseThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((relay_fuse_kernel<128>), dim3(nwg), dim3(kFuseThreads), 0, stream, a);
+  const bool wide = fuse_threads(head_dim, a.n_rows) == 256;
+  if (head_dim == 64) {
+    if (wide) hipLaunchKernelGGL((relay_fuse_kernel<64, 256>), dim3(nwg), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((relay_fuse_kernel<64, 64>), dim3(nwg), dim3(64), 0, stream, a);
+  } else {
+    if (wide) hipLaunchKernelGGL((relay_fuse_kernel<128, 256>), dim3(nwg), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((relay_fuse_kernel<128, 64>), dim3(nwg), dim3(64), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

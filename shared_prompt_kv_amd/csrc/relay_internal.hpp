@@ -127,9 +127,12 @@ inline __host__ __device__ int lean_part_of(long long x, int total, int parts) {
 hipError_t launch_sys_attn_mfma(const SysArgs& a, int nwg, hipStream_t stream);
 hipError_t launch_attn_units(const UnitArgs& a, int ctx_rt, int what, int in_dtype, int head_dim,
                              hipStream_t stream);
-// relay_fuse workgroups hold fuse_rows_per_wg(head_dim) rows (one 64-lane wave, D/4
-// lanes per row).
-inline int fuse_rows_per_wg(int head_dim) { return 256 / head_dim; }
+// relay_fuse workgroup size: one wave, or four once there are enough rows for two
+// four-wave workgroups per CU (D/4 lanes per row).
+inline int fuse_threads(int head_dim, long long n_rows) {
+  return n_rows >= 2LL * 256 * (256 / (head_dim / 4)) ? 256 : 64;
+}
+inline int fuse_rows_per_wg(int head_dim, long long n_rows) { return fuse_threads(head_dim, n_rows) / (head_dim / 4); }
 hipError_t launch_relay_fuse(const FuseArgs& a, int head_dim, int nwg, hipStream_t stream);
 
 
