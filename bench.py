@@ -99,7 +99,9 @@ def sys_scaling(torch, relay, steps):
             E = 2 if spec.dtype == "bf16" else 4
             print(json.dumps({"shape": name, "batch": B, "sys_len": spec.sys_len,
                               "rows_per_kv_head": w.total_q * spec.group,
-                              "kernel": "sys_attn" if plan["sys_mode"] == 1 else "sys_attn_tiled",
+                              "kernel": ("sys_attn" if plan["sys_mode"] == 1 else
+                                         "sys_attn_mfma" if (spec.dtype == "bf16" and spec.head_dim == 128)
+                                         else "sys_attn_tiled"),
                               "dispatches": 3 + steps,
                               "sys_kv_bytes": 2 * spec.num_kv_heads * spec.head_dim * E * spec.sys_len,
                               "us_per_call": round(1000 * e0.elapsed_time(e1) / steps, 2)}), flush=True)
