@@ -120,12 +120,12 @@ template <> struct PFrag<float> {
   float p[8];
 };
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  // Round to nearest even (gfx950 converts in hardware).
-  __bf16 a = static_cast<__bf16>(lo);
-  __bf16 b = static_cast<__bf16>(hi);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+  // Round to nearest even, both halves in one v_cvt_pk_bf16_f32 (gfx950).
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ inline float bf16_lo_as_float(uint32_t w) { return __uint_as_float(w << 16); }

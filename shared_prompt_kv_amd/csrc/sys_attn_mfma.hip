@@ -52,6 +52,16 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// K rows are stored in LDS with the middle two 4-key groups of every 16 swapped (row
+// 4..7 holds key 8..11 and row 8..11 key 4..7).  The score accumulators then give the
+// lanes l / 32 = 0 the keys 0..7 and lanes l / 32 = 1 the keys 8..15 of each 16-key
+// block, in order: exactly the k slots of the P.V product's B operand, so V^T for a
+// lane is one contiguous 16-byte read of the dimension-major V tile.
+__device__ __forceinline__ int mf_key_of_row(int row) {
+  const int q = row & 15;
+  return (row & ~15) + ((q >= 4 && q < 8) ? q + 4 : ((q >= 8 && q < 12) ? q - 4 : q));
+}
+
 // Issues the loads of the step whose first key is key0 straight into an LDS buffer:
 // lane i of a wave's load lands at the instruction's LDS base + 16 i, so each lane
 // fetches the global 16 bytes that belong at its position of the swizzled layout.  K
@@ -64,8 +74,8 @@ __device__ __forceinline__ void mf_issue(char* buf, const char* kbase, const cha
   for (int j = 0; j < mf::kChunks; ++j) {
     const int base = mf::kThreads * j + kWave * wave;  // first 16-byte position of this load
     const int p = base + lane;
-    const int key = p >> 4, c = (p & 15) ^ (key & 15);
-    const char* src = kbase + (size_t)min(key0 + key, Ls - 1) * mf::D * 2 + c * 16;
+    const int row = p >> 4, c = (p & 15) ^ (row & 15);
+    const char* src = kbase + (size_t)min(key0 + mf_key_of_row(row), Ls - 1) * mf::D * 2 + c * 16;
     __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(buf + base * 16), 16, 0, 0);
   }
 #pragma unroll
@@ -115,6 +125,10 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
   const int Ls = a.sys_len;
   const int M = a.total_q * a.group;
   const int ntile = (Ls + kTile - 1) / kTile;
+  // scores are taken scale-free with the sign folded in: s' = sign(scale) q.k, and
+  // p = 2^(|scale| s' - m)
+  const bool negative_scale = a.scale_log2 < 0.f;
+  const float scale = negative_scale ? -a.scale_log2 : a.scale_log2;
   const int m = rb * kSysMfmaRows + wave * mf::kRowsPerWave + r32;  // this lane's stacked row
   const bool row_ok = m < M;
   const int t = m / a.group, gi = m % a.group;
@@ -172,29 +186,33 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
           sacc[kb2] = mfma32(ka, qf[kk], sacc[kb2]);
         }
       }
+      // raw scores; lane (row, hh) holds keys 32 kb2 + 16 (j / 8) + 8 hh + j % 8
       float sc[32];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sc[16 * kb2 + j] = sacc[kb2][j] * a.scale_log2;
+        for (int j = 0; j < 16; ++j) sc[16 * kb2 + j] = sacc[kb2][j];
+      }
+      if (negative_scale) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) sc[i] = -sc[i];
       }
       const int lim = key_end - key0;  // keys [0, lim) of the step exist
-      if (lim < mf::kKB) {
+      const bool partial = lim < mf::kKB;
+      if (partial) {
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (32 * kb2 + 8 * (j >> 2) + 4 * hh + (j & 3) >= lim) sc[16 * kb2 + j] = neg_inf();
-        }
+        for (int i = 0; i < 32; ++i)
+          if (16 * (i >> 3) + 8 * hh + (i & 7) >= lim) sc[i] = neg_inf();
       }
-      // ---- online softmax (lanes l and l ^ 32 hold the same row)
+      // ---- online softmax on scale-free scores (lanes l and l ^ 32 hold the same row):
+      // the reference m is kept scaled, p = 2^(|scale| s - m) is one FMA and an exp
       float mx = sc[0];
 #pragma unroll
       for (int i = 1; i < 32; ++i) mx = fmaxf(mx, sc[i]);
       {
         float x, y;
         swap32(mx, x, y);
-        mx = fmaxf(x, y);
+        mx = fmaxf(x, y) * scale;
       }
       const bool grow = mx > mrow + kLazyRescale;
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -207,15 +225,20 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
       }
       const float m_use = (mrow == neg_inf()) ? 0.f : mrow;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        sc[i] = fast_exp2(sc[i] - m_use);
-        lsum += sc[i];
+      for (int i = 0; i < 32; ++i) sc[i] = fast_exp2(__builtin_fmaf(sc[i], scale, -m_use));
+      if (partial) {  // exact zeros for keys that do not exist (also when scale is 0)
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          if (16 * (i >> 3) + 8 * hh + (i & 7) >= lim) sc[i] = 0.f;
       }
-      // ---- P (bf16) per 16-key block, then O^T += V^T P^T
+#pragma unroll
+      for (int i = 0; i < 32; ++i) lsum += sc[i];
+      // ---- P (bf16) per 16-key block kb: k slots 0..7 = keys 0..7 (lanes hh = 0),
+      // 8..15 = keys 8..15 (hh = 1), i.e. sc[8 kb .. 8 kb + 7]; then O^T += V^T P^T
       u32x4 pb[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const float* p = sc + 16 * (kb >> 1) + 8 * (kb & 1);
+        const float* p = sc + 8 * kb;
         pb[kb] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                        pack_bf16x2(p[6], p[7])};
       }
@@ -223,12 +246,11 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
 #pragma unroll
       for (int db = 0; db < mf::D / 32; ++db) {
         const int d = 32 * db + r32;
-        const char* vrow = vt + d * 128 + 8 * hh;
+        const char* vrow = vt + d * 128;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow + (((2 * kb) ^ (d & 7)) << 4));
-          const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + (((2 * kb + 1) ^ (d & 7)) << 4));
-          o[db] = mfma32(u32x4{v0.x, v0.y, v1.x, v1.y}, pb[kb], o[db]);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(vrow + (((2 * kb + hh) ^ (d & 7)) << 4));
+          o[db] = mfma32(v, pb[kb], o[db]);
         }
       }
       if (more) __builtin_amdgcn_s_waitcnt(0);  // the next step's tiles have landed
