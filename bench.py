@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--sys-scaling", action="store_true",
                     help="only run the system-attention step over batch sweeps of the Llama2-7B and "
                          "Llama-3-8B shapes (for counters: system-KV bytes read vs batch size)")
+    ap.add_argument("--batch-sweep", action="store_true",
+                    help="only run relay vs the no-relay baseline (prefix-shared system pages) over "
+                         "batch sizes of the Llama2-7B shape (one JSON line per batch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run torch's device copy of COPY_BYTES, 10 times (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -67,6 +70,7 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes": COPY_BYTES, "dispatches": 10}), flush=True)
 
 
+BATCH_SWEEP = (1, 2, 4, 8, 16, 32, 64, 128, 256)
 SYS_SCALING = (("llama2_7b_mha", 2, (1, 4, 8, 16, 32)), ("llama3_8b_gqa", 4, (1, 4, 16, 64, 256)))
 
 
@@ -205,7 +209,7 @@ def clone_set(torch, t):
     return {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
 
 
-def measure(torch, relay, w, steps, warmup, per_kernel=True, graph=True):
+def measure(torch, relay, w, steps, warmup, per_kernel=True, graph=True, prep=None):
     """Times decode steps over rotating input copies.
 
     graph: the steps captured in one HIP graph (a full rotation over the copies)
@@ -215,6 +219,8 @@ def measure(torch, relay, w, steps, warmup, per_kernel=True, graph=True):
     between its launches (eager).
     """
     t0 = relay.to_device(w, "cuda")
+    if prep is not None:  # e.g. the no-relay baseline's inputs
+        t0 = prep(t0)
     work = work_of(w)
     n_sets = max(2, math.ceil(3 * MALL_BYTES / max(work["step_bytes"], 1)))
     n_sets = min(n_sets, 16)
@@ -338,21 +344,35 @@ def cpu_baseline(w, budget_cpu_s):
                       f"tokens in {elapsed:.2f} s wall on {cores} threads"}
 
 
-def point(torch, relay, spec, args):
+def point(torch, relay, spec, args, with_baseline=False):
     """One workload measured like the main line (fewer steps): throughput and
-    roofline fractions."""
+    roofline fractions; with_baseline adds the no-relay baseline's step time."""
     w = workloads_generate(spec)
     rr = measure(torch, relay, w, min(args.steps, 50), min(args.warmup, 10))
     print(f"[bench] {spec.name}: {1000 * rr['ms_per_step']:.2f} us/step", file=sys.stderr, flush=True)
     m = rr["ms_per_step"]
     work = rr["work"]
     peak = (BF16_PEAK_TFLOPS if spec.dtype == "bf16" else FP32_PEAK_TFLOPS) * 1e12
-    return {"workload": spec.name, "qtok_s": round(w.total_q / (m * 1e-3), 1),
-            "us_per_step": round(1000 * m, 2), "eager_us_per_step": round(1000 * rr["eager_ms_per_step"], 2),
-            "hbm_frac": round(work["step_bytes"] / (m * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-            "mfma_frac": round(work["step_flops"] / (m * 1e-3) / peak, 4),
-            "kernel_us": {k: round(v, 2) for k, v in rr["kernel_us"].items()},
-            "sys_mode": rr["plan"]["sys_mode"]}
+    out = {"workload": spec.name, "qtok_s": round(w.total_q / (m * 1e-3), 1),
+           "us_per_step": round(1000 * m, 2), "eager_us_per_step": round(1000 * rr["eager_ms_per_step"], 2),
+           "hbm_frac": round(work["step_bytes"] / (m * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+           "mfma_frac": round(work["step_flops"] / (m * 1e-3) / peak, 4),
+           "kernel_us": {k: round(v, 2) for k, v in rr["kernel_us"].items()},
+           "sys_mode": rr["plan"]["sys_mode"]}
+    if with_baseline:
+        out.update(no_relay_baseline(torch, relay, w, args, m))
+    return out
+
+
+def no_relay_baseline(torch, relay, w, args, relay_ms):
+    """The same decode step without relay: every request's block table starts with
+    the shared system pages and the context step reads them once per request."""
+    from shared_prompt_kv_amd import baseline
+    rb = measure(torch, relay, w, min(args.steps, 50), min(args.warmup, 10), per_kernel=False,
+                 prep=baseline.prefix_shared)
+    bm = rb["ms_per_step"]
+    print(f"[bench] {w.spec.name} no-relay baseline: {1000 * bm:.2f} us/step", file=sys.stderr, flush=True)
+    return {"no_relay_us_per_step": round(1000 * bm, 2), "relay_speedup": round(bm / relay_ms, 3)}
 
 
 def workloads_generate(spec):
@@ -377,6 +397,16 @@ def main():
     if args.sys_scaling:
         relay.load_library()
         sys_scaling(torch, relay, min(args.steps, 20))
+        return
+    if args.batch_sweep:
+        relay.load_library()
+        for B in BATCH_SWEEP:
+            spec = workloads.config_spec(2, 0).replace(batch=B)
+            r = point(torch, relay, spec, args, with_baseline=True)
+            print(json.dumps({"shape": "llama2_7b_mha", "batch": B, "sys_len": spec.sys_len,
+                              "relay_us_per_step": r["us_per_step"], "qtok_s": r["qtok_s"],
+                              "no_relay_us_per_step": r["no_relay_us_per_step"],
+                              "relay_speedup": r["relay_speedup"]}), flush=True)
         return
     relay.load_library()
     spec = workloads.config_spec(args.config, args.sweep_index)
@@ -423,9 +453,13 @@ def main():
     }
     if not args.no_sweep and args.config == 2:
         line["sweep"] = {"workload": "llama30b_mha (batch 32, 52 heads, ctx 128)",
-                         "points": [dict(sys_len=Ls, **point(torch, relay, workloads.config_spec(3, i), args))
+                         "points": [dict(sys_len=Ls, **point(torch, relay, workloads.config_spec(3, i), args,
+                                                             with_baseline=True))
                                     for i, Ls in enumerate(workloads.CONFIG3_SYS_LENS)]}
-        line["other_configs"] = [point(torch, relay, workloads.config_spec(c, 0), args) for c in (1, 4, 5)]
+        line["other_configs"] = [point(torch, relay, workloads.config_spec(c, 0), args, with_baseline=True)
+                                 for c in (1, 4, 5)]
+    if not args.no_sweep:
+        line["no_relay_baseline"] = no_relay_baseline(torch, relay, w, args, ms)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
