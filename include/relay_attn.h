@@ -223,6 +223,53 @@ int relay_fuse(int64_t n_rows, int32_t head_dim, const float* o_sys, const float
 int relay_validate(const relay_dims* dims, const int32_t* h_block_tables,
                    const int32_t* h_ctx_lens, const int32_t* h_cu_q_lens, int32_t sys_len);
 
+/*
+ * ---- The step before the path: position embedding and KV append --------------
+ *
+ * The system K/V are prefilled offline at positions 0 .. L_s - 1; a request's own
+ * tokens are placed after them, context token j at absolute position L_s + j
+ * (atyun.com article, section "RelayAttention": context positions offset by the
+ * system prompt's length; linnk.ai summary, section "Deeper Inquiries").  The
+ * embedding is rotary (RoPE), rotate-half form: for i < d/2 the pair
+ * (x[i], x[i + d/2]) is rotated by the angle p * base^(-2i/d), applied to queries and
+ * keys, not values.
+ */
+
+/*
+ * Builds the cos/sin table that relay_rope_append / relay_rope_system read:
+ * cos_sin float32 [max_pos, head_dim], row p = cos(p f_i) for i < d/2, then
+ * sin(p f_i), f_i = base^(-2i/d); angles reduced in fp64 on the device.  Caller
+ * owns the buffer.  head_dim 64 or 128; max_pos >= 1; base > 0.
+ */
+int relay_rope_table(float* cos_sin, int32_t max_pos, int32_t head_dim, float base, void* stream);
+
+/*
+ * Appends a decode step's new tokens: for new token t of request b (rows
+ * cu_q_lens[b] .. cu_q_lens[b+1]-1, or row b when cu_q_lens is NULL) at context
+ * position p = c_b - n_b + t_local and absolute position sys_len + p:
+ *   q_out[t, h]  = RoPE(q_new[t, h], sys_len + p)            h < H_q
+ *   K page slot  = RoPE(k_new[t, hk], sys_len + p)           hk < H_kv
+ *   V page slot  = v_new[t, hk]
+ * at page block_tables[b][p / 16], slot p % 16 of ctx_k_pages [num_blocks, H_kv,
+ * 16, d] / ctx_v_pages [num_blocks, H_kv, d, 16].  q_new / q_out [T_q, H_q, d] and
+ * k_new / v_new [T_q, H_kv, d] are in_dtype (q_out may alias q_new).  ctx_lens
+ * already include the new tokens.  cos_sin: relay_rope_table's table, max_pos rows;
+ * a row whose position is >= max_pos, or whose page id is out of range, is not
+ * written.  Then relay_attn_decode(q_out, ...) runs the relay path.
+ */
+int relay_rope_append(const relay_dims* dims, int32_t sys_len, const void* q_new,
+                      const void* k_new, const void* v_new, const float* cos_sin,
+                      int32_t max_pos, const int32_t* block_tables, const int32_t* ctx_lens,
+                      const int32_t* cu_q_lens, void* q_out, void* ctx_k_pages,
+                      void* ctx_v_pages, void* stream);
+
+/*
+ * The offline prefill's position embedding of the system keys: sys_k [H_kv, L_s, d]
+ * (in_dtype) rotated in place at positions 0 .. sys_len - 1.  sys_len <= max_pos.
+ */
+int relay_rope_system(int32_t num_kv_heads, int32_t head_dim, int32_t sys_len, int32_t in_dtype,
+                      void* sys_k, const float* cos_sin, int32_t max_pos, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -504,4 +504,64 @@ int relay_validate(const relay_dims* dims, const int32_t* h_block_tables, const 
   return RELAY_OK;
 }
 
+int relay_rope_table(float* cos_sin, int32_t max_pos, int32_t head_dim, float base, void* stream) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(RELAY_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", head_dim);
+  if (max_pos < 1 || !(base > 0.f) || !isfinite(base)) return fail(RELAY_ERR_INVALID, "max_pos >= 1 and base > 0 required");
+  if (!cos_sin) return fail(RELAY_ERR_INVALID, "cos_sin is NULL");
+  hipError_t e = relay::launch_rope_table(cos_sin, max_pos, head_dim, (double)base, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RELAY_OK : hip_fail(e, "rope table launch");
+}
+
+int relay_rope_append(const relay_dims* dims, int32_t sys_len, const void* q_new, const void* k_new,
+                      const void* v_new, const float* cos_sin, int32_t max_pos, const int32_t* block_tables,
+                      const int32_t* ctx_lens, const int32_t* cu_q_lens, void* q_out, void* ctx_k_pages,
+                      void* ctx_v_pages, void* stream) {
+  int rc = check_dims(dims, sys_len);
+  if (rc != RELAY_OK) return rc;
+  if ((rc = check_q_layout(dims, cu_q_lens)) != RELAY_OK) return rc;
+  if (!q_new || !k_new || !v_new || !cos_sin || !block_tables || !ctx_lens || !q_out || !ctx_k_pages || !ctx_v_pages)
+    return fail(RELAY_ERR_INVALID, "NULL array argument");
+  if (max_pos < 1) return fail(RELAY_ERR_INVALID, "max_pos must be >= 1");
+  if (dims->max_q_len > 65535 || dims->num_q_heads + dims->num_kv_heads > 65535)
+    return fail(RELAY_ERR_INVALID, "too many tokens per request or heads for one launch");
+  relay::RopeArgs a{};
+  a.q_new = q_new;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.cos_sin = cos_sin;
+  a.block_tables = block_tables;
+  a.ctx_lens = ctx_lens;
+  a.cu_q_lens = cu_q_lens;
+  a.q_out = q_out;
+  a.ctx_k = ctx_k_pages;
+  a.ctx_v = ctx_v_pages;
+  a.batch = dims->batch;
+  a.num_q_heads = dims->num_q_heads;
+  a.num_kv_heads = dims->num_kv_heads;
+  a.head_dim = dims->head_dim;
+  a.total_q = dims->total_q;
+  a.max_blocks_per_seq = dims->max_blocks_per_seq;
+  a.num_blocks = dims->num_blocks;
+  a.sys_len = sys_len;
+  a.max_pos = max_pos;
+  a.bf16 = dims->in_dtype == RELAY_BF16;
+  hipError_t e = relay::launch_rope_append(a, dims->max_q_len, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RELAY_OK : hip_fail(e, "rope append launch");
+}
+
+int relay_rope_system(int32_t num_kv_heads, int32_t head_dim, int32_t sys_len, int32_t in_dtype, void* sys_k,
+                      const float* cos_sin, int32_t max_pos, void* stream) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(RELAY_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", head_dim);
+  if (in_dtype != RELAY_F32 && in_dtype != RELAY_BF16) return fail(RELAY_ERR_UNSUPPORTED, "dtype %d unsupported", in_dtype);
+  if (num_kv_heads < 1 || num_kv_heads > 65535 || sys_len < 0 || sys_len > max_pos)
+    return fail(RELAY_ERR_INVALID, "need 1 <= num_kv_heads <= 65535 and 0 <= sys_len <= max_pos");
+  if (sys_len == 0) return RELAY_OK;
+  if (!sys_k || !cos_sin) return fail(RELAY_ERR_INVALID, "NULL array argument");
+  hipError_t e = relay::launch_rope_system(sys_k, cos_sin, sys_len, num_kv_heads, head_dim, in_dtype == RELAY_BF16,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RELAY_OK : hip_fail(e, "rope system launch");
+}
+
 }  // extern "C"

@@ -111,6 +111,26 @@ struct FuseArgs {
   int out_bf16;
 };
 
+// relay_rope.hip: position embedding and KV append.
+struct RopeArgs {
+  const void* q_new;
+  const void* k_new;
+  const void* v_new;
+  const float* cos_sin;  // [max_pos, head_dim]
+  const int32_t* block_tables;
+  const int32_t* ctx_lens;
+  const int32_t* cu_q_lens;  // NULL: one token per request
+  void* q_out;
+  void* ctx_k;
+  void* ctx_v;
+  int batch, num_q_heads, num_kv_heads, head_dim, total_q;
+  int max_blocks_per_seq, num_blocks, sys_len, max_pos, bf16;
+};
+hipError_t launch_rope_table(float* cos_sin, int max_pos, int d, double base, hipStream_t s);
+hipError_t launch_rope_append(const RopeArgs& a, int max_q_len, hipStream_t s);
+hipError_t launch_rope_system(void* sys_k, const float* cos_sin, int sys_len, int num_kv_heads, int d, int bf16,
+                              hipStream_t s);
+
 hipError_t launch_sys_attn_tiled(const SysArgs& a, const SysConfig& c, int in_dtype, int head_dim,
                                  int nwg, hipStream_t stream);
 

@@ -1,0 +1,112 @@
+// The step before the relay path on gfx950: rotary position embedding with context
+// positions offset by the system length, and the append of a decode step's new
+// tokens to the paged context cache.
+//
+// The system K/V are prefilled offline at positions 0 .. L_s - 1, so a request's own
+// tokens are placed after them: context token j is at absolute position L_s + j
+// (atyun.com article, section "RelayAttention"; linnk.ai summary, section "Deeper
+// Inquiries").  The embedding is RoPE in rotate-half form (the Llama family's): for
+// i < d/2 the pair (x[i], x[i + d/2]) is rotated by the angle p * base^(-2i/d).  The
+// cos/sin of every (position, i) come from a table [max_pos, d] fp32 (cos in the
+// first d/2 columns, sin in the last), built once by relay_rope_table with the angle
+// reduced in fp64.
+//
+// Elementwise and HBM-bound (a few KB per token): one workgroup of d/2 lanes per
+// (token, head) row, lane i rotating the pair (i, i + d/2).
+#include "relay_device.hpp"
+#include "relay_internal.hpp"
+
+namespace relay {
+
+__device__ __forceinline__ float rope_load(const void* p, size_t i, int bf16) {
+  if (bf16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+  return static_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ void rope_store(void* p, size_t i, float v, int bf16) {
+  if (bf16) static_cast<__bf16*>(p)[i] = static_cast<__bf16>(v);  // round to nearest even
+  else static_cast<float*>(p)[i] = v;
+}
+
+__global__ void rope_table_kernel(float* cos_sin, int max_pos, int d, double base) {
+  const int pos = blockIdx.x;
+  const int half = d / 2;
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const double a = (double)pos * pow(base, -2.0 * i / d);
+    cos_sin[(size_t)pos * d + i] = (float)cos(a);
+    cos_sin[(size_t)pos * d + half + i] = (float)sin(a);
+  }
+}
+
+// New token t (row t of q_new) of request b sits at context position
+// p = c_b - n_b + t_local, absolute position L_s + p.  Rows: blockIdx.z < H_q are query
+// heads (rotated into q_out), the rest KV heads (K rotated and V copied into page
+// block_tables[b][p / 16], slot p % 16).  Rows whose position or page is out of range
+// are skipped (nothing written).
+__global__ void rope_append_kernel(RopeArgs a) {
+  const int b = blockIdx.x, tl = blockIdx.y, row = blockIdx.z;
+  const int i = threadIdx.x;
+  const int half = a.head_dim / 2, d = a.head_dim;
+  int qs = b, nq = 1;
+  if (a.cu_q_lens) {
+    qs = a.cu_q_lens[b];
+    nq = a.cu_q_lens[b + 1] - qs;
+  }
+  if (tl >= nq || qs < 0 || qs + tl >= a.total_q) return;
+  const int t = qs + tl;
+  const int p = a.ctx_lens[b] - nq + tl;  // context position
+  const long long pos = (long long)a.sys_len + p;
+  if (p < 0 || pos >= a.max_pos) return;
+  const float c = a.cos_sin[pos * d + i], s = a.cos_sin[pos * d + half + i];
+  if (row < a.num_q_heads) {
+    const size_t base = ((size_t)t * a.num_q_heads + row) * d;
+    const float x1 = rope_load(a.q_new, base + i, a.bf16), x2 = rope_load(a.q_new, base + half + i, a.bf16);
+    rope_store(a.q_out, base + i, x1 * c - x2 * s, a.bf16);
+    rope_store(a.q_out, base + half + i, x2 * c + x1 * s, a.bf16);
+    return;
+  }
+  const int hk = row - a.num_q_heads;
+  if (p / kTile >= a.max_blocks_per_seq) return;
+  const int page = a.block_tables[(size_t)b * a.max_blocks_per_seq + p / kTile];
+  if (page < 0 || page >= a.num_blocks) return;
+  const int slot = p % kTile;
+  const size_t src = ((size_t)t * a.num_kv_heads + hk) * d;
+  const float k1 = rope_load(a.k_new, src + i, a.bf16), k2 = rope_load(a.k_new, src + half + i, a.bf16);
+  const size_t kdst = (((size_t)page * a.num_kv_heads + hk) * kTile + slot) * d;
+  rope_store(a.ctx_k, kdst + i, k1 * c - k2 * s, a.bf16);
+  rope_store(a.ctx_k, kdst + half + i, k2 * c + k1 * s, a.bf16);
+  const size_t vdst = ((size_t)page * a.num_kv_heads + hk) * (size_t)d * kTile + slot;
+  rope_store(a.ctx_v, vdst + (size_t)i * kTile, rope_load(a.v_new, src + i, a.bf16), a.bf16);
+  rope_store(a.ctx_v, vdst + (size_t)(half + i) * kTile, rope_load(a.v_new, src + half + i, a.bf16), a.bf16);
+}
+
+// System keys [H_kv, L_s, d] rotated in place at positions 0 .. L_s - 1 (the offline
+// prefill's position embedding).
+__global__ void rope_system_kernel(void* sys_k, const float* cos_sin, int sys_len, int d, int bf16) {
+  const int j = blockIdx.x, hk = blockIdx.y, i = threadIdx.x, half = d / 2;
+  const float c = cos_sin[(size_t)j * d + i], s = cos_sin[(size_t)j * d + half + i];
+  const size_t base = ((size_t)hk * sys_len + j) * d;
+  const float x1 = rope_load(sys_k, base + i, bf16), x2 = rope_load(sys_k, base + half + i, bf16);
+  rope_store(sys_k, base + i, x1 * c - x2 * s, bf16);
+  rope_store(sys_k, base + half + i, x2 * c + x1 * s, bf16);
+}
+
+hipError_t launch_rope_table(float* cos_sin, int max_pos, int d, double base, hipStream_t s) {
+  hipLaunchKernelGGL(rope_table_kernel, dim3(max_pos), dim3(64), 0, s, cos_sin, max_pos, d, base);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_append(const RopeArgs& a, int max_q_len, hipStream_t s) {
+  hipLaunchKernelGGL(rope_append_kernel, dim3(a.batch, max_q_len, a.num_q_heads + a.num_kv_heads),
+                     dim3(a.head_dim / 2), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_system(void* sys_k, const float* cos_sin, int sys_len, int num_kv_heads, int d, int bf16,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(rope_system_kernel, dim3(sys_len, num_kv_heads), dim3(d / 2), 0, s, sys_k, cos_sin, sys_len,
+                     d, bf16);
+  return hipGetLastError();
+}
+
+}  // namespace relay

@@ -56,7 +56,8 @@ class RelayError(RuntimeError):
 
 EXPORTS = ("relay_abi_version", "relay_strerror", "relay_last_error", "relay_workspace_size",
            "relay_get_plan", "relay_attn_decode", "relay_attn_decode_timed", "relay_sys_attn",
-           "relay_ctx_attn", "relay_fuse", "relay_validate")
+           "relay_ctx_attn", "relay_fuse", "relay_validate", "relay_rope_table", "relay_rope_append",
+           "relay_rope_system")
 
 _lib = None
 
@@ -90,6 +91,12 @@ def load_library(path: str = LIB_PATH):
     lib.relay_fuse.restype = ctypes.c_int
     lib.relay_validate.argtypes = [D, vp, vp, vp, i32]
     lib.relay_validate.restype = ctypes.c_int
+    lib.relay_rope_table.argtypes = [vp, i32, i32, ctypes.c_float, vp]
+    lib.relay_rope_table.restype = ctypes.c_int
+    lib.relay_rope_append.argtypes = [D, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.relay_rope_append.restype = ctypes.c_int
+    lib.relay_rope_system.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp]
+    lib.relay_rope_system.restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -254,6 +261,43 @@ def relay_validate(dims: relay_dims, block_tables, ctx_lens, cu_q_lens, sys_len:
     _check(load_library().relay_validate(
         ctypes.byref(dims), bt.ctypes.data_as(ctypes.c_void_p), cl.ctypes.data_as(ctypes.c_void_p),
         None if cu is None else cu.ctypes.data_as(ctypes.c_void_p), int(sys_len)))
+
+
+def relay_rope_table(max_pos: int, head_dim: int, base: float = 10000.0, device="cuda", stream=None):
+    """The cos/sin table [max_pos, head_dim] float32 the position-embedding entries read."""
+    t = torch.empty((max_pos, head_dim), dtype=torch.float32, device=device)
+    _require_device(t)
+    _check(load_library().relay_rope_table(_ptr(t), int(max_pos), int(head_dim), float(base), _stream(stream)))
+    return t
+
+
+def relay_rope_append(dims: relay_dims, sys_len: int, q_new, k_new, v_new, cos_sin, block_tables, ctx_lens,
+                      cu_q_lens, ctx_k_pages, ctx_v_pages, *, q_out=None, stream=None):
+    """Position embedding of a decode step's new tokens at sys_len + context position,
+    and their K/V appended to the pages (in place).  Returns q_out."""
+    if q_out is None:
+        q_out = torch.empty_like(q_new)
+    _require_device(q_new, k_new, v_new, cos_sin, block_tables, ctx_lens, cu_q_lens, ctx_k_pages, ctx_v_pages, q_out)
+    for x in (q_new, k_new, v_new, ctx_k_pages, ctx_v_pages, q_out):
+        if x.dtype != q_new.dtype or not x.is_contiguous():
+            raise ValueError("q/k/v/pages must be contiguous and of one dtype")
+    if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or cos_sin.shape[1] != q_new.shape[-1]:
+        raise ValueError("cos_sin must be float32 [max_pos, head_dim]")
+    _check(load_library().relay_rope_append(
+        ctypes.byref(dims), int(sys_len), _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(cos_sin), cos_sin.shape[0],
+        _ptr(block_tables), _ptr(ctx_lens), _ptr(cu_q_lens), _ptr(q_out), _ptr(ctx_k_pages), _ptr(ctx_v_pages),
+        _stream(stream)))
+    return q_out
+
+
+def relay_rope_system(sys_k, sys_len: int, cos_sin, *, stream=None):
+    """The system keys [H_kv, L_s, d] rotated in place at positions 0 .. sys_len - 1."""
+    _require_device(sys_k, cos_sin)
+    if not sys_k.is_contiguous() or sys_k.dim() != 3:
+        raise ValueError("sys_k must be a contiguous [H_kv, L_s, d] tensor")
+    _check(load_library().relay_rope_system(sys_k.shape[0], sys_k.shape[2], int(sys_len), _dtype_code(sys_k.dtype),
+                                            _ptr(sys_k), _ptr(cos_sin), cos_sin.shape[0], _stream(stream)))
+    return sys_k
 
 
 # ---- marshalling of generator workloads -------------------------------------------------
