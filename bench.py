@@ -375,6 +375,43 @@ def no_relay_baseline(torch, relay, w, args, relay_ms):
     return {"no_relay_us_per_step": round(1000 * bm, 2), "relay_speedup": round(bm / relay_ms, 3)}
 
 
+def rope_append_time(torch, relay, w, args):
+    """The step before the path on the same workload: position embedding of the new
+    tokens' q and k at sys_len + context position and their K/V appended to the pages
+    (relay_rope_append), timed alone with HIP events over back-to-back calls."""
+    t = relay.to_device(w, "cuda")
+    s = w.spec
+    dt = t["q"].dtype
+    tab = relay.relay_rope_table(s.sys_len + int(w.ctx_lens.max()), s.head_dim)
+    g = torch.Generator(device="cuda").manual_seed(1)
+    q_new = torch.randn(t["q"].shape, generator=g, device="cuda").to(dt)
+    k_new = torch.randn((w.total_q, s.num_kv_heads, s.head_dim), generator=g, device="cuda").to(dt)
+    v_new = torch.randn((w.total_q, s.num_kv_heads, s.head_dim), generator=g, device="cuda").to(dt)
+    q_out = torch.empty_like(q_new)
+    dims = relay.dims_of(t)
+    call = lambda: relay.relay_rope_append(dims, s.sys_len, q_new, k_new, v_new, tab, t["block_tables"],
+                                           t["ctx_lens"], t["cu_q_lens"], t["ctx_k_pages"], t["ctx_v_pages"],
+                                           q_out=q_out)
+    for _ in range(10):
+        call()
+    torch.cuda.synchronize()
+    n = min(args.steps, 200)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1000 * e0.elapsed_time(e1) / n
+    E = 2 if s.dtype == "bf16" else 4
+    nbytes = (2 * w.total_q * s.num_q_heads * s.head_dim * E      # q in and out
+              + 4 * w.total_q * s.num_kv_heads * s.head_dim * E   # k, v in; k, v pages out
+              + w.total_q * s.head_dim * 4)                       # one table row per token
+    return {"us_per_call": round(us, 2), "bytes_alg": nbytes,
+            "hbm_frac": round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+            "note": "back-to-back eager launches; a few MB per call, launch-latency bound"}
+
+
 def workloads_generate(spec):
     from shared_prompt_kv_amd import workloads
     return workloads.generate(spec)
@@ -460,6 +497,7 @@ def main():
                                  for c in (1, 4, 5)]
     if not args.no_sweep:
         line["no_relay_baseline"] = no_relay_baseline(torch, relay, w, args, ms)
+        line["rope_append"] = rope_append_time(torch, relay, w, args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
