@@ -322,12 +322,8 @@ __device__ inline void store_row_tile(const RowState<D>& st, float* o_row, float
 
 // ---- one 16-key step of the streaming units ------------------------------------------
 //
-// A step is one 16-key block (a context page, or a 16-key system tile) with a
-// wave-uniform base address.  The score tile S^T = K Q^T gives lane group q the
-// scores of keys 4q..4q+3, which are its reduction slice in O^T = V^T P^T
-// (v_mfma_f32_16x16x16_bf16: 4 keys per lane group); V^T for them is 4 contiguous
-// keys of the block's dimension-major tile.
-
+// Value fragments of one 16-key page for the two-page steps below: V^T for the 4 keys
+// 4q..4q+3 of lane group q, contiguous in the page's dimension-major tile.
 // V^T[dim][4q..4q+3] of one block.
 template <typename T> struct VFrag4;
 template <> struct VFrag4<bf16_t> {
@@ -335,13 +331,6 @@ template <> struct VFrag4<bf16_t> {
 };
 template <> struct VFrag4<float> {
   u32x4 c;  // 4 fp32
-};
-
-template <typename T, int D>
-struct PageFrag {
-  static constexpr int NCH = D * Elem<T>::kBytes / 64;
-  u32x4 k[NCH];          // this lane's K row, 16 bytes at 64*kk + 16*(l/16)
-  VFrag4<T> v[D / 16];   // V^T fragments, one per 16-dimension output tile
 };
 
 __device__ inline void load_v4(VFrag4<bf16_t>& f, const char* p) { f.c = *reinterpret_cast<const u32x2*>(p); }
@@ -357,91 +346,6 @@ __device__ inline void mask_v4(VFrag4<float>& f, int n) {
   f.c.y = 1 < n ? f.c.y : 0u;
   f.c.z = 2 < n ? f.c.z : 0u;
   f.c.w = 3 < n ? f.c.w : 0u;
-}
-
-// P for this lane's row and the lane group's 4 keys, as the output product's B operand.
-template <typename T> struct PFrag4;
-template <> struct PFrag4<bf16_t> {
-  u32x2 c, lo;  // bf16 P and its rounding residual
-};
-template <> struct PFrag4<float> {
-  float p[4];
-};
-
-template <bool SPLIT>
-__device__ inline void make_p4(PFrag4<bf16_t>& f, const float (&p)[4]) {
-  f.c.x = pack_bf16x2(p[0], p[1]);
-  f.c.y = pack_bf16x2(p[2], p[3]);
-  if constexpr (SPLIT) {
-    f.lo.x = pack_bf16x2(p[0] - bf16_lo_as_float(f.c.x), p[1] - bf16_hi_as_float(f.c.x));
-    f.lo.y = pack_bf16x2(p[2] - bf16_lo_as_float(f.c.y), p[3] - bf16_hi_as_float(f.c.y));
-  }
-}
-template <bool SPLIT>
-__device__ inline void make_p4(PFrag4<float>& f, const float (&p)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.p[i] = p[i];
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-template <bool SPLIT>
-__device__ inline void mfma_pv4(f32x4& acc, const VFrag4<bf16_t>& v, const PFrag4<bf16_t>& p) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v.c), __builtin_bit_cast(s16x4, p.c),
-                                                  acc, 0, 0, 0);
-  if constexpr (SPLIT)
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v.c),
-                                                    __builtin_bit_cast(s16x4, p.lo), acc, 0, 0, 0);
-}
-template <bool SPLIT>
-__device__ inline void mfma_pv4(f32x4& acc, const VFrag4<float>& v, const PFrag4<float>& p) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c.x), p.p[0], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c.y), p.p[1], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c.z), p.p[2], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c.w), p.p[3], acc, 0, 0, 0);
-}
-
-// Issues the loads of one block.  kp: base of its 16 K rows; vp: base of its
-// dimension-major V^T tile; krow: the K row this lane reads (its A-operand row,
-// clamped where the block is short).
-template <typename T, int D>
-__device__ inline void load_page(PageFrag<T, D>& f, const char* kp, const char* vp, int krow) {
-  constexpr int E = Elem<T>::kBytes;
-  const int q4 = lane_id() >> 4, r16 = lane_id() & 15;
-  const char* kr = kp + krow * D * E + 16 * q4;
-#pragma unroll
-  for (int kk = 0; kk < PageFrag<T, D>::NCH; ++kk) f.k[kk] = ld16(kr + 64 * kk);
-  const char* vr = vp + r16 * kTile * E + 4 * q4 * E;
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) load_v4(f.v[t], vr + 16 * t * kTile * E);
-}
-
-// Folds one loaded block into the row states.  keyq: index of this lane group's
-// first key (keys keyq..keyq+3); kv_len: keys that exist (values of the others are
-// zeroed); last[rt]: last key index the rows of tile rt may see (causal bound; -1
-// sees nothing).  PSPLIT: bf16 P as hi + lo.
-template <typename T, int D, int RT, bool PSPLIT>
-__device__ inline void compute_page(PageFrag<T, D>& f, const u32x4 (&qf)[RT][PageFrag<T, D>::NCH],
-                                    RowState<D> (&st)[RT], int keyq, int kv_len, const int (&last)[RT],
-                                    float scale_log2) {
-  if (keyq + 4 > kv_len) {
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) mask_v4(f.v[t], kv_len - keyq);
-  }
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    f32x4 sa = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < PageFrag<T, D>::NCH; ++kk) mfma_chunk(sa, f.k[kk], qf[rt][kk], T{});
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = (keyq + i <= last[rt]) ? sa[i] * scale_log2 : neg_inf();
-    softmax_step(st[rt], sc);
-    PFrag4<T> pf;
-    make_p4<PSPLIT>(pf, sc);
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) mfma_pv4<PSPLIT>(st[rt].o[t], f.v[t], pf);
-  }
 }
 
 // ---- two-page steps (32 keys) ----------------------------------------------------------
