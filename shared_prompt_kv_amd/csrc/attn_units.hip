@@ -30,10 +30,10 @@
 
 namespace relay {
 
-// Units shorter than this many keys compute P.V with P split into bf16 hi + lo (two
-// products): there single probabilities can be large and bf16 rounding of P alone
-// would cost up to 2^-9 of the output.  Longer units spread their weight over many
-// keys and round P once.
+// Units in which some row sees fewer than this many keys compute P.V with P split
+// into bf16 hi + lo (two products): there single probabilities can be large and bf16
+// rounding of P alone would cost up to 2^-9 of the output.  Where every row sees many
+// keys the weight is spread over them and P is rounded once.
 constexpr int kPSplitBelow = 256;
 
 template <typename T, int D>
@@ -224,7 +224,10 @@ __device__ __forceinline__ void ctx_unit(const UnitArgs& a, int v, CtxMeta m, fl
     r.ra = r.rb = r16;
     return r;
   };
-  if (key_end - key_begin < kPSplitBelow)
+  // the unit's first row sees the fewest of its keys (causal bound c - n_b + t): P is
+  // split when that row sees few, whatever the unit's length
+  const int first_seen = min(key_end, c - nq + row0 / a.group + 1) - key_begin;
+  if (first_seen < kPSplitBelow)
     stream_pipelined<T, D, RT, WK, true>(kl, nsteps, qf, st, key_begin, key_end, last, a.scale_log2, addr);
   else
     stream_pipelined<T, D, RT, WK, false>(kl, nsteps, qf, st, key_begin, key_end, last, a.scale_log2, addr);
