@@ -270,6 +270,18 @@ int relay_rope_append(const relay_dims* dims, int32_t sys_len, const void* q_new
 int relay_rope_system(int32_t num_kv_heads, int32_t head_dim, int32_t sys_len, int32_t in_dtype,
                       void* sys_k, const float* cos_sin, int32_t max_pos, void* stream);
 
+/*
+ * The offline prefill's cache fill (the system K/V are filled before serving:
+ * atyun.com article, section "RelayAttention"): the system prompt's keys and values
+ * as a projection produces them, token-major k_raw / v_raw [L_s, H_kv, d] (in_dtype),
+ * written into the system cache: sys_k [H_kv, L_s, d] with RoPE at positions
+ * 0 .. L_s - 1 and sys_v [H_kv, ceil(L_s/16), d, 16] (the tail tile's padding set to
+ * 0).  cos_sin: relay_rope_table's table, sys_len <= max_pos.
+ */
+int relay_system_fill(int32_t num_kv_heads, int32_t head_dim, int32_t sys_len, int32_t in_dtype,
+                      const void* k_raw, const void* v_raw, const float* cos_sin, int32_t max_pos,
+                      void* sys_k, void* sys_v, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

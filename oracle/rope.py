@@ -104,3 +104,40 @@ def append_expect(w, q_new, k_new, v_new, base: float = ROPE_BASE):
     L_s + that; its K/V land at page block_tables[b][p / 16], slot p % 16."""
     pos = token_positions(w)
     return rotate(q_new, pos[:, None], base), rotate(k_new, pos[:, None], base), np.asarray(v_new, np.float64)
+
+
+def prefill_expect(q_raw, k_raw, v_raw, dtype: str, base: float = ROPE_BASE):
+    """The offline prefill of a system prompt, as values: queries q_raw [L, H_q, d] and
+    keys / values k_raw, v_raw [L, H_kv, d] in storage form (bf16 bit patterns or
+    float32), before position embedding.  Returns (sys_k [H_kv, L, d] and sys_v
+    [H_kv, ceil(L/16), d, 16] in storage form, out [L, H_q, d] fp64): the system cache
+    (keys embedded at positions 0..L-1, values in 16-key dimension-major tiles, tail
+    padding 0) and every prompt token's causal attention over keys 0..its own position
+    (computed by the fp64 C oracle on a one-request workload whose L tokens are new)."""
+    from . import Problem
+    L, H_q, d = q_raw.shape
+    H_kv = k_raw.shape[1]
+    vals = (lambda a: W.bf16_bits_to_f32(a).astype(np.float64)) if dtype == "bf16" else \
+        (lambda a: np.asarray(a, np.float64))
+    store = (lambda x: W.f32_to_bf16_bits(np.asarray(x, np.float32))) if dtype == "bf16" else \
+        (lambda x: np.asarray(x, np.float32))
+    pos = np.arange(L)
+    k_rot = store(rotate(vals(k_raw), pos[:, None]))          # [L, H_kv, d]
+    q_rot = store(rotate(vals(q_raw), pos[:, None]))          # [L, H_q, d]
+    ntile = (L + 15) // 16
+    sys_k = np.ascontiguousarray(k_rot.transpose(1, 0, 2))
+    sys_v = np.zeros((H_kv, ntile * 16, d), dtype=np.asarray(v_raw).dtype)
+    sys_v[:, :L] = np.asarray(v_raw).transpose(1, 0, 2)
+    sys_v = np.ascontiguousarray(sys_v.reshape(H_kv, ntile, 16, d).transpose(0, 1, 3, 2))
+    # the prompt as one request: pages 0..ntile-1 in order, every token new
+    kp = np.zeros((ntile * 16, H_kv, d), dtype=k_rot.dtype)
+    kp[:L] = k_rot
+    kp = np.ascontiguousarray(kp.reshape(ntile, 16, H_kv, d).transpose(0, 2, 1, 3))
+    vp = np.ascontiguousarray(sys_v.transpose(1, 0, 2, 3))     # [ntile, H_kv, d, 16]
+    spec = W.WorkloadSpec("prefill", 0, 0, dtype, 1, H_q, H_kv, d, 0, "fixed", L, L, q_lo=L, q_hi=L)
+    empty = np.zeros((H_kv, 0, d), dtype=k_rot.dtype)
+    w = W.Workload(spec, q_rot, empty, np.zeros((H_kv, 0, d, 16), dtype=k_rot.dtype), kp, vp,
+                   np.arange(ntile, dtype=np.int32)[None, :], np.array([L], np.int32),
+                   np.array([L], np.int32), np.array([0, L], np.int32))
+    out, _ = Problem(w).attention()
+    return sys_k, sys_v, out

@@ -564,4 +564,19 @@ int relay_rope_system(int32_t num_kv_heads, int32_t head_dim, int32_t sys_len, i
   return e == hipSuccess ? RELAY_OK : hip_fail(e, "rope system launch");
 }
 
+int relay_system_fill(int32_t num_kv_heads, int32_t head_dim, int32_t sys_len, int32_t in_dtype, const void* k_raw,
+                      const void* v_raw, const float* cos_sin, int32_t max_pos, void* sys_k, void* sys_v,
+                      void* stream) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(RELAY_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", head_dim);
+  if (in_dtype != RELAY_F32 && in_dtype != RELAY_BF16) return fail(RELAY_ERR_UNSUPPORTED, "dtype %d unsupported", in_dtype);
+  if (num_kv_heads < 1 || num_kv_heads > 65535 || sys_len < 0 || sys_len > max_pos)
+    return fail(RELAY_ERR_INVALID, "need 1 <= num_kv_heads <= 65535 and 0 <= sys_len <= max_pos");
+  if (sys_len == 0) return RELAY_OK;
+  if (!k_raw || !v_raw || !cos_sin || !sys_k || !sys_v) return fail(RELAY_ERR_INVALID, "NULL array argument");
+  hipError_t e = relay::launch_system_fill(k_raw, v_raw, cos_sin, sys_k, sys_v, sys_len, num_kv_heads, head_dim,
+                                           in_dtype == RELAY_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RELAY_OK : hip_fail(e, "system fill launch");
+}
+
 }  // extern "C"

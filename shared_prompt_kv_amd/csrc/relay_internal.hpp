@@ -128,6 +128,8 @@ struct RopeArgs {
 };
 hipError_t launch_rope_table(float* cos_sin, int max_pos, int d, double base, hipStream_t s);
 hipError_t launch_rope_append(const RopeArgs& a, int max_q_len, hipStream_t s);
+hipError_t launch_system_fill(const void* k_raw, const void* v_raw, const float* cos_sin, void* sys_k, void* sys_v,
+                              int sys_len, int num_kv_heads, int d, int bf16, hipStream_t s);
 hipError_t launch_rope_system(void* sys_k, const float* cos_sin, int sys_len, int num_kv_heads, int d, int bf16,
                               hipStream_t s);
 

@@ -91,6 +91,38 @@ __global__ void rope_system_kernel(void* sys_k, const float* cos_sin, int sys_le
   rope_store(sys_k, base + half + i, x2 * c + x1 * s, bf16);
 }
 
+// The offline prefill's cache fill: the system prompt's keys and values, token-major
+// as a projection produces them (k_raw / v_raw [L_s, H_kv, d]), into the system cache
+// layouts: sys_k [H_kv, L_s, d] with RoPE at position j, sys_v [H_kv, ceil(L_s/16),
+// d, 16] (dimension-major 16-key tiles; the tail tile's padding is written as 0).
+__global__ void system_fill_kernel(const void* k_raw, const void* v_raw, const float* cos_sin, void* sys_k,
+                                   void* sys_v, int sys_len, int num_kv_heads, int d, int bf16) {
+  const int j = blockIdx.x, hk = blockIdx.y, i = threadIdx.x, half = d / 2;
+  const int ntile = (sys_len + kTile - 1) / kTile;
+  const size_t vt = ((size_t)hk * ntile + j / kTile) * (size_t)d * kTile + j % kTile;
+  if (j >= sys_len) {  // padding keys of the tail tile (grid covers whole tiles)
+    rope_store(sys_v, vt + (size_t)i * kTile, 0.f, bf16);
+    rope_store(sys_v, vt + (size_t)(half + i) * kTile, 0.f, bf16);
+    return;
+  }
+  const size_t src = ((size_t)j * num_kv_heads + hk) * d;
+  const float c = cos_sin[(size_t)j * d + i], s = cos_sin[(size_t)j * d + half + i];
+  const float k1 = rope_load(k_raw, src + i, bf16), k2 = rope_load(k_raw, src + half + i, bf16);
+  const size_t kd = ((size_t)hk * sys_len + j) * d;
+  rope_store(sys_k, kd + i, k1 * c - k2 * s, bf16);
+  rope_store(sys_k, kd + half + i, k2 * c + k1 * s, bf16);
+  rope_store(sys_v, vt + (size_t)i * kTile, rope_load(v_raw, src + i, bf16), bf16);
+  rope_store(sys_v, vt + (size_t)(half + i) * kTile, rope_load(v_raw, src + half + i, bf16), bf16);
+}
+
+hipError_t launch_system_fill(const void* k_raw, const void* v_raw, const float* cos_sin, void* sys_k, void* sys_v,
+                              int sys_len, int num_kv_heads, int d, int bf16, hipStream_t s) {
+  const int padded = (sys_len + kTile - 1) / kTile * kTile;
+  hipLaunchKernelGGL(system_fill_kernel, dim3(padded, num_kv_heads), dim3(d / 2), 0, s, k_raw, v_raw, cos_sin,
+                     sys_k, sys_v, sys_len, num_kv_heads, d, bf16);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_table(float* cos_sin, int max_pos, int d, double base, hipStream_t s) {
   hipLaunchKernelGGL(rope_table_kernel, dim3(max_pos), dim3(64), 0, s, cos_sin, max_pos, d, base);
   return hipGetLastError();

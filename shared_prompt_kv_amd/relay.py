@@ -57,7 +57,7 @@ class RelayError(RuntimeError):
 EXPORTS = ("relay_abi_version", "relay_strerror", "relay_last_error", "relay_workspace_size",
            "relay_get_plan", "relay_attn_decode", "relay_attn_decode_timed", "relay_sys_attn",
            "relay_ctx_attn", "relay_fuse", "relay_validate", "relay_rope_table", "relay_rope_append",
-           "relay_rope_system")
+           "relay_rope_system", "relay_system_fill")
 
 _lib = None
 
@@ -97,6 +97,8 @@ def load_library(path: str = LIB_PATH):
     lib.relay_rope_append.restype = ctypes.c_int
     lib.relay_rope_system.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp]
     lib.relay_rope_system.restype = ctypes.c_int
+    lib.relay_system_fill.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, vp, vp, vp]
+    lib.relay_system_fill.restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -298,6 +300,23 @@ def relay_rope_system(sys_k, sys_len: int, cos_sin, *, stream=None):
     _check(load_library().relay_rope_system(sys_k.shape[0], sys_k.shape[2], int(sys_len), _dtype_code(sys_k.dtype),
                                             _ptr(sys_k), _ptr(cos_sin), cos_sin.shape[0], _stream(stream)))
     return sys_k
+
+
+def relay_system_fill(k_raw, v_raw, cos_sin, *, sys_k=None, sys_v=None, stream=None):
+    """The system cache from token-major k_raw / v_raw [L_s, H_kv, d]: returns
+    (sys_k [H_kv, L_s, d] with RoPE at 0 .. L_s - 1, sys_v [H_kv, ceil(L_s/16), d, 16])."""
+    L, H_kv, d = k_raw.shape
+    if sys_k is None:
+        sys_k = torch.empty((H_kv, L, d), dtype=k_raw.dtype, device=k_raw.device)
+    if sys_v is None:
+        sys_v = torch.empty((H_kv, (L + 15) // 16, d, 16), dtype=k_raw.dtype, device=k_raw.device)
+    _require_device(k_raw, v_raw, cos_sin, sys_k, sys_v)
+    if v_raw.shape != k_raw.shape or v_raw.dtype != k_raw.dtype:
+        raise ValueError("k_raw and v_raw must have one shape and dtype")
+    _check(load_library().relay_system_fill(H_kv, d, L, _dtype_code(k_raw.dtype), _ptr(k_raw), _ptr(v_raw),
+                                            _ptr(cos_sin), cos_sin.shape[0], _ptr(sys_k), _ptr(sys_v),
+                                            _stream(stream)))
+    return sys_k, sys_v
 
 
 # ---- marshalling of generator workloads -------------------------------------------------

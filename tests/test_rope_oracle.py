@@ -85,3 +85,24 @@ def test_relay_with_offset_positions_equals_unsplit_rotated_attention():
     # a planted mistake: context positions restarting at 0 instead of after the system prompt
     wrong, _ = Problem(rope.rotated_workload(w, ctx_offset=0)).relay()
     assert max(float(np.abs(wrong[t, h] - e).max()) for (t, h), e in expect.items()) > 1e-3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_oracle_against_brute_force(dtype):
+    r = rng(5)
+    L, Hq, Hkv, d = 37, 4, 2, 64
+    conv = (lambda x: W.f32_to_bf16_bits(x.astype(np.float32))) if dtype == "bf16" else (lambda x: x.astype(np.float32))
+    back = (lambda a: W.bf16_bits_to_f32(a).astype(np.float64)) if dtype == "bf16" else (lambda a: a.astype(np.float64))
+    q, k, v = (conv(r.standard_normal(s)) for s in ((L, Hq, d), (L, Hkv, d), (L, Hkv, d)))
+    sk, sv, out = rope.prefill_expect(q, k, v, dtype)
+    # cache layouts: keys embedded at their positions, values tiled, padding zero
+    np.testing.assert_array_equal(back(sv).transpose(0, 1, 3, 2).reshape(Hkv, -1, d)[:, :L], back(v).transpose(1, 0, 2))
+    assert not back(sv).transpose(0, 1, 3, 2).reshape(Hkv, -1, d)[:, L:].any()
+    qv = back(conv(rope.rotate(back(q), np.arange(L)[:, None])))
+    kv = back(conv(rope.rotate(back(k), np.arange(L)[:, None])))
+    np.testing.assert_array_equal(back(sk), kv.transpose(1, 0, 2))
+    for t in (0, 1, 15, 16, 36):
+        for h in range(Hq):
+            s = kv[: t + 1, h // 2] @ qv[t, h] / np.sqrt(d)
+            p = np.exp(s - s.max())
+            np.testing.assert_allclose(out[t, h], p @ back(v)[: t + 1, h // 2] / p.sum(), rtol=0, atol=1e-13)
