@@ -412,6 +412,36 @@ def rope_append_time(torch, relay, w, args):
             "note": "back-to-back eager launches; a few MB per call, launch-latency bound"}
 
 
+def prefill_time(torch, relay, w, args):
+    """The offline step before serving on the same shapes: the system prompt's cache fill
+    (position embedding, layouts) and its causal attention (shared_prompt_kv_amd.prefill),
+    timed over repeated calls on synthetic projections."""
+    from shared_prompt_kv_amd import prefill
+    s = w.spec
+    L = s.sys_len
+    dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(2)
+    q = torch.randn((L, s.num_q_heads, s.head_dim), generator=g, device="cuda").to(dt)
+    k = torch.randn((L, s.num_kv_heads, s.head_dim), generator=g, device="cuda").to(dt)
+    v = torch.randn((L, s.num_kv_heads, s.head_dim), generator=g, device="cuda").to(dt)
+    tab = relay.relay_rope_table(L, s.head_dim)
+    for _ in range(2):
+        prefill.prefill_system(q, k, v, tab, s.scale)
+    torch.cuda.synchronize()
+    n = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        prefill.prefill_system(q, k, v, tab, s.scale)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1000 * e0.elapsed_time(e1) / n
+    flops = 4 * s.num_q_heads * s.head_dim * (L * (L + 1) // 2)   # causal: token j sees j + 1 keys
+    return {"sys_len": L, "us_per_call": round(us, 1), "attn_tflops": round(flops / (us * 1e-6) / 1e12, 2),
+            "note": "cache fill + the prompt's causal attention through the decode path (one request, all "
+                    "tokens new); includes its allocations"}
+
+
 def workloads_generate(spec):
     from shared_prompt_kv_amd import workloads
     return workloads.generate(spec)
@@ -498,6 +528,7 @@ def main():
     if not args.no_sweep:
         line["no_relay_baseline"] = no_relay_baseline(torch, relay, w, args, ms)
         line["rope_append"] = rope_append_time(torch, relay, w, args)
+        line["system_prefill"] = prefill_time(torch, relay, w, args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

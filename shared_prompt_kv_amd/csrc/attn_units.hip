@@ -17,8 +17,8 @@
 // lies past the end of the context writes LSE = -inf for its rows, so relay_fuse
 // can read every split slot without knowing the context lengths.
 //
-// A unit is one workgroup of WK waves (key lanes).  Key lane kl streams the 16-key
-// steps (pages) kl, kl+WK, ... of the unit, so a unit's critical path is 1/WK of its steps;
+// A unit is one workgroup of WK waves (key lanes).  Key lane kl streams the 32-key
+// steps (two pages) kl, kl+WK, ... of the unit, so a unit's critical path is 1/WK of its steps;
 // the lanes' softmax states are merged through LDS (fixed order) and key lane 0
 // writes one partial (O, LSE) per row.  sys_ctx_attn_kernel carries both kinds of
 // unit in one launch (system units first: they are the longest), so the two steps
