@@ -51,7 +51,8 @@ def parse():
                          "Llama-3-8B shapes (for counters: system-KV bytes read vs batch size)")
     ap.add_argument("--batch-sweep", action="store_true",
                     help="only run relay vs the no-relay baseline (prefix-shared system pages) over "
-                         "batch sizes of the Llama2-7B shape (one JSON line per batch)")
+                         "batch sizes of the Llama2-7B shape, then over request context lengths at batch 32 "
+                         "(one JSON line per point)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run torch's device copy of COPY_BYTES, 10 times (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -71,6 +72,7 @@ def copy_calibration(torch):
 
 
 BATCH_SWEEP = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+CTX_SWEEP = (64, 256, 1024, 4096)  # every request's own context length, Llama2-7B shape, batch 32
 SYS_SCALING = (("llama2_7b_mha", 2, (1, 4, 8, 16, 32)), ("llama3_8b_gqa", 4, (1, 4, 16, 64, 256)))
 
 
@@ -474,6 +476,16 @@ def main():
                               "relay_us_per_step": r["us_per_step"], "qtok_s": r["qtok_s"],
                               "no_relay_us_per_step": r["no_relay_us_per_step"],
                               "relay_speedup": r["relay_speedup"]}), flush=True)
+        # long request contexts dilute the gain: the system share of the bytes shrinks
+        for C in CTX_SWEEP:
+            spec = workloads.config_spec(2, 0).replace(ctx_len_dist="fixed", ctx_lo=C, ctx_hi=C)
+            r = point(torch, relay, spec, args, with_baseline=True)
+            L, B = spec.sys_len, spec.batch
+            print(json.dumps({"shape": "llama2_7b_mha", "batch": B, "sys_len": L, "ctx_len": C,
+                              "relay_us_per_step": r["us_per_step"], "qtok_s": r["qtok_s"],
+                              "no_relay_us_per_step": r["no_relay_us_per_step"],
+                              "relay_speedup": r["relay_speedup"],
+                              "kv_bytes_ratio": round(B * (L + C) / (L + B * C), 3)}), flush=True)
         return
     relay.load_library()
     spec = workloads.config_spec(args.config, args.sweep_index)

@@ -89,6 +89,44 @@ __device__ __forceinline__ void mf_issue(char* buf, const char* kbase, const cha
   }
 }
 
+// Per-lane byte offsets of one step's loads relative to its first key key0: both
+// layouts hold 256 bytes per key (a 128-dim bf16 key row; a 16-key value tile is 4096
+// bytes), and steps start at multiples of 64 keys, so every load of a step is
+// base + 256 key0 + a constant of the lane.  Steps that end inside the prompt use
+// these; the step holding the prompt's end goes through mf_issue (clamped rows).
+struct MfLaneOffsets {
+  uint32_t k[mf::kChunks];
+  uint32_t v[mf::kChunks];
+};
+
+__device__ __forceinline__ MfLaneOffsets mf_lane_offsets(int wave) {
+  const int lane = lane_id();
+  MfLaneOffsets o;
+#pragma unroll
+  for (int j = 0; j < mf::kChunks; ++j) {
+    const int p = mf::kThreads * j + kWave * wave + lane;
+    const int row = p >> 4, c = (p & 15) ^ (row & 15);
+    o.k[j] = (uint32_t)(mf_key_of_row(row) * mf::D * 2 + c * 16);
+    const int d = p >> 3, cv = (p & 7) ^ (d & 7);
+    o.v[j] = (uint32_t)((cv >> 1) * (mf::D * kTile * 2) + d * (kTile * 2) + (cv & 1) * 16);
+  }
+  return o;
+}
+
+__device__ __forceinline__ void mf_issue_full(char* buf, const char* kstep, const char* vstep, int wave,
+                                              const MfLaneOffsets& o) {
+#pragma unroll
+  for (int j = 0; j < mf::kChunks; ++j) {
+    const int base = mf::kThreads * j + kWave * wave;
+    __builtin_amdgcn_global_load_lds(kstep + o.k[j], (lds_ptr_t)(buf + base * 16), 16, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < mf::kChunks; ++j) {
+    const int base = mf::kThreads * j + kWave * wave;
+    __builtin_amdgcn_global_load_lds(vstep + o.v[j], (lds_ptr_t)(buf + mf::kTileBytes + base * 16), 16, 0, 0);
+  }
+}
+
 // Zeroes the V values of keys [nvalid, 64) of a landed step (values of keys past the
 // system prompt must not reach an output through 0 * NaN).
 __device__ __forceinline__ void mf_zero_tail(char* buf, int nvalid) {
@@ -102,8 +140,9 @@ __device__ __forceinline__ void mf_zero_tail(char* buf, int nvalid) {
 __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r32 = lane & 31, hh = lane >> 5;
+  const MfLaneOffsets lo_ = mf_lane_offsets(wave);
 
   // workgroup -> (row block, part).  Part p streams the 64-key steps
   // [p S / P, (p + 1) S / P) of the S = H_kv * steps_per_head steps of all heads
@@ -159,19 +198,28 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
     for (int db = 0; db < mf::D / 32; ++db) o[db] = f32x16{};
     float mrow = neg_inf(), lsum = 0.f;
 
-    mf_issue(lds_raw, kbase, vbase, key_begin, Ls, ntile);
+    // loads of the step at key0 into buffer dst: plain offsets unless it holds the end
+    auto issue = [&](char* dst, int key0) {
+      if (key0 + mf::kKB <= Ls)
+        mf_issue_full(dst, kbase + (size_t)key0 * (mf::D * 2), vbase + (size_t)key0 * (mf::D * 2), wave, lo_);
+      else
+        mf_issue(dst, kbase, vbase, key0, Ls, ntile);
+    };
+
+    issue(lds_raw, key_begin);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int s = 0; s < nsteps; ++s) {
       const int key0 = key_begin + s * mf::kKB;
       char* buf = lds_raw + (s & 1) * mf::kBufBytes;
-      if (key0 + mf::kKB > Ls) {  // the last step of the prompt: clear V past its end
+      const bool partial = key0 + mf::kKB > Ls;  // the last step of the prompt
+      if (partial) {  // clear V past the prompt's end
         mf_zero_tail(buf, Ls - key0);
         __syncthreads();
       }
       const bool more = s + 1 < nsteps;
-      if (more) mf_issue(lds_raw + ((s + 1) & 1) * mf::kBufBytes, kbase, vbase, key0 + mf::kKB, Ls, ntile);
+      if (more) issue(lds_raw + ((s + 1) & 1) * mf::kBufBytes, key0 + mf::kKB);
 
       // ---- scores of the 64 keys: two 32-key blocks
       f32x16 sacc[2];
@@ -197,13 +245,10 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
 #pragma unroll
         for (int i = 0; i < 32; ++i) sc[i] = -sc[i];
       }
-      const int lim = key_end - key0;  // keys [0, lim) of the step exist
-      const bool partial = lim < mf::kKB;
-      if (partial) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-          if (16 * (i >> 3) + 8 * hh + (i & 7) >= lim) sc[i] = neg_inf();
-      }
+      // No masking before the exponentials: in the step holding the prompt's end, rows
+      // past it hold copies of the last key (mf_issue clamps them), whose scores leave
+      // the maximum unchanged, and their values are zero in LDS, so they add nothing to
+      // O; only the row sum below leaves them out.
       // ---- online softmax on scale-free scores (lanes l and l ^ 32 hold the same row):
       // the reference m is kept scaled, p = 2^(|scale| s - m) is one FMA and an exp
       float mx = sc[0];
@@ -226,13 +271,16 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
       const float m_use = (mrow == neg_inf()) ? 0.f : mrow;
 #pragma unroll
       for (int i = 0; i < 32; ++i) sc[i] = fast_exp2(__builtin_fmaf(sc[i], scale, -m_use));
-      if (partial) {  // exact zeros for keys that do not exist (also when scale is 0)
+      if (partial) {
+        // score i of the lane is key 16 (i / 8) + 8 hh + i % 8 of the step; keys
+        // [0, Ls - key0) exist
+        const int lim_h = Ls - key0 - 8 * hh;
 #pragma unroll
-        for (int i = 0; i < 32; ++i)
-          if (16 * (i >> 3) + 8 * hh + (i & 7) >= lim) sc[i] = 0.f;
+        for (int i = 0; i < 32; ++i) lsum += (16 * (i >> 3) + (i & 7) < lim_h) ? sc[i] : 0.f;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) lsum += sc[i];
       }
-#pragma unroll
-      for (int i = 0; i < 32; ++i) lsum += sc[i];
       // ---- P (bf16) per 16-key block kb: k slots 0..7 = keys 0..7 (lanes hh = 0),
       // 8..15 = keys 8..15 (hh = 1), i.e. sc[8 kb .. 8 kb + 7]; then O^T += V^T P^T
       u32x4 pb[4];
