@@ -414,12 +414,13 @@ def rope_append_time(torch, relay, w, args):
             "note": "back-to-back eager launches; a few MB per call, launch-latency bound"}
 
 
-def prefill_time(torch, relay, w, args):
-    """The offline step before serving on the same shapes: the system prompt's cache fill
-    (position embedding, layouts) and its causal attention (shared_prompt_kv_amd.prefill),
-    timed over repeated calls on synthetic projections."""
+def prefill_time(torch, relay, spec, args):
+    """The offline step before serving on a workload's shapes: the system prompt's cache
+    fill (position embedding, layouts) and its causal attention
+    (shared_prompt_kv_amd.prefill), timed over repeated calls on synthetic projections;
+    the causal attention call (relay_prefill_attn) also alone."""
     from shared_prompt_kv_amd import prefill
-    s = w.spec
+    s = spec
     L = s.sys_len
     dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
     g = torch.Generator(device="cuda").manual_seed(2)
@@ -427,21 +428,36 @@ def prefill_time(torch, relay, w, args):
     k = torch.randn((L, s.num_kv_heads, s.head_dim), generator=g, device="cuda").to(dt)
     v = torch.randn((L, s.num_kv_heads, s.head_dim), generator=g, device="cuda").to(dt)
     tab = relay.relay_rope_table(L, s.head_dim)
-    for _ in range(2):
-        prefill.prefill_system(q, k, v, tab, s.scale)
-    torch.cuda.synchronize()
-    n = 5
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(n):
-        prefill.prefill_system(q, k, v, tab, s.scale)
-    e1.record()
-    torch.cuda.synchronize()
-    us = 1000 * e0.elapsed_time(e1) / n
     flops = 4 * s.num_q_heads * s.head_dim * (L * (L + 1) // 2)   # causal: token j sees j + 1 keys
-    return {"sys_len": L, "us_per_call": round(us, 1), "attn_tflops": round(flops / (us * 1e-6) / 1e12, 2),
-            "note": "cache fill + the prompt's causal attention through the decode path (one request, all "
-                    "tokens new); includes its allocations"}
+    peak = (BF16_PEAK_TFLOPS if s.dtype == "bf16" else FP32_PEAK_TFLOPS) * 1e12
+
+    def timed(fn, n=5):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1000 * e0.elapsed_time(e1) / n
+
+    us = timed(lambda: prefill.prefill_system(q, k, v, tab, s.scale))
+    out = {"workload": s.name, "sys_len": L, "us_per_call": round(us, 1),
+           "attn_tflops": round(flops / (us * 1e-6) / 1e12, 2)}
+    if prefill.uses_matrix_cores(q, k, s.scale):
+        sk, sv, _ = prefill.prefill_system(q, k, v, tab, s.scale)
+        dims = relay.prefill_dims(q, sk, s.scale)
+        ws = relay.prefill_workspace(dims, L, "cuda")
+        ua = timed(lambda: relay.relay_prefill_attn(q, sk, sv, L, s.scale, workspace_buf=ws))
+        out.update(attn_us=round(ua, 1), attn_kernel_tflops=round(flops / (ua * 1e-6) / 1e12, 2),
+                   attn_mfma_frac=round(flops / (ua * 1e-6) / peak, 4))
+    out["note"] = ("cache fill + the prompt's causal attention (matrix-core system kernel with a causal mask "
+                   "when bf16 / head_dim 128, else the decode path), its allocations included; attn_*: "
+                   "relay_prefill_attn alone (causal system kernel + merge)")
+    print(f"[bench] {s.name} system prefill L={L}: {us:.1f} us", file=sys.stderr, flush=True)
+    return out
 
 
 def workloads_generate(spec):
@@ -540,7 +556,7 @@ def main():
     if not args.no_sweep:
         line["no_relay_baseline"] = no_relay_baseline(torch, relay, w, args, ms)
         line["rope_append"] = rope_append_time(torch, relay, w, args)
-        line["system_prefill"] = prefill_time(torch, relay, w, args)
+        line["system_prefill"] = [prefill_time(torch, relay, workloads.config_spec(c, 0), args) for c in (2, 4)]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

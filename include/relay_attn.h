@@ -192,6 +192,32 @@ int relay_sys_attn(const relay_dims* dims, const void* q, const void* sys_k, con
                    size_t workspace_bytes, void* stream);
 
 /*
+ * The attention half of the offline system prefill.  RelayAttention fills the
+ * system KV cache once, offline, before serving (atyun.com article, section
+ * "RelayAttention"; the cost analysis there); the system prompt's own tokens then
+ * need their causal attention over that cache, which is this call.  Query row
+ * (t, h) -- prompt token t, query head h -- attends to system keys 0..min(t,
+ * sys_len - 1) of KV head h / g, exactly.
+ *   q:      [total_q, H_q, d], token t at position t, already position-embedded
+ *           (relay_rope_append with sys_len = 0 does that);
+ *   sys_k, sys_v: the system cache as for relay_attn_decode (relay_system_fill);
+ *   out:    [total_q, H_q, d] of out_dtype (RELAY_F32 or RELAY_BF16);
+ *   lse_out: float32 [total_q, H_q] (natural log, scale included), or NULL.
+ * Only dims' total_q, num_q_heads, num_kv_heads, head_dim, in_dtype and scale
+ * matter; the rest must pass the usual checks (e.g. batch 1, max_q_len =
+ * max_ctx_len = total_q, ceil(total_q / 16) blocks).  Runs
+ * the matrix-core system kernel with a causal mask, then relay_fuse (2 launches):
+ * needs bf16 inputs, head_dim 128, more than 64 query rows per KV head (else
+ * RELAY_ERR_UNSUPPORTED), sys_len >= 1 and scale > 0 (else RELAY_ERR_INVALID).
+ * workspace: relay_prefill_workspace_size(dims, sys_len) bytes, 256-byte aligned,
+ * contents irrelevant on entry.
+ */
+size_t relay_prefill_workspace_size(const relay_dims* dims, int32_t sys_len);
+int relay_prefill_attn(const relay_dims* dims, const void* q, const void* sys_k, const void* sys_v,
+                       int32_t sys_len, void* out, int32_t out_dtype, float* lse_out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
  * Context-attention step alone (RelayAttention's second step): for every query
  * row, causal attention over its request's visible context keys only.
  * o_ctx / lse_ctx as for relay_sys_attn.  Enqueues ctx_attn and a relay_fuse

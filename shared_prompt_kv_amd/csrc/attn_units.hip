@@ -30,12 +30,6 @@
 
 namespace relay {
 
-// Units in which some row sees fewer than this many keys compute P.V with P split
-// into bf16 hi + lo (two products): there single probabilities can be large and bf16
-// rounding of P alone would cost up to 2^-9 of the output.  Where every row sees many
-// keys the weight is spread over them and P is rounded once.
-constexpr int kPSplitBelow = 256;
-
 template <typename T, int D>
 __device__ inline void load_q_tile(u32x4* qf, const void* q, size_t row_index, bool valid) {
   constexpr int E = Elem<T>::kBytes;

@@ -45,6 +45,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 struct Plan {
   int sys_mode = 0;  // 0: no system step, 1: streaming units, 2: matrix-core kernel
   int sys_mfma = 0;  // sys_mode 2: 1 = sys_attn_mfma (bf16, d = 128), 0 = sys_attn_tiled
+  int causal = 0;    // the offline prefill's causal system attention (sys_attn_mfma only)
   SysConfig sc{};
   int sys_chunks = 0, sys_chunk_len = 0, sys_row_blocks = 0, sys_wgs = 0, xcd_remap = 0;
   int sys_steps_per_head = 0, sys_total_steps = 0, sys_parts = 0;  // sys_attn_mfma
@@ -85,7 +86,8 @@ int check_dims(const relay_dims* d, int32_t sys_len) {
 
 int clamp_int(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-void make_plan(const relay_dims* d, int32_t sys_len, Plan* p) {
+void make_plan(const relay_dims* d, int32_t sys_len, Plan* p, bool causal = false) {
+  p->causal = causal ? 1 : 0;
   const int g = d->num_q_heads / d->num_kv_heads;
   const long long rows = (long long)d->total_q * d->num_q_heads;
   // ---- system step
@@ -109,6 +111,9 @@ void make_plan(const relay_dims* d, int32_t sys_len, Plan* p) {
       const long long S = (long long)p->sys_steps_per_head * d->num_kv_heads;
       p->sys_total_steps = (int)S;
       long long parts = relay::kSysMfmaSlots / p->sys_row_blocks;
+      // causal: a row block's work grows with its tokens, so the runs are cut finer
+      // and the workgroups of early row blocks, which finish first, free their slots
+      if (causal) parts *= relay::kSysCausalRunsPerSlot;
       const int forced = env_int("RELAY_SYS_PARTS", 0);
       if (forced > 0) parts = forced;
       if (parts < 1) parts = 1;
@@ -196,6 +201,7 @@ int launch_sys_tiled(const relay_dims* d, const Plan& p, const void* q, const vo
   a.steps_per_head = p.sys_steps_per_head;
   a.total_steps = p.sys_total_steps;
   a.parts = p.sys_parts;
+  a.causal = p.causal;
   hipError_t e = p.sys_mfma ? relay::launch_sys_attn_mfma(a, p.sys_wgs, s)
                             : relay::launch_sys_attn_tiled(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s);
   return e == hipSuccess ? RELAY_OK : hip_fail(e, "system attention launch");
@@ -417,6 +423,44 @@ int relay_sys_attn(const relay_dims* dims, const void* q, const void* sys_k, con
   f.a_count = p.sys_chunks;
   f.out = o_sys;
   f.lse_out = lse_sys;
+  f.n_rows = (long long)dims->total_q * dims->num_q_heads;
+  return launch_fuse(f, dims->head_dim, s);
+}
+
+size_t relay_prefill_workspace_size(const relay_dims* dims, int32_t sys_len) {
+  if (check_dims(dims, sys_len) != RELAY_OK) return 0;
+  Plan p;
+  make_plan(dims, sys_len, &p, true);
+  return p.ws_bytes;
+}
+
+int relay_prefill_attn(const relay_dims* dims, const void* q, const void* sys_k, const void* sys_v,
+                       int32_t sys_len, void* out, int32_t out_dtype, float* lse_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int rc = check_dims(dims, sys_len);
+  if (rc != RELAY_OK) return rc;
+  if (!q || !sys_k || !sys_v || !out) return fail(RELAY_ERR_INVALID, "NULL array argument");
+  if (sys_len < 1) return fail(RELAY_ERR_INVALID, "the prefill needs sys_len >= 1");
+  if (!(dims->scale > 0.f)) return fail(RELAY_ERR_INVALID, "the prefill needs scale > 0");
+  if (out_dtype != RELAY_F32 && out_dtype != RELAY_BF16) return fail(RELAY_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
+  if (!aligned16(q) || !aligned16(sys_k) || !aligned16(sys_v) || !aligned16(out))
+    return fail(RELAY_ERR_INVALID, "arrays must be 16-byte aligned");
+  Plan p;
+  make_plan(dims, sys_len, &p, true);
+  if (!p.sys_mfma)
+    return fail(RELAY_ERR_UNSUPPORTED, "the prefill runs on the matrix-core system kernel: bf16, head_dim 128 and "
+                                       "more than %d query rows per KV head", relay::kUnitMaxRows);
+  if ((rc = check_ws(p, workspace, workspace_bytes)) != RELAY_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if ((rc = launch_sys_tiled(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
+  FuseArgs f{};
+  f.a_o = reinterpret_cast<const float*>(ws + p.off_sys_o);
+  f.a_lse = reinterpret_cast<const float*>(ws + p.off_sys_lse);
+  f.a_count = p.sys_chunks;
+  f.out = out;
+  f.out_bf16 = out_dtype == RELAY_BF16;
+  f.lse_out = lse_out;
   f.n_rows = (long long)dims->total_q * dims->num_q_heads;
   return launch_fuse(f, dims->head_dim, s);
 }

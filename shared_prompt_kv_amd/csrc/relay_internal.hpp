@@ -30,6 +30,9 @@ struct SysArgs {
   int steps_per_head;
   int total_steps;
   int parts;
+  // sys_attn_mfma only: 1 = causal, query token t sees system keys 0..t only (the
+  // prompt's own attention in the offline prefill; scale must be > 0)
+  int causal;
 };
 
 // Tile configuration of sys_attn: rt row tiles (16 rows each) per wave, wk waves
@@ -141,6 +144,12 @@ hipError_t launch_sys_attn_tiled(const SysArgs& a, const SysConfig& c, int in_dt
 constexpr int kSysMfmaRows = 128;
 constexpr int kSysMfmaSlots = 512;
 constexpr int kSysMfmaStep = 64;
+// Partials in which some row sees fewer than this many keys compute P.V with P split
+// into bf16 hi + lo (two products): there single probabilities can be large and bf16
+// rounding of P alone would cost up to 2^-9 of the output.  Where every row sees many
+// keys the weight is spread over them and P is rounded once.
+constexpr int kPSplitBelow = 256;
+constexpr int kSysCausalRunsPerSlot = 4;  // causal plans: runs per resident workgroup slot
 
 // The part (of `parts` equal runs over `total` steps) that holds step x.
 inline __host__ __device__ int lean_part_of(long long x, int total, int parts) {

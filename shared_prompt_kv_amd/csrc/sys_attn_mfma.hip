@@ -137,6 +137,9 @@ __device__ __forceinline__ void mf_zero_tail(char* buf, int nvalid) {
   }
 }
 
+// CAUSAL: the offline prefill's attention (query token t sees keys 0..t); its own
+// instantiation, so the decode kernel carries none of the masking or P splitting.
+template <bool CAUSAL>
 __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   const int lane = lane_id();
@@ -171,6 +174,9 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
   const int m = rb * kSysMfmaRows + wave * mf::kRowsPerWave + r32;  // this lane's stacked row
   const bool row_ok = m < M;
   const int t = m / a.group, gi = m % a.group;
+  // causal: query token t sees keys 0..t; the workgroup's tokens span [t_lo, t_hi]
+  const int t_lo = rb * kSysMfmaRows / a.group;
+  const int t_hi = (min(rb * kSysMfmaRows + kSysMfmaRows, M) - 1) / a.group;
 
   // one segment per head the run touches: keys [ls0 * 64, min(ls1 * 64, Ls)) of head h
   while (sbeg < send) {
@@ -180,7 +186,15 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
     sbeg += ls1 - ls0;
     const int key_begin = ls0 * mf::kKB;
     const int key_end = min(ls1 * mf::kKB, Ls);
-    const int nsteps = ls1 - ls0;
+    int nsteps = ls1 - ls0;
+    // causal: steps no token of the workgroup sees are skipped (maybe all), and where
+    // some token sees between 1 and kPSplitBelow - 1 of the segment's keys P is split
+    bool psplit = false;
+    if constexpr (CAUSAL) {
+      const int seen = min(key_end, t_hi + 1) - key_begin;
+      nsteps = seen > 0 ? (seen + mf::kKB - 1) / mf::kKB : 0;
+      psplit = seen > 0 && t_lo + 1 - key_begin < kPSplitBelow;
+    }
     const char* kbase = static_cast<const char*>(a.sys_k) + (size_t)h * Ls * mf::D * 2;
     const char* vbase = static_cast<const char*>(a.sys_v) + (size_t)h * ntile * mf::D * kTile * 2;
 
@@ -206,9 +220,11 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
         mf_issue(dst, kbase, vbase, key0, Ls, ntile);
     };
 
-    issue(lds_raw, key_begin);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if (nsteps > 0) {
+      issue(lds_raw, key_begin);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
 
     for (int s = 0; s < nsteps; ++s) {
       const int key0 = key_begin + s * mf::kKB;
@@ -245,7 +261,16 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
 #pragma unroll
         for (int i = 0; i < 32; ++i) sc[i] = -sc[i];
       }
-      // No masking before the exponentials: in the step holding the prompt's end, rows
+      // causal steps some token of the workgroup does not wholly see: score i of the
+      // lane (key 16 (i / 8) + 8 hh + i % 8 of the step) is masked unless that key is
+      // <= t and < Ls; with scale > 0 a masked score's exponential is exactly 0
+      if (CAUSAL && key0 + mf::kKB - 1 > t_lo) {
+        const int lim_c = min(t + 1, Ls) - key0 - 8 * hh;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          if (16 * (i >> 3) + (i & 7) >= lim_c) sc[i] = neg_inf();
+      }
+      // Otherwise no masking before the exponentials: in the step holding the prompt's end, rows
       // past it hold copies of the last key (mf_issue clamps them), whose scores leave
       // the maximum unchanged, and their values are zero in LDS, so they add nothing to
       // O; only the row sum below leaves them out.
@@ -283,22 +308,44 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
       }
       // ---- P (bf16) per 16-key block kb: k slots 0..7 = keys 0..7 (lanes hh = 0),
       // 8..15 = keys 8..15 (hh = 1), i.e. sc[8 kb .. 8 kb + 7]; then O^T += V^T P^T
-      u32x4 pb[4];
+      u32x4 pb[4], pl[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const float* p = sc + 8 * kb;
         pb[kb] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                        pack_bf16x2(p[6], p[7])};
+        if constexpr (CAUSAL) {  // P = hi + lo, both bf16: lo is what rounding left out
+          const u32x4 h = pb[kb];
+          pl[kb] = psplit ? u32x4{pack_bf16x2(p[0] - bf16_lo_as_float(h[0]), p[1] - bf16_hi_as_float(h[0])),
+                                  pack_bf16x2(p[2] - bf16_lo_as_float(h[1]), p[3] - bf16_hi_as_float(h[1])),
+                                  pack_bf16x2(p[4] - bf16_lo_as_float(h[2]), p[5] - bf16_hi_as_float(h[2])),
+                                  pack_bf16x2(p[6] - bf16_lo_as_float(h[3]), p[7] - bf16_hi_as_float(h[3]))}
+                          : u32x4{0u, 0u, 0u, 0u};
+        }
       }
       const char* vt = buf + mf::kTileBytes;
+      if (CAUSAL && psplit) {  // a second product per fragment with the low parts
 #pragma unroll
-      for (int db = 0; db < mf::D / 32; ++db) {
-        const int d = 32 * db + r32;
-        const char* vrow = vt + d * 128;
+        for (int db = 0; db < mf::D / 32; ++db) {
+          const int d = 32 * db + r32;
+          const char* vrow = vt + d * 128;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(vrow + (((2 * kb + hh) ^ (d & 7)) << 4));
-          o[db] = mfma32(v, pb[kb], o[db]);
+          for (int kb = 0; kb < 4; ++kb) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(vrow + (((2 * kb + hh) ^ (d & 7)) << 4));
+            o[db] = mfma32(v, pb[kb], o[db]);
+            o[db] = mfma32(v, pl[kb], o[db]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < mf::D / 32; ++db) {
+          const int d = 32 * db + r32;
+          const char* vrow = vt + d * 128;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(vrow + (((2 * kb + hh) ^ (d & 7)) << 4));
+            o[db] = mfma32(v, pb[kb], o[db]);
+          }
         }
       }
       if (more) __builtin_amdgcn_s_waitcnt(0);  // the next step's tiles have landed
@@ -339,7 +386,10 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
 }
 
 hipError_t launch_sys_attn_mfma(const SysArgs& a, int nwg, hipStream_t stream) {
-  hipLaunchKernelGGL(sys_attn_mfma_kernel, dim3(nwg), dim3(mf::kThreads), kSysMfmaLds, stream, a);
+  if (a.causal)
+    hipLaunchKernelGGL(sys_attn_mfma_kernel<true>, dim3(nwg), dim3(mf::kThreads), kSysMfmaLds, stream, a);
+  else
+    hipLaunchKernelGGL(sys_attn_mfma_kernel<false>, dim3(nwg), dim3(mf::kThreads), kSysMfmaLds, stream, a);
   return hipGetLastError();
 }
 

@@ -57,7 +57,7 @@ class RelayError(RuntimeError):
 EXPORTS = ("relay_abi_version", "relay_strerror", "relay_last_error", "relay_workspace_size",
            "relay_get_plan", "relay_attn_decode", "relay_attn_decode_timed", "relay_sys_attn",
            "relay_ctx_attn", "relay_fuse", "relay_validate", "relay_rope_table", "relay_rope_append",
-           "relay_rope_system", "relay_system_fill")
+           "relay_rope_system", "relay_system_fill", "relay_prefill_workspace_size", "relay_prefill_attn")
 
 _lib = None
 
@@ -85,6 +85,10 @@ def load_library(path: str = LIB_PATH):
     lib.relay_attn_decode_timed.restype = ctypes.c_int
     lib.relay_sys_attn.argtypes = [D, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.relay_sys_attn.restype = ctypes.c_int
+    lib.relay_prefill_workspace_size.argtypes = [D, i32]
+    lib.relay_prefill_workspace_size.restype = sz
+    lib.relay_prefill_attn.argtypes = [D, vp, vp, vp, i32, vp, i32, vp, vp, sz, vp]
+    lib.relay_prefill_attn.restype = ctypes.c_int
     lib.relay_ctx_attn.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.relay_ctx_attn.restype = ctypes.c_int
     lib.relay_fuse.argtypes = [ctypes.c_int64, i32, vp, vp, vp, vp, vp, i32, vp, vp]
@@ -219,6 +223,43 @@ def relay_sys_attn(q, sys_k, sys_v, sys_len, dims: relay_dims, *, workspace_buf=
                                          int(sys_len), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
                                          _stream(stream)))
     return o, lse
+
+
+def prefill_dims(q, sys_k, scale: float, out_dtype=torch.float32) -> relay_dims:
+    """relay_dims for relay_prefill_attn: the prompt's L tokens as one request."""
+    L, Hq, d = q.shape
+    Hkv = sys_k.shape[0]
+    nb = -(-L // 16)
+    return relay_dims(1, Hq, Hkv, d, 16, nb, nb, L, L, L, float(scale), _dtype_code(q.dtype), _dtype_code(out_dtype))
+
+
+def prefill_workspace(dims: relay_dims, sys_len: int, device) -> torch.Tensor:
+    """A workspace of relay_prefill_workspace_size bytes."""
+    lib = load_library()
+    n = lib.relay_prefill_workspace_size(ctypes.byref(dims), int(sys_len))
+    if n == 0 and lib.relay_last_error():
+        raise RelayError(-1, lib.relay_last_error().decode())
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def relay_prefill_attn(q, sys_k, sys_v, sys_len, scale: float, *, out_dtype=torch.float32, with_lse=False,
+                       workspace_buf=None, stream=None):
+    """Causal attention of the system prompt's tokens over the system cache -> (out, lse or None).
+
+    q [L, H_q, d] (position-embedded); sys_k / sys_v the system cache.  Row (t, h) sees
+    system keys 0..t.  Raises RelayError(RELAY_ERR_UNSUPPORTED) off the matrix-core
+    path (bf16, head_dim 128, more than 64 rows per KV head)."""
+    _require_device(q, sys_k, sys_v)
+    dims = prefill_dims(q, sys_k, scale, out_dtype)
+    lib = load_library()
+    out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if with_lse else None
+    if workspace_buf is None:
+        workspace_buf = prefill_workspace(dims, sys_len, q.device)
+    _check(lib.relay_prefill_attn(ctypes.byref(dims), _ptr(q), _ptr(sys_k), _ptr(sys_v), int(sys_len), _ptr(out),
+                                  _dtype_code(out_dtype), _ptr(lse) if lse is not None else None,
+                                  _ptr(workspace_buf), workspace_buf.numel(), _stream(stream)))
+    return out, lse
 
 
 def relay_ctx_attn(q, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens, dims: relay_dims,

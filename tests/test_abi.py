@@ -178,3 +178,35 @@ def test_binding_refuses_cpu_tensors(lib):
     q = torch.zeros(4, 8, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         R.relay_fuse(q.float(), q[..., 0].float(), q.float(), q[..., 0].float())
+
+
+def test_prefill_entry_rejects_what_it_does_not_run(lib):
+    """relay_prefill_attn runs only on the matrix-core system kernel; everything else
+    is refused with an error code before any device work (fake pointers here)."""
+    p = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(1 << 20)
+
+    def call(d, sys_len=300, out_dtype=0, n=1 << 30):
+        return lib.relay_prefill_attn(ctypes.byref(d), p, p, p, sys_len, p, out_dtype, None, ws, n, None)
+
+    big = dict(batch=1, total_q=300, max_q_len=300, max_ctx_len=300, max_blocks_per_seq=19, num_blocks=1)
+    assert call(base_dims(**big, in_dtype=0)) == -2                        # fp32: not on matrix cores
+    assert call(base_dims(**big, head_dim=64)) == -2                        # head_dim 64
+    assert call(base_dims(**dict(big, total_q=16, max_q_len=16))) == -2     # 16 x 4 = 64 rows per KV head
+    assert call(base_dims(**big, scale=-0.1)) == -1                         # masked scores need scale > 0
+    assert call(base_dims(**big), sys_len=0) == -1
+    assert call(base_dims(**big), out_dtype=5) == -2
+    d = base_dims(**big)
+    need = lib.relay_prefill_workspace_size(ctypes.byref(d), 300)
+    assert need >= lib.relay_workspace_size(ctypes.byref(d), 300) > 0
+    assert call(d, n=need - 1) == -3
+
+
+@pytest.mark.parametrize("L,Hq,Hkv", [(37, 8, 2), (2048, 32, 32), (8192, 32, 8)])
+def test_prefill_dims_pass_the_checks(lib, L, Hq, Hkv):
+    """The binding's dims for relay_prefill_attn are valid and get a workspace."""
+    import torch
+    q = torch.empty((L, Hq, 128), dtype=torch.bfloat16)
+    sk = torch.empty((Hkv, L, 128), dtype=torch.bfloat16)
+    d = R.prefill_dims(q, sk, 128 ** -0.5)
+    assert lib.relay_prefill_workspace_size(ctypes.byref(d), L) > 0, lib.relay_last_error()

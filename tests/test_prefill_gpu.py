@@ -15,7 +15,12 @@ from tests.test_rope_gpu import assert_stored_close, upload
 
 pytestmark = pytest.mark.gpu
 
-CASES = [("bf16", 37, 8, 2, 128), ("bf16", 512, 32, 8, 128), ("f32", 100, 4, 4, 64)]
+# (dtype, L_s, H_q, H_kv, d, method): bf16 d = 128 runs the causal matrix-core kernel
+# ("auto") and, for comparison, the decode path; other inputs only the decode path
+CASES = [("bf16", 37, 8, 2, 128, "auto"), ("bf16", 37, 8, 2, 128, "decode"),
+         ("bf16", 200, 4, 4, 128, "auto"), ("bf16", 512, 32, 8, 128, "auto"),
+         ("bf16", 512, 32, 8, 128, "decode"), ("bf16", 1100, 8, 8, 128, "auto"),
+         ("f32", 100, 4, 4, 64, "auto")]
 
 
 def host(dtype, x):
@@ -23,16 +28,18 @@ def host(dtype, x):
     return x.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else x.numpy()
 
 
-@pytest.mark.parametrize("dtype,L,Hq,Hkv,d", CASES)
-def test_prefill_matches_oracle_and_cache_round_trips(dtype, L, Hq, Hkv, d, tmp_path):
-    say(f"[parity] system prefill {dtype} L={L} Hq={Hq} Hkv={Hkv} d={d}")
+@pytest.mark.parametrize("dtype,L,Hq,Hkv,d,method", CASES)
+def test_prefill_matches_oracle_and_cache_round_trips(dtype, L, Hq, Hkv, d, method, tmp_path):
+    say(f"[parity] system prefill {dtype} L={L} Hq={Hq} Hkv={Hkv} d={d} method={method}")
     spec = W.config_spec(2).replace(dtype=dtype)
     r = np.random.default_rng(L)
     conv = (lambda x: W.f32_to_bf16_bits(x.astype(np.float32))) if dtype == "bf16" else (lambda x: x.astype(np.float32))
     q, k, v = (conv(r.standard_normal(s)) for s in ((L, Hq, d), (L, Hkv, d), (L, Hkv, d)))
     tab = R.relay_rope_table(L, d)
     scale = 1.0 / np.sqrt(d)
-    sys_k, sys_v, out = prefill.prefill_system(upload(spec, q), upload(spec, k), upload(spec, v), tab, scale)
+    qd, kd, vd = upload(spec, q), upload(spec, k), upload(spec, v)
+    assert prefill.uses_matrix_cores(qd, kd, scale) == (dtype == "bf16")
+    sys_k, sys_v, out = prefill.prefill_system(qd, kd, vd, tab, scale, method=method)
     torch.cuda.synchronize()
     ek, ev, eo = rope.prefill_expect(q, k, v, dtype)
     assert_stored_close(spec, host(dtype, sys_k), ek, "system keys")
