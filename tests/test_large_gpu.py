@@ -1,5 +1,6 @@
-"""GPU: a system cache larger than 4 GiB per tensor (byte offsets past 2^32), on the
-single-wave unit path (16 stacked rows) and on the matrix-core path (160 rows).
+"""GPU: a system cache, and a context page pool, larger than 4 GiB per tensor (byte
+offsets past 2^32), on the single-wave unit path (at most 64 stacked rows) and on the
+matrix-core path.
 
 The system K/V are drawn on the device (torch's seeded generator; 2^31+ values are too
 many to draw on the host in a test).  The oracle checks sampled rows one by one: for a
@@ -57,3 +58,30 @@ def test_system_cache_past_4_gib(batch):
                          np.array([1], np.int32), np.array([0, 1], np.int32))
         ref, _ = oracle.Problem(sub).attention()
         check(out[tok:tok + 1, rows], ref, "bf16", f"request {b} head {hk}")
+
+
+@pytest.mark.parametrize("batch", [4, 40])
+def test_context_pages_past_4_gib(batch):
+    """The same requests with their pages moved to the end of a page pool larger than
+    4 GiB per tensor (block ids relabelled; the rest of the pool is random): every
+    output against the oracle on the original workload (relabelling pages leaves
+    attention unchanged)."""
+    spec = W.config_spec(5).replace(batch=batch, sys_len=100, ctx_lo=16, ctx_hi=700, q_lo=1, q_hi=3)
+    say(f"[parity] context pages past 4 GiB: batch={batch}")
+    w = W.generate(spec)
+    t = R.to_device(w)
+    nb, hkv, _, d = t["ctx_k_pages"].shape
+    big = (2**32 // (hkv * 16 * d * 2)) + 4096   # pages: each tensor > 4 GiB
+    g = torch.Generator(device="cuda").manual_seed(5)
+    pool_k = torch.randn((big, hkv, 16, d), generator=g, device="cuda").to(torch.bfloat16)
+    pool_v = torch.randn((big, hkv, d, 16), generator=g, device="cuda").to(torch.bfloat16)
+    off = big - nb
+    pool_k[off:] = t["ctx_k_pages"]
+    pool_v[off:] = t["ctx_v_pages"]
+    bt = t["block_tables"]
+    t.update(ctx_k_pages=pool_k, ctx_v_pages=pool_v, block_tables=torch.where(bt >= 0, bt + off, bt).contiguous())
+    assert pool_k.numel() * 2 > 2**32 and int(t["block_tables"].max()) * hkv * 16 * d * 2 > 2**32
+    out = R.decode_workload(t).cpu().numpy()
+    torch.cuda.synchronize()
+    ref, _ = oracle.Problem(w).attention()
+    check(out, ref, "bf16", "decode over relabelled pages")
