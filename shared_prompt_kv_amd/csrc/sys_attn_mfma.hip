@@ -157,7 +157,9 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
   const int total = gridDim.x;
   int li = blockIdx.x;
   if (a.xcd_remap) li = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int rb = li % a.row_blocks;
+  // causal: a row block's work grows with its tokens, so the last row blocks (the
+  // longest workgroups) are dispatched first
+  const int rb = CAUSAL ? a.row_blocks - 1 - li % a.row_blocks : li % a.row_blocks;
   const int part = li / a.row_blocks;
   if (part >= a.parts) return;  // padding workgroup (whole workgroup)
   const int S = a.total_steps, P = a.parts, sph = a.steps_per_head;
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
 
     // loads of the step at key0 into buffer dst: plain offsets unless it holds the end
     auto issue = [&](char* dst, int key0) {
-      if (key0 + mf::kKB <= Ls)
+      if (!CAUSAL && key0 + mf::kKB <= Ls)  // (the causal kernel keeps the registers)
         mf_issue_full(dst, kbase + (size_t)key0 * (mf::D * 2), vbase + (size_t)key0 * (mf::D * 2), wave, lo_);
       else
         mf_issue(dst, kbase, vbase, key0, Ls, ntile);
