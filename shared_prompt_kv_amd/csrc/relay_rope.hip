@@ -11,8 +11,10 @@
 // first d/2 columns, sin in the last), built once by relay_rope_table with the angle
 // reduced in fp64.
 //
-// Elementwise and HBM-bound (a few KB per token): one workgroup of d/2 lanes per
-// (token, head) row, lane i rotating the pair (i, i + d/2).
+// Elementwise and HBM-bound (a few KB per token): d/2 lanes per (token, head) row,
+// lane i rotating the pair (i, i + d/2), and kRopeThreads / (d/2) rows per workgroup
+// (a prefill embeds thousands of tokens: one small workgroup per row would leave the
+// launch bound by workgroup dispatch).
 #include "relay_device.hpp"
 #include "relay_internal.hpp"
 
@@ -38,15 +40,19 @@ __global__ void rope_table_kernel(float* cos_sin, int max_pos, int d, double bas
   }
 }
 
+constexpr int kRopeThreads = 256;
+
 // New token t (row t of q_new) of request b sits at context position
-// p = c_b - n_b + t_local, absolute position L_s + p.  Rows: blockIdx.z < H_q are query
-// heads (rotated into q_out), the rest KV heads (K rotated and V copied into page
-// block_tables[b][p / 16], slot p % 16).  Rows whose position or page is out of range
-// are skipped (nothing written).
-__global__ void rope_append_kernel(RopeArgs a) {
-  const int b = blockIdx.x, tl = blockIdx.y, row = blockIdx.z;
-  const int i = threadIdx.x;
+// p = c_b - n_b + t_local, absolute position L_s + p.  Rows (heads of the token):
+// row < H_q are query heads (rotated into q_out), the rest KV heads (K rotated and V
+// copied into page block_tables[b][p / 16], slot p % 16).  Rows whose position or page
+// is out of range are skipped (nothing written).
+__global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeArgs a) {
   const int half = a.head_dim / 2, d = a.head_dim;
+  const int b = blockIdx.x, tl = blockIdx.y;
+  const int row = blockIdx.z * (kRopeThreads / half) + threadIdx.x / half;
+  const int i = threadIdx.x % half;
+  if (row >= a.num_q_heads + a.num_kv_heads) return;
   int qs = b, nq = 1;
   if (a.cu_q_lens) {
     qs = a.cu_q_lens[b];
@@ -81,9 +87,12 @@ __global__ void rope_append_kernel(RopeArgs a) {
 }
 
 // System keys [H_kv, L_s, d] rotated in place at positions 0 .. L_s - 1 (the offline
-// prefill's position embedding).
-__global__ void rope_system_kernel(void* sys_k, const float* cos_sin, int sys_len, int d, int bf16) {
-  const int j = blockIdx.x, hk = blockIdx.y, i = threadIdx.x, half = d / 2;
+// prefill's position embedding); kRopeThreads / (d/2) keys per workgroup.
+__global__ __launch_bounds__(kRopeThreads) void rope_system_kernel(void* sys_k, const float* cos_sin, int sys_len,
+                                                                   int d, int bf16) {
+  const int half = d / 2, hk = blockIdx.y, i = threadIdx.x % half;
+  const int j = blockIdx.x * (kRopeThreads / half) + threadIdx.x / half;
+  if (j >= sys_len) return;
   const float c = cos_sin[(size_t)j * d + i], s = cos_sin[(size_t)j * d + half + i];
   const size_t base = ((size_t)hk * sys_len + j) * d;
   const float x1 = rope_load(sys_k, base + i, bf16), x2 = rope_load(sys_k, base + half + i, bf16);
@@ -95,10 +104,13 @@ __global__ void rope_system_kernel(void* sys_k, const float* cos_sin, int sys_le
 // as a projection produces them (k_raw / v_raw [L_s, H_kv, d]), into the system cache
 // layouts: sys_k [H_kv, L_s, d] with RoPE at position j, sys_v [H_kv, ceil(L_s/16),
 // d, 16] (dimension-major 16-key tiles; the tail tile's padding is written as 0).
-__global__ void system_fill_kernel(const void* k_raw, const void* v_raw, const float* cos_sin, void* sys_k,
-                                   void* sys_v, int sys_len, int num_kv_heads, int d, int bf16) {
-  const int j = blockIdx.x, hk = blockIdx.y, i = threadIdx.x, half = d / 2;
+__global__ __launch_bounds__(kRopeThreads) void system_fill_kernel(const void* k_raw, const void* v_raw,
+                                                                   const float* cos_sin, void* sys_k, void* sys_v,
+                                                                   int sys_len, int num_kv_heads, int d, int bf16) {
+  const int half = d / 2, hk = blockIdx.y, i = threadIdx.x % half;
+  const int j = blockIdx.x * (kRopeThreads / half) + threadIdx.x / half;
   const int ntile = (sys_len + kTile - 1) / kTile;
+  if (j >= ntile * kTile) return;
   const size_t vt = ((size_t)hk * ntile + j / kTile) * (size_t)d * kTile + j % kTile;
   if (j >= sys_len) {  // padding keys of the tail tile (grid covers whole tiles)
     rope_store(sys_v, vt + (size_t)i * kTile, 0.f, bf16);
@@ -118,8 +130,9 @@ __global__ void system_fill_kernel(const void* k_raw, const void* v_raw, const f
 hipError_t launch_system_fill(const void* k_raw, const void* v_raw, const float* cos_sin, void* sys_k, void* sys_v,
                               int sys_len, int num_kv_heads, int d, int bf16, hipStream_t s) {
   const int padded = (sys_len + kTile - 1) / kTile * kTile;
-  hipLaunchKernelGGL(system_fill_kernel, dim3(padded, num_kv_heads), dim3(d / 2), 0, s, k_raw, v_raw, cos_sin,
-                     sys_k, sys_v, sys_len, num_kv_heads, d, bf16);
+  const int per = kRopeThreads / (d / 2);
+  hipLaunchKernelGGL(system_fill_kernel, dim3((padded + per - 1) / per, num_kv_heads), dim3(kRopeThreads), 0, s,
+                     k_raw, v_raw, cos_sin, sys_k, sys_v, sys_len, num_kv_heads, d, bf16);
   return hipGetLastError();
 }
 
@@ -129,15 +142,17 @@ hipError_t launch_rope_table(float* cos_sin, int max_pos, int d, double base, hi
 }
 
 hipError_t launch_rope_append(const RopeArgs& a, int max_q_len, hipStream_t s) {
-  hipLaunchKernelGGL(rope_append_kernel, dim3(a.batch, max_q_len, a.num_q_heads + a.num_kv_heads),
-                     dim3(a.head_dim / 2), 0, s, a);
+  const int per = kRopeThreads / (a.head_dim / 2);
+  hipLaunchKernelGGL(rope_append_kernel, dim3(a.batch, max_q_len, (a.num_q_heads + a.num_kv_heads + per - 1) / per),
+                     dim3(kRopeThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_rope_system(void* sys_k, const float* cos_sin, int sys_len, int num_kv_heads, int d, int bf16,
                               hipStream_t s) {
-  hipLaunchKernelGGL(rope_system_kernel, dim3(sys_len, num_kv_heads), dim3(d / 2), 0, s, sys_k, cos_sin, sys_len,
-                     d, bf16);
+  const int per = kRopeThreads / (d / 2);
+  hipLaunchKernelGGL(rope_system_kernel, dim3((sys_len + per - 1) / per, num_kv_heads), dim3(kRopeThreads), 0, s,
+                     sys_k, cos_sin, sys_len, d, bf16);
   return hipGetLastError();
 }
 
