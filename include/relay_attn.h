@@ -52,11 +52,14 @@
  * Layouts (E-byte elements unless stated):
  *   q            [T_q, H_q, d]               tokens of request b are rows
  *                                            cu_q_lens[b] .. cu_q_lens[b+1]-1
- *   sys_k        [H_kv, L_s, d]              system keys, key-major
+ *   sys_k        [H_kv, ceil(L_s/16), d/G, 16, G]  system keys in 16-key tiles,
+ *                                            chunk-major inside a tile (the tail
+ *                                            tile's padding keys are ignored)
  *   sys_v        [H_kv, ceil(L_s/16), d, 16] system values in 16-key tiles,
  *                                            dimension-major inside a tile (the
  *                                            tail tile's padding is ignored)
- *   ctx_k_pages  [num_blocks, H_kv, 16, d]   paged context keys, 16 tokens a page
+ *   ctx_k_pages  [num_blocks, H_kv, d/G, 16, G]  paged context keys, 16 tokens a
+ *                                            page, chunk-major inside a page
  *   ctx_v_pages  [num_blocks, H_kv, d, 16]   paged context values, dimension-major
  *                                            inside a page
  *   block_tables int32 [B, max_blocks_per_seq]  context token j of request b is in
@@ -70,7 +73,11 @@
  *                -inf marks an empty key set
  *   O partials   float32 [T_q, H_q, d]
  * Values are stored dimension-major (d before the 16 keys of a tile/page) so that
- * the keys a matrix-core lane reduces over are contiguous in memory.
+ * the keys a matrix-core lane reduces over are contiguous in memory.  Keys are stored
+ * chunk-major: G = 16 / E elements (8 bf16, 4 fp32) make one 16-byte chunk, and a
+ * tile/page holds chunk 0 of its 16 keys, then chunk 1, ...  Element c of key r of a
+ * tile is at ((c / G) * 16 + r) * G + c % G.  The 64 lanes that load one matrix-core
+ * operand of a 16-key tile then read 1 KB of contiguous memory.
  */
 #ifndef RELAY_ATTN_H
 #define RELAY_ATTN_H
@@ -82,7 +89,7 @@
 extern "C" {
 #endif
 
-#define RELAY_ATTN_ABI_VERSION 1
+#define RELAY_ATTN_ABI_VERSION 2  /* 2: keys stored in chunk-major 16-key tiles */
 
 /* element types */
 #define RELAY_F32 0  /* IEEE float32 */
@@ -277,7 +284,7 @@ int relay_rope_table(float* cos_sin, int32_t max_pos, int32_t head_dim, float ba
  *   K page slot  = RoPE(k_new[t, hk], sys_len + p)           hk < H_kv
  *   V page slot  = v_new[t, hk]
  * at page block_tables[b][p / 16], slot p % 16 of ctx_k_pages [num_blocks, H_kv,
- * 16, d] / ctx_v_pages [num_blocks, H_kv, d, 16].  q_new / q_out [T_q, H_q, d] and
+ * d/G, 16, G] / ctx_v_pages [num_blocks, H_kv, d, 16].  q_new / q_out [T_q, H_q, d] and
  * k_new / v_new [T_q, H_kv, d] are in_dtype (q_out may alias q_new).  ctx_lens
  * already include the new tokens.  cos_sin: relay_rope_table's table, max_pos rows;
  * a row whose position is >= max_pos, or whose page id is out of range, is not
@@ -290,8 +297,9 @@ int relay_rope_append(const relay_dims* dims, int32_t sys_len, const void* q_new
                       void* ctx_v_pages, void* stream);
 
 /*
- * The offline prefill's position embedding of the system keys: sys_k [H_kv, L_s, d]
- * (in_dtype) rotated in place at positions 0 .. sys_len - 1.  sys_len <= max_pos.
+ * The offline prefill's position embedding of the system keys: sys_k [H_kv,
+ * ceil(L_s/16), d/G, 16, G] (in_dtype) rotated in place at positions 0 .. sys_len - 1
+ * (padding keys untouched).  sys_len <= max_pos.
  */
 int relay_rope_system(int32_t num_kv_heads, int32_t head_dim, int32_t sys_len, int32_t in_dtype,
                       void* sys_k, const float* cos_sin, int32_t max_pos, void* stream);
@@ -300,9 +308,9 @@ int relay_rope_system(int32_t num_kv_heads, int32_t head_dim, int32_t sys_len, i
  * The offline prefill's cache fill (the system K/V are filled before serving:
  * atyun.com article, section "RelayAttention"): the system prompt's keys and values
  * as a projection produces them, token-major k_raw / v_raw [L_s, H_kv, d] (in_dtype),
- * written into the system cache: sys_k [H_kv, L_s, d] with RoPE at positions
- * 0 .. L_s - 1 and sys_v [H_kv, ceil(L_s/16), d, 16] (the tail tile's padding set to
- * 0).  cos_sin: relay_rope_table's table, sys_len <= max_pos.
+ * written into the system cache: sys_k [H_kv, ceil(L_s/16), d/G, 16, G] with RoPE
+ * at positions 0 .. L_s - 1 and sys_v [H_kv, ceil(L_s/16), d, 16] (the tail tiles'
+ * padding keys set to 0 in both).  cos_sin: relay_rope_table's table, sys_len <= max_pos.
  */
 int relay_system_fill(int32_t num_kv_heads, int32_t head_dim, int32_t sys_len, int32_t in_dtype,
                       const void* k_raw, const void* v_raw, const float* cos_sin, int32_t max_pos,

@@ -39,9 +39,11 @@
  *
  * Storage layouts (the C ABI's):
  *   q            [T_q, H_q, d]
- *   sys_k        [H_kv, L_s, d]
+ *   sys_k        [H_kv, ceil(L_s/16), d/G, 16, G]   (16-key tiles, chunk-major)
  *   sys_v        [H_kv, ceil(L_s/16), d, 16]   (16-key tiles, dim-major)
- *   ctx_k        [num_blocks, H_kv, 16, d]
+ *   ctx_k        [num_blocks, H_kv, d/G, 16, G]   (chunk-major within a page)
+ *                G = elements per 16-byte chunk (8 bf16, 4 fp32; d when smaller): a key tile holds
+ *                chunk 0 of its 16 keys, then chunk 1, ...
  *   ctx_v        [num_blocks, H_kv, d, 16]     (dim-major within a page)
  *   block_tables [B, max_blocks]  context key j of request b lives in page
  *                block_tables[b][j/16], slot j%16
@@ -105,15 +107,29 @@ static int request_of(const oracle_problem* p, int t) {
   return b;
 }
 
+/* Index of element c of key r (0..15) inside one 16-key tile of keys (g elements per
+ * 16-byte chunk; the whole row when d is smaller). */
+static size_t key_in_tile(int r, int c, int dtype, int d) {
+  int g = dtype == ORACLE_BF16 ? 8 : 4;
+  if (g > d) g = d;
+  return ((size_t)(c / g) * ORACLE_BLOCK + r) * g + c % g;
+}
+
 /* Element c of key j of the concatenated sequence for (request b, kv head hk). */
 static double key_elem(const oracle_problem* p, int b, int hk, int j, int c) {
   int d = p->head_dim, Ls = p->sys_len;
-  if (j < Ls)
-    return elem(p->sys_k, ((size_t)hk * Ls + j) * d + c, p->dtype);
+  if (j < Ls) {
+    size_t ntile = (size_t)(Ls + ORACLE_SYS_TILE - 1) / ORACLE_SYS_TILE;
+    return elem(p->sys_k,
+                ((size_t)hk * ntile + j / ORACLE_SYS_TILE) * ORACLE_SYS_TILE * d +
+                    key_in_tile(j % ORACLE_SYS_TILE, c, p->dtype, d),
+                p->dtype);
+  }
   j -= Ls;
   int blk = p->block_tables[(size_t)b * p->max_blocks_per_seq + j / ORACLE_BLOCK];
   return elem(p->ctx_k,
-              (((size_t)blk * p->num_kv_heads + hk) * ORACLE_BLOCK + j % ORACLE_BLOCK) * d + c,
+              ((size_t)blk * p->num_kv_heads + hk) * ORACLE_BLOCK * d +
+                  key_in_tile(j % ORACLE_BLOCK, c, p->dtype, d),
               p->dtype);
 }
 

@@ -82,17 +82,21 @@ def rotated_workload(w, base: float = ROPE_BASE, ctx_offset=None):
     # queries [T_q, H_q, d]
     q = _values(w, w.q)
     r.q = _store(w, rotate(q, token_positions(w)[:, None]))
-    # system keys [H_kv, L_s, d]
+    # system keys: key tiles -> [H_kv, padded L_s, d], first L_s rotated, back to tiles
     if L > 0:
-        sk = _values(w, w.sys_k)
-        r.sys_k = _store(w, rotate(sk, np.arange(L)[None, :]))
-    # context keys through the block tables: [num_blocks, H_kv, 16, d]
-    ck = _values(w, w.ctx_k_pages).copy()
+        sk = W.k_untile(w.sys_k)
+        sk = sk.reshape(sk.shape[0], -1, d)
+        rot = _store(w, rotate(_values(w, sk[:, :L]), np.arange(L)[None, :]))
+        sk = sk.copy()
+        sk[:, :L] = rot
+        r.sys_k = W.k_tiles(sk.reshape(H_kv, -1, 16, d), spec.dtype)
+    # context keys through the block tables: key tiles -> [num_blocks, H_kv, 16, d]
+    ck = _values(w, W.k_untile(w.ctx_k_pages)).copy()
     for b in range(spec.batch):
         for j in range(int(w.ctx_lens[b])):
             p = int(w.block_tables[b, j // 16])
             ck[p, :, j % 16, :] = rotate(ck[p, :, j % 16, :], off + j)
-    r.ctx_k_pages = _store(w, ck)
+    r.ctx_k_pages = W.k_tiles(_store(w, ck), spec.dtype)
     r.ctx_k_dense = r.ctx_v_dense = None
     return r
 
@@ -109,10 +113,10 @@ def append_expect(w, q_new, k_new, v_new, base: float = ROPE_BASE):
 def prefill_expect(q_raw, k_raw, v_raw, dtype: str, base: float = ROPE_BASE):
     """The offline prefill of a system prompt, as values: queries q_raw [L, H_q, d] and
     keys / values k_raw, v_raw [L, H_kv, d] in storage form (bf16 bit patterns or
-    float32), before position embedding.  Returns (sys_k [H_kv, L, d] and sys_v
-    [H_kv, ceil(L/16), d, 16] in storage form, out [L, H_q, d] fp64): the system cache
-    (keys embedded at positions 0..L-1, values in 16-key dimension-major tiles, tail
-    padding 0) and every prompt token's causal attention over keys 0..its own position
+    float32), before position embedding.  Returns (sys_k [H_kv, ceil(L/16), d/G, 16, G]
+    and sys_v [H_kv, ceil(L/16), d, 16] in storage form, out [L, H_q, d] fp64): the
+    system cache (keys embedded at positions 0..L-1 in 16-key chunk-major tiles, values
+    in 16-key dimension-major tiles, tail padding 0 in both) and every prompt token's causal attention over keys 0..its own position
     (computed by the fp64 C oracle on a one-request workload whose L tokens are new)."""
     from . import Problem
     L, H_q, d = q_raw.shape
@@ -125,17 +129,20 @@ def prefill_expect(q_raw, k_raw, v_raw, dtype: str, base: float = ROPE_BASE):
     k_rot = store(rotate(vals(k_raw), pos[:, None]))          # [L, H_kv, d]
     q_rot = store(rotate(vals(q_raw), pos[:, None]))          # [L, H_q, d]
     ntile = (L + 15) // 16
-    sys_k = np.ascontiguousarray(k_rot.transpose(1, 0, 2))
+    sys_k = np.zeros((H_kv, ntile * 16, d), dtype=k_rot.dtype)
+    sys_k[:, :L] = k_rot.transpose(1, 0, 2)
+    sys_k = W.k_tiles(sys_k.reshape(H_kv, ntile, 16, d), dtype)
     sys_v = np.zeros((H_kv, ntile * 16, d), dtype=np.asarray(v_raw).dtype)
     sys_v[:, :L] = np.asarray(v_raw).transpose(1, 0, 2)
     sys_v = np.ascontiguousarray(sys_v.reshape(H_kv, ntile, 16, d).transpose(0, 1, 3, 2))
     # the prompt as one request: pages 0..ntile-1 in order, every token new
     kp = np.zeros((ntile * 16, H_kv, d), dtype=k_rot.dtype)
     kp[:L] = k_rot
-    kp = np.ascontiguousarray(kp.reshape(ntile, 16, H_kv, d).transpose(0, 2, 1, 3))
+    kp = W.k_tiles(kp.reshape(ntile, 16, H_kv, d).transpose(0, 2, 1, 3), dtype)
     vp = np.ascontiguousarray(sys_v.transpose(1, 0, 2, 3))     # [ntile, H_kv, d, 16]
     spec = W.WorkloadSpec("prefill", 0, 0, dtype, 1, H_q, H_kv, d, 0, "fixed", L, L, q_lo=L, q_hi=L)
-    empty = np.zeros((H_kv, 0, d), dtype=k_rot.dtype)
+    G = W.k_chunk(dtype, d)
+    empty = np.zeros((H_kv, 0, d // G, 16, G), dtype=k_rot.dtype)
     w = W.Workload(spec, q_rot, empty, np.zeros((H_kv, 0, d, 16), dtype=k_rot.dtype), kp, vp,
                    np.arange(ntile, dtype=np.int32)[None, :], np.array([L], np.int32),
                    np.array([L], np.int32), np.array([0, L], np.int32))

@@ -32,12 +32,14 @@ def prefix_shared(t: dict) -> dict:
     if L % PAGE:
         raise ValueError(f"system length {L} is not a multiple of {PAGE}: no whole shared pages")
     ck, cv, bt = t["ctx_k_pages"], t["ctx_v_pages"], t["block_tables"]
-    nb, H_kv, _, d = ck.shape
+    nb, H_kv = ck.shape[:2]
+    d = cv.shape[2]
     ns = L // PAGE
     if ns:
-        # sys_k [H_kv, L, d] -> pages [ns, H_kv, 16, d]; sys_v [H_kv, ns, d, 16] -> [ns, H_kv, d, 16]
-        sk = t["sys_k"].reshape(H_kv, ns, PAGE, d).permute(1, 0, 2, 3)
-        sv = t["sys_v"].reshape(H_kv, ns, d, PAGE).permute(1, 0, 2, 3)
+        # the system caches are already 16-key tiles of the page layouts:
+        # sys_k [H_kv, ns, d/G, 16, G] -> [ns, H_kv, d/G, 16, G]; sys_v [H_kv, ns, d, 16] -> [ns, H_kv, d, 16]
+        sk = t["sys_k"].reshape(H_kv, ns, *ck.shape[2:]).transpose(0, 1)
+        sv = t["sys_v"].reshape(H_kv, ns, d, PAGE).transpose(0, 1)
         pool_k = torch.cat([sk, ck], 0).contiguous()
         pool_v = torch.cat([sv, cv], 0).contiguous()
     else:

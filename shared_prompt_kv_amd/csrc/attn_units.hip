@@ -69,7 +69,8 @@ __device__ __forceinline__ void sys_unit(const UnitArgs& a, int u, float* lds) {
   const int key_begin = chunk * a.sys_chunk_len;
   const int key_end = min(key_begin + a.sys_chunk_len, Ls);
   const int ntile = (Ls + kTile - 1) / kTile;
-  const char* kbase = static_cast<const char*>(a.sys_k) + (size_t)h * Ls * D * E;
+  // both caches are 16-key tiles, ntile per KV head (keys chunk-major, values dim-major)
+  const char* kbase = static_cast<const char*>(a.sys_k) + (size_t)h * ntile * kTile * D * E;
   const char* vbase = static_cast<const char*>(a.sys_v) + (size_t)h * ntile * D * kTile * E;
 
   // step s covers system tiles key_begin/16 + 2s and + 2s + 1; a page past the end of
@@ -80,8 +81,8 @@ __device__ __forceinline__ void sys_unit(const UnitArgs& a, int u, float* lds) {
     const int ka = key_begin + 2 * kTile * st_;
     const int kb = ka + kTile < Ls ? ka + kTile : ka;
     StepAddr r;
-    r.ka = kbase + (size_t)ka * D * E;
-    r.kb = kbase + (size_t)kb * D * E;
+    r.ka = kbase + (size_t)(ka / kTile) * kTile * D * E;
+    r.kb = kbase + (size_t)(kb / kTile) * kTile * D * E;
     r.ra = min(r16, Ls - 1 - ka);
     r.rb = min(r16, Ls - 1 - kb);
     r.va = vbase + (size_t)(ka / kTile) * D * kTile * E;

@@ -18,8 +18,10 @@
 //     16-byte (bf16) or 32-byte (fp32) load.
 //   * The reduction order inside one MFMA does not matter for the sum, so any
 //     assignment of head dimensions (for S) or keys (for O) to the k slots is
-//     valid as long as the A and B operands use the same one.  Each lane loads
-//     16 bytes of its row at byte offset 64*kk + 16*(l/16).
+//     valid as long as the A and B operands use the same one.  For product kk a
+//     lane loads 16 bytes of its query row at byte offset 64*kk + 16*(l/16), and the
+//     same head dimensions of its key: chunk 4*kk + l/16 of the key's 16-key tile,
+//     which stores keys chunk-major (see key_chunk_offset).
 //
 // bf16 uses v_mfma_f32_16x16x32_bf16 (one 16-byte chunk = 8 elements per
 // instruction); fp32 uses v_mfma_f32_16x16x4f32 (one chunk = 4 instructions).
@@ -422,18 +424,23 @@ __device__ __forceinline__ void mfma_pstep(f32x4& acc, const VFrag4<float>& va, 
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb.c.w), p.p[7], acc, 0, 0, 0);
 }
 
-// Issues the K loads of a step: kpa/kpb are the bases of the two pages' 16 K rows,
-// krow_a/krow_b the row this lane reads (clamped where a page is short).
+// Byte offset of 16-byte chunk c of key r inside a 16-key tile of keys.  Key tiles
+// are stored chunk-major: chunk 0 of the tile's 16 keys, then chunk 1, ...  The chunk a
+// lane needs for k slot group q4 of product kk is c = 4 kk + q4 (head dims 32 kk + 8 q4
+// .. + 7 for bf16), so for a whole tile the 64 lanes of one load read 1 KB contiguous.
+__device__ inline int key_chunk_offset(int r, int c) { return (c * kTile + r) * 16; }
+
+// Issues the K loads of a step: kpa/kpb are the two key tiles (pages), krow_a/krow_b
+// the key this lane reads (clamped where a tile is short).
 template <typename T, int D>
 __device__ __forceinline__ void issue_k(StepK<T, D>& f, const char* kpa, const char* kpb, int krow_a, int krow_b) {
-  constexpr int E = Elem<T>::kBytes;
   const int q4 = lane_id() >> 4;
-  const char* ra = kpa + krow_a * D * E + 16 * q4;
-  const char* rb = kpb + krow_b * D * E + 16 * q4;
+  const char* ra = kpa + key_chunk_offset(krow_a, q4);
+  const char* rb = kpb + key_chunk_offset(krow_b, q4);
 #pragma unroll
   for (int kk = 0; kk < StepK<T, D>::NCH; ++kk) {
-    f.a[kk] = ld16(ra + 64 * kk);
-    f.b[kk] = ld16(rb + 64 * kk);
+    f.a[kk] = ld16(ra + 4 * kTile * 16 * kk);
+    f.b[kk] = ld16(rb + 4 * kTile * 16 * kk);
   }
 }
 

@@ -20,6 +20,13 @@
 
 namespace relay {
 
+// Element index of head dimension c of key r (0..15) inside a 16-key tile of keys:
+// tiles are chunk-major, 16-byte chunks of 8 bf16 / 4 fp32 elements.
+__device__ __forceinline__ size_t key_tile_elem(int r, int c, int bf16) {
+  const int g = bf16 ? 8 : 4;
+  return ((size_t)(c / g) * kTile + r) * g + c % g;
+}
+
 __device__ __forceinline__ float rope_load(const void* p, size_t i, int bf16) {
   if (bf16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
   return static_cast<const float*>(p)[i];
@@ -78,32 +85,36 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(RopeArgs a) {
   const int slot = p % kTile;
   const size_t src = ((size_t)t * a.num_kv_heads + hk) * d;
   const float k1 = rope_load(a.k_new, src + i, a.bf16), k2 = rope_load(a.k_new, src + half + i, a.bf16);
-  const size_t kdst = (((size_t)page * a.num_kv_heads + hk) * kTile + slot) * d;
-  rope_store(a.ctx_k, kdst + i, k1 * c - k2 * s, a.bf16);
-  rope_store(a.ctx_k, kdst + half + i, k2 * c + k1 * s, a.bf16);
+  const size_t kdst = ((size_t)page * a.num_kv_heads + hk) * kTile * d;  // the page's key tile
+  rope_store(a.ctx_k, kdst + key_tile_elem(slot, i, a.bf16), k1 * c - k2 * s, a.bf16);
+  rope_store(a.ctx_k, kdst + key_tile_elem(slot, half + i, a.bf16), k2 * c + k1 * s, a.bf16);
   const size_t vdst = ((size_t)page * a.num_kv_heads + hk) * (size_t)d * kTile + slot;
   rope_store(a.ctx_v, vdst + (size_t)i * kTile, rope_load(a.v_new, src + i, a.bf16), a.bf16);
   rope_store(a.ctx_v, vdst + (size_t)(half + i) * kTile, rope_load(a.v_new, src + half + i, a.bf16), a.bf16);
 }
 
-// System keys [H_kv, L_s, d] rotated in place at positions 0 .. L_s - 1 (the offline
-// prefill's position embedding); kRopeThreads / (d/2) keys per workgroup.
+// System keys (16-key tiles [H_kv, ceil(L_s/16), d/G, 16, G]) rotated in place at
+// positions 0 .. L_s - 1 (the offline prefill's position embedding); kRopeThreads /
+// (d/2) keys per workgroup.
 __global__ __launch_bounds__(kRopeThreads) void rope_system_kernel(void* sys_k, const float* cos_sin, int sys_len,
                                                                    int d, int bf16) {
   const int half = d / 2, hk = blockIdx.y, i = threadIdx.x % half;
   const int j = blockIdx.x * (kRopeThreads / half) + threadIdx.x / half;
   if (j >= sys_len) return;
   const float c = cos_sin[(size_t)j * d + i], s = cos_sin[(size_t)j * d + half + i];
-  const size_t base = ((size_t)hk * sys_len + j) * d;
-  const float x1 = rope_load(sys_k, base + i, bf16), x2 = rope_load(sys_k, base + half + i, bf16);
-  rope_store(sys_k, base + i, x1 * c - x2 * s, bf16);
-  rope_store(sys_k, base + half + i, x2 * c + x1 * s, bf16);
+  const int ntile = (sys_len + kTile - 1) / kTile;
+  const size_t base = ((size_t)hk * ntile + j / kTile) * kTile * d;
+  const size_t e1 = base + key_tile_elem(j % kTile, i, bf16), e2 = base + key_tile_elem(j % kTile, half + i, bf16);
+  const float x1 = rope_load(sys_k, e1, bf16), x2 = rope_load(sys_k, e2, bf16);
+  rope_store(sys_k, e1, x1 * c - x2 * s, bf16);
+  rope_store(sys_k, e2, x2 * c + x1 * s, bf16);
 }
 
 // The offline prefill's cache fill: the system prompt's keys and values, token-major
 // as a projection produces them (k_raw / v_raw [L_s, H_kv, d]), into the system cache
-// layouts: sys_k [H_kv, L_s, d] with RoPE at position j, sys_v [H_kv, ceil(L_s/16),
-// d, 16] (dimension-major 16-key tiles; the tail tile's padding is written as 0).
+// layouts: sys_k [H_kv, ceil(L_s/16), d/G, 16, G] (chunk-major 16-key tiles) with RoPE
+// at position j, sys_v [H_kv, ceil(L_s/16), d, 16] (dimension-major 16-key tiles); the
+// tail tiles' padding keys are written as 0.
 __global__ __launch_bounds__(kRopeThreads) void system_fill_kernel(const void* k_raw, const void* v_raw,
                                                                    const float* cos_sin, void* sys_k, void* sys_v,
                                                                    int sys_len, int num_kv_heads, int d, int bf16) {
@@ -112,7 +123,11 @@ __global__ __launch_bounds__(kRopeThreads) void system_fill_kernel(const void* k
   const int ntile = (sys_len + kTile - 1) / kTile;
   if (j >= ntile * kTile) return;
   const size_t vt = ((size_t)hk * ntile + j / kTile) * (size_t)d * kTile + j % kTile;
+  const size_t kt = ((size_t)hk * ntile + j / kTile) * (size_t)d * kTile;
+  const size_t k_e1 = kt + key_tile_elem(j % kTile, i, bf16), k_e2 = kt + key_tile_elem(j % kTile, half + i, bf16);
   if (j >= sys_len) {  // padding keys of the tail tile (grid covers whole tiles)
+    rope_store(sys_k, k_e1, 0.f, bf16);
+    rope_store(sys_k, k_e2, 0.f, bf16);
     rope_store(sys_v, vt + (size_t)i * kTile, 0.f, bf16);
     rope_store(sys_v, vt + (size_t)(half + i) * kTile, 0.f, bf16);
     return;
@@ -120,9 +135,8 @@ __global__ __launch_bounds__(kRopeThreads) void system_fill_kernel(const void* k
   const size_t src = ((size_t)j * num_kv_heads + hk) * d;
   const float c = cos_sin[(size_t)j * d + i], s = cos_sin[(size_t)j * d + half + i];
   const float k1 = rope_load(k_raw, src + i, bf16), k2 = rope_load(k_raw, src + half + i, bf16);
-  const size_t kd = ((size_t)hk * sys_len + j) * d;
-  rope_store(sys_k, kd + i, k1 * c - k2 * s, bf16);
-  rope_store(sys_k, kd + half + i, k2 * c + k1 * s, bf16);
+  rope_store(sys_k, k_e1, k1 * c - k2 * s, bf16);
+  rope_store(sys_k, k_e2, k2 * c + k1 * s, bf16);
   rope_store(sys_v, vt + (size_t)i * kTile, rope_load(v_raw, src + i, bf16), bf16);
   rope_store(sys_v, vt + (size_t)(half + i) * kTile, rope_load(v_raw, src + half + i, bf16), bf16);
 }

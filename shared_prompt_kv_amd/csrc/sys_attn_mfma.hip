@@ -21,8 +21,10 @@
 //     accumulators, 16 keys per product: k slots 0..3 hold keys 4 (l/32) + 0..3, slots
 //     4..7 keys 8 + 4 (l/32) + 0..3 of the 16-key block; A is V^T with the same key
 //     order, two 8-byte reads from the dimension-major LDS tile.
-// LDS tiles are XOR-swizzled in 16-byte chunks (K: by key % 16, V: by dim % 8) so
-// those reads hit distinct banks.  Softmax uses a lazily moved reference (rows
+// The K tile sits in LDS chunk-major ([16-byte chunk][64 keys]), as the key cache
+// stores its 16-key tiles, so a load instruction fetches whole 256-byte runs of the
+// cache and a wave's operand read is 512 contiguous bytes per half wave; the V tile is
+// XOR-swizzled in 16-byte chunks (by dim % 8) so its reads hit distinct banks.  Softmax uses a lazily moved reference (rows
 // rescale only when their maximum grows by more than 2^8).
 #include "relay_device.hpp"
 #include "relay_internal.hpp"
@@ -62,11 +64,19 @@ __device__ __forceinline__ int mf_key_of_row(int row) {
   return (row & ~15) + ((q >= 4 && q < 8) ? q + 4 : ((q >= 8 && q < 12) ? q - 4 : q));
 }
 
+// Offset of 16-byte chunk c of the key held by LDS row `row` (0..63) of a step, from
+// the step's first key tile: key tiles are 16 keys x 256 bytes, chunk-major.
+__device__ __forceinline__ uint32_t mf_key_offset(int row, int c) {
+  const int k = mf_key_of_row(row);
+  return (uint32_t)((k >> 4) * (kTile * mf::D * 2) + key_chunk_offset(k & 15, c));
+}
+
 // Issues the loads of the step whose first key is key0 straight into an LDS buffer:
 // lane i of a wave's load lands at the instruction's LDS base + 16 i, so each lane
-// fetches the global 16 bytes that belong at its position of the swizzled layout.  K
-// rows past the keys are clamped (their scores are masked); V tiles past the last are
-// clamped (mf_zero_tail clears values of keys that do not exist).
+// fetches the global 16 bytes that belong at its position of the LDS layout (K: LDS
+// position p holds chunk p / 64 of row p % 64).  K rows past the keys are clamped
+// (their scores are masked); V tiles past the last are clamped (mf_zero_tail clears
+// values of keys that do not exist).
 __device__ __forceinline__ void mf_issue(char* buf, const char* kbase, const char* vbase, int key0, int Ls,
                                          int ntile) {
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -74,8 +84,9 @@ __device__ __forceinline__ void mf_issue(char* buf, const char* kbase, const cha
   for (int j = 0; j < mf::kChunks; ++j) {
     const int base = mf::kThreads * j + kWave * wave;  // first 16-byte position of this load
     const int p = base + lane;
-    const int row = p >> 4, c = (p & 15) ^ (row & 15);
-    const char* src = kbase + (size_t)min(key0 + mf_key_of_row(row), Ls - 1) * mf::D * 2 + c * 16;
+    const int row = p & 63, c = p >> 6;
+    const int key = min(key0 + mf_key_of_row(row), Ls - 1);
+    const char* src = kbase + (size_t)(key / kTile) * (kTile * mf::D * 2) + key_chunk_offset(key % kTile, c);
     __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(buf + base * 16), 16, 0, 0);
   }
 #pragma unroll
@@ -90,7 +101,7 @@ __device__ __forceinline__ void mf_issue(char* buf, const char* kbase, const cha
 }
 
 // Per-lane byte offsets of one step's loads relative to its first key key0: both
-// layouts hold 256 bytes per key (a 128-dim bf16 key row; a 16-key value tile is 4096
+// layouts hold 256 bytes per key (a 16-key tile of 128-dim bf16 keys or values is 4096
 // bytes), and steps start at multiples of 64 keys, so every load of a step is
 // base + 256 key0 + a constant of the lane.  Steps that end inside the prompt use
 // these; the step holding the prompt's end goes through mf_issue (clamped rows).
@@ -105,8 +116,7 @@ __device__ __forceinline__ MfLaneOffsets mf_lane_offsets(int wave) {
 #pragma unroll
   for (int j = 0; j < mf::kChunks; ++j) {
     const int p = mf::kThreads * j + kWave * wave + lane;
-    const int row = p >> 4, c = (p & 15) ^ (row & 15);
-    o.k[j] = (uint32_t)(mf_key_of_row(row) * mf::D * 2 + c * 16);
+    o.k[j] = mf_key_offset(p & 63, p >> 6);
     const int d = p >> 3, cv = (p & 7) ^ (d & 7);
     o.v[j] = (uint32_t)((cv >> 1) * (mf::D * kTile * 2) + d * (kTile * 2) + (cv & 1) * 16);
   }
@@ -197,7 +207,7 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
       nsteps = seen > 0 ? (seen + mf::kKB - 1) / mf::kKB : 0;
       psplit = seen > 0 && t_lo + 1 - key_begin < kPSplitBelow;
     }
-    const char* kbase = static_cast<const char*>(a.sys_k) + (size_t)h * Ls * mf::D * 2;
+    const char* kbase = static_cast<const char*>(a.sys_k) + (size_t)h * ntile * kTile * mf::D * 2;
     const char* vbase = static_cast<const char*>(a.sys_v) + (size_t)h * ntile * mf::D * kTile * 2;
 
     // this lane's query row (B operand of S^T: 8 consecutive dims of 16 per product)
@@ -244,11 +254,10 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         sacc[kb2] = f32x16{};
-        const int key = 32 * kb2 + r32;
-        const char* krow = buf + key * 256;
+        const char* krow = buf + (32 * kb2 + r32) * 16;  // LDS row 32 kb2 + r32, chunk-major
 #pragma unroll
         for (int kk = 0; kk < mf::D / 16; ++kk) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(krow + (((2 * kk + hh) ^ (key & 15)) << 4));
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(krow + (2 * kk + hh) * (mf::kKB * 16));
           sacc[kb2] = mfma32(ka, qf[kk], sacc[kb2]);
         }
       }

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kWave* WK* WR) void sys_attn_tiled_kernel(SysArgs a
   const int key_end = min(key_begin + a.chunk_len, Ls);
   const int nsteps = (key_end - key_begin + kStep - 1) / kStep;
   const int ntile = (Ls + kTile - 1) / kTile;
-  const char* kbase = static_cast<const char*>(a.sys_k) + (size_t)h * Ls * D * E;
+  const char* kbase = static_cast<const char*>(a.sys_k) + (size_t)h * ntile * kTile * D * E;  // key tiles
   const char* vbase = static_cast<const char*>(a.sys_v) + (size_t)h * ntile * D * kTile * E;
 
   for (int s = kl; s < nsteps; s += WK) {
@@ -87,8 +87,8 @@ __global__ __launch_bounds__(kWave* WK* WR) void sys_attn_tiled_kernel(SysArgs a
     u32x4 kfa[NCH], kfb[NCH];
 #pragma unroll
     for (int kk = 0; kk < NCH; ++kk) {
-      kfa[kk] = ld16(kbase + (size_t)ka * D * E + 64 * kk + 16 * q4);
-      kfb[kk] = ld16(kbase + (size_t)kb * D * E + 64 * kk + 16 * q4);
+      kfa[kk] = ld16(kbase + (size_t)(ka / kTile) * kTile * D * E + key_chunk_offset(ka % kTile, 4 * kk + q4));
+      kfb[kk] = ld16(kbase + (size_t)(kb / kTile) * kTile * D * E + key_chunk_offset(kb % kTile, 4 * kk + q4));
     }
     // V^T fragments: keys key0 + 8*q4 .. +7 of every 16-dim tile
     const int vkey = key0 + 8 * q4;

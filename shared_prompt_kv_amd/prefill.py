@@ -41,7 +41,7 @@ def uses_matrix_cores(q_raw: torch.Tensor, k_raw: torch.Tensor, scale: float) ->
 
 def prefill_system(q_raw: torch.Tensor, k_raw: torch.Tensor, v_raw: torch.Tensor, cos_sin: torch.Tensor,
                    scale: float, *, out_dtype=torch.float32, method: str = "auto", stream=None):
-    """(sys_k [H_kv, L_s, d], sys_v [H_kv, ceil(L_s/16), d, 16], out [L_s, H_q, d]).
+    """(sys_k [H_kv, ceil(L_s/16), d/G, 16, G], sys_v [H_kv, ceil(L_s/16), d, 16], out [L_s, H_q, d]).
 
     q_raw [L_s, H_q, d], k_raw / v_raw [L_s, H_kv, d]: the prompt's projections before
     position embedding (bf16 or fp32, one dtype).  cos_sin: ``relay.relay_rope_table``
@@ -62,14 +62,14 @@ def prefill_system(q_raw: torch.Tensor, k_raw: torch.Tensor, v_raw: torch.Tensor
         bt = torch.full((1, npages), -1, dtype=torch.int32, device=dev)
         ctx_lens = torch.tensor([L], dtype=torch.int32, device=dev)
         cu = torch.tensor([0, L], dtype=torch.int32, device=dev)
-        no_page = torch.empty((1, H_kv, PAGE, d), dtype=k_raw.dtype, device=dev)
+        no_page = torch.empty(relay.key_tile_shape((1, H_kv), d, k_raw.dtype), dtype=k_raw.dtype, device=dev)
         dims = relay.make_dims(q_raw, no_page, bt, scale=scale, max_ctx_len=L, max_q_len=L)
         q_rot = relay.relay_rope_append(dims, 0, q_raw, k_raw, v_raw, cos_sin, bt, ctx_lens, cu, no_page,
                                         torch.empty((1, H_kv, d, PAGE), dtype=k_raw.dtype, device=dev),
                                         stream=stream)
         out, _ = relay.relay_prefill_attn(q_rot, sys_k, sys_v, L, scale, out_dtype=out_dtype, stream=stream)
         return sys_k, sys_v, out
-    pages_k = torch.empty((npages, H_kv, PAGE, d), dtype=k_raw.dtype, device=dev)
+    pages_k = torch.empty(relay.key_tile_shape((npages, H_kv), d, k_raw.dtype), dtype=k_raw.dtype, device=dev)
     pages_v = torch.empty((npages, H_kv, d, PAGE), dtype=k_raw.dtype, device=dev)
     bt = torch.arange(npages, dtype=torch.int32, device=dev).view(1, npages)
     ctx_lens = torch.tensor([L], dtype=torch.int32, device=dev)
@@ -86,8 +86,8 @@ def save_system_cache(path: str, sys_k: torch.Tensor, sys_v: torch.Tensor, sys_l
                       rope_base: float = 10000.0) -> None:
     """Write the system cache to a safetensors file (tensors and a small JSON header)."""
     from safetensors.torch import save_file
-    meta = {"format": "relay-system-kv/1", "sys_len": str(int(sys_len)), "rope_base": repr(float(rope_base)),
-            "layout": json.dumps({"sys_k": "[H_kv, L_s, d]", "sys_v": "[H_kv, ceil(L_s/16), d, 16]"})}
+    meta = {"format": "relay-system-kv/2", "sys_len": str(int(sys_len)), "rope_base": repr(float(rope_base)),
+            "layout": json.dumps({"sys_k": "[H_kv, ceil(L_s/16), d/G, 16, G]", "sys_v": "[H_kv, ceil(L_s/16), d, 16]"})}
     save_file({"sys_k": sys_k.contiguous().cpu(), "sys_v": sys_v.contiguous().cpu()}, path, metadata=meta)
 
 
@@ -96,7 +96,7 @@ def load_system_cache(path: str, device="cuda"):
     from safetensors import safe_open
     with safe_open(path, framework="pt") as f:
         meta = f.metadata() or {}
-        if meta.get("format") != "relay-system-kv/1":
+        if meta.get("format") != "relay-system-kv/2":
             raise ValueError(f"{path}: not a system KV cache file")
         sys_k = f.get_tensor("sys_k").to(device)
         sys_v = f.get_tensor("sys_v").to(device)

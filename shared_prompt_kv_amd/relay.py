@@ -149,8 +149,10 @@ def make_dims(q: torch.Tensor, ctx_k_pages: torch.Tensor, block_tables: torch.Te
               out_dtype: torch.dtype = torch.float32) -> relay_dims:
     """relay_dims from tensor shapes plus the host-known maxima."""
     Tq, Hq, d = q.shape
-    nb, Hkv, bs, d2 = ctx_k_pages.shape
-    if d2 != d:
+    if ctx_k_pages.dim() != 5:
+        raise ValueError("ctx_k_pages must be key tiles [num_blocks, H_kv, d/G, 16, G]")
+    nb, Hkv, nc, bs, g = ctx_k_pages.shape
+    if nc * g != d:
         raise ValueError("head_dim mismatch between q and ctx_k_pages")
     B, mb = block_tables.shape
     return relay_dims(B, Hq, Hkv, d, bs, mb, nb, Tq, max_q_len, max_ctx_len, float(scale),
@@ -333,22 +335,32 @@ def relay_rope_append(dims: relay_dims, sys_len: int, q_new, k_new, v_new, cos_s
     return q_out
 
 
+def key_tile_shape(lead: tuple, d: int, dtype: torch.dtype) -> tuple:
+    """Shape of key tiles: lead + (d/G, 16, G), G the elements of 16 bytes."""
+    g = 8 if dtype == torch.bfloat16 else 4
+    return (*lead, d // g, 16, g)
+
+
 def relay_rope_system(sys_k, sys_len: int, cos_sin, *, stream=None):
-    """The system keys [H_kv, L_s, d] rotated in place at positions 0 .. sys_len - 1."""
+    """The system keys (key tiles [H_kv, ceil(L_s/16), d/G, 16, G]) rotated in place at
+    positions 0 .. sys_len - 1."""
     _require_device(sys_k, cos_sin)
-    if not sys_k.is_contiguous() or sys_k.dim() != 3:
-        raise ValueError("sys_k must be a contiguous [H_kv, L_s, d] tensor")
-    _check(load_library().relay_rope_system(sys_k.shape[0], sys_k.shape[2], int(sys_len), _dtype_code(sys_k.dtype),
+    if not sys_k.is_contiguous() or sys_k.dim() != 5 or sys_k.shape[1] * 16 < sys_len:
+        raise ValueError("sys_k must be contiguous key tiles [H_kv, ceil(L_s/16), d/G, 16, G]")
+    d = sys_k.shape[2] * sys_k.shape[4]
+    _check(load_library().relay_rope_system(sys_k.shape[0], d, int(sys_len), _dtype_code(sys_k.dtype),
                                             _ptr(sys_k), _ptr(cos_sin), cos_sin.shape[0], _stream(stream)))
     return sys_k
 
 
 def relay_system_fill(k_raw, v_raw, cos_sin, *, sys_k=None, sys_v=None, stream=None):
     """The system cache from token-major k_raw / v_raw [L_s, H_kv, d]: returns
-    (sys_k [H_kv, L_s, d] with RoPE at 0 .. L_s - 1, sys_v [H_kv, ceil(L_s/16), d, 16])."""
+    (sys_k [H_kv, ceil(L_s/16), d/G, 16, G] with RoPE at 0 .. L_s - 1, sys_v
+    [H_kv, ceil(L_s/16), d, 16]); the tail tiles' padding keys are 0."""
     L, H_kv, d = k_raw.shape
     if sys_k is None:
-        sys_k = torch.empty((H_kv, L, d), dtype=k_raw.dtype, device=k_raw.device)
+        sys_k = torch.empty(key_tile_shape((H_kv, (L + 15) // 16), d, k_raw.dtype), dtype=k_raw.dtype,
+                            device=k_raw.device)
     if sys_v is None:
         sys_v = torch.empty((H_kv, (L + 15) // 16, d, 16), dtype=k_raw.dtype, device=k_raw.device)
     _require_device(k_raw, v_raw, cos_sin, sys_k, sys_v)

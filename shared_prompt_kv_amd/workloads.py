@@ -29,7 +29,11 @@ Recipe (all integer ranges inclusive):
   ``block_tables`` rows are padded with -1.  Unused slots of tail pages and spare
   pages are filled with a poison value (finite sentinel K=+1e4, V=-1e4 by default, or
   NaN), which must never reach an output.
-* System V padding: the tail 16-key tile of ``sys_v`` is filled with the same poison.
+* System V padding: the tail 16-key tile of ``sys_v`` is filled with the same poison;
+  so are the padding keys of the tail tile of ``sys_k``.
+* Key layout: keys are stored in 16-key tiles, each tile as ``[d/G, 16, G]`` with G the
+  elements of one 16-byte chunk (8 bf16, 4 fp32; d itself when d is smaller): chunk c
+  of every key of the tile, then chunk c + 1.  ``k_tiles`` / ``k_untile`` convert from / to ``[..., 16, d]``.
 """
 from __future__ import annotations
 
@@ -142,9 +146,9 @@ class Workload:
 
     spec: WorkloadSpec
     q: np.ndarray              # [T_q, H_q, d]
-    sys_k: np.ndarray          # [H_kv, L_s, d]
+    sys_k: np.ndarray          # [H_kv, ceil(L_s/16), d/G, 16, G]  (key tiles)
     sys_v: np.ndarray          # [H_kv, ceil(L_s/16), d, 16]
-    ctx_k_pages: np.ndarray    # [num_blocks, H_kv, 16, d]
+    ctx_k_pages: np.ndarray    # [num_blocks, H_kv, d/G, 16, G]    (key tiles)
     ctx_v_pages: np.ndarray    # [num_blocks, H_kv, d, 16]
     block_tables: np.ndarray   # int32 [B, max_blocks]
     ctx_lens: np.ndarray       # int32 [B]
@@ -170,6 +174,14 @@ class Workload:
     @property
     def max_blocks_per_seq(self) -> int:
         return int(self.block_tables.shape[1])
+
+    def sys_k_keys(self) -> np.ndarray:
+        """System keys in storage form, key-major ``[H_kv, L_s, d]``."""
+        return sys_k_dense(self.sys_k, self.spec.sys_len)
+
+    def ctx_k_keys(self) -> np.ndarray:
+        """Context key pages in storage form, key-major ``[num_blocks, H_kv, 16, d]``."""
+        return k_untile(self.ctx_k_pages)
 
     def values(self, a: np.ndarray) -> np.ndarray:
         """Exact float32 values of a storage array."""
@@ -199,6 +211,30 @@ def _draw_lens(spec: WorkloadSpec) -> tuple:
         raise ValueError(spec.ctx_len_dist)
     ctx = np.maximum(ctx.astype(np.int64), q_lens).astype(np.int32)
     return q_lens, ctx
+
+
+def k_chunk(dtype: str, d: int) -> int:
+    """Elements of one 16-byte chunk of a key row (a whole row when d is below it)."""
+    return min(8 if dtype == BF16 else 4, d)
+
+
+def k_tiles(k: np.ndarray, dtype: str) -> np.ndarray:
+    """Key-major 16-key tiles ``[..., 16, d]`` -> the cache's key layout ``[..., d/G, 16, G]``."""
+    *lead, t, d = k.shape
+    G = k_chunk(dtype, d)
+    return np.ascontiguousarray(k.reshape(*lead, t, d // G, G).swapaxes(-3, -2))
+
+
+def k_untile(k: np.ndarray) -> np.ndarray:
+    """The cache's key layout ``[..., d/G, 16, G]`` -> key-major ``[..., 16, d]``."""
+    *lead, c, t, g = k.shape
+    return np.ascontiguousarray(k.swapaxes(-3, -2).reshape(*lead, t, c * g))
+
+
+def sys_k_dense(sys_k: np.ndarray, sys_len: int) -> np.ndarray:
+    """The system key cache ``[H_kv, ceil(L_s/16), d/G, 16, G]`` as ``[H_kv, L_s, d]``."""
+    t = k_untile(sys_k)
+    return t.reshape(t.shape[0], -1, t.shape[-1])[:, :sys_len]
 
 
 def _to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -233,11 +269,13 @@ def generate(spec: WorkloadSpec, keep_dense: bool = False) -> Workload:
     sk = _rng(spec, S_SYS_K).standard_normal((Hkv, Ls, d), dtype=np.float32)
     if kscale is not None:
         sk *= kscale[:, None, :]
-    sys_k = _to_storage(sk, spec.dtype)
-    del sk
-    sv = _to_storage(_rng(spec, S_SYS_V).standard_normal((Hkv, Ls, d), dtype=np.float32), spec.dtype)
     pk, pv = _poison_values(spec)
     nbs = -(-Ls // SYS_TILE)
+    sys_k = np.full((Hkv, nbs * SYS_TILE, d), pk, dtype=store)
+    sys_k[:, :Ls, :] = _to_storage(sk, spec.dtype)
+    del sk
+    sys_k = k_tiles(sys_k.reshape(Hkv, nbs, SYS_TILE, d), spec.dtype)
+    sv = _to_storage(_rng(spec, S_SYS_V).standard_normal((Hkv, Ls, d), dtype=np.float32), spec.dtype)
     sys_v = np.full((Hkv, nbs * SYS_TILE, d), pv, dtype=store)
     sys_v[:, :Ls, :] = sv
     # [H_kv, nbs, 16, d] -> dim-major tiles [H_kv, nbs, d, 16]
@@ -271,6 +309,7 @@ def generate(spec: WorkloadSpec, keep_dense: bool = False) -> Workload:
         if keep_dense:
             k_dense.append(kb)
             v_dense.append(vb)
+    kp = k_tiles(kp, spec.dtype)
     return Workload(spec, q, sys_k, sys_v, kp, vp, block_tables, ctx_lens, q_lens, cu,
                     k_dense if keep_dense else None, v_dense if keep_dense else None,
                     sv if keep_dense else None)

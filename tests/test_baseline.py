@@ -17,8 +17,14 @@ SPECS = [
 ]
 
 
+def untile(k):
+    """Key tiles [..., d/G, 16, G] -> key-major [..., 16, d]."""
+    return k.transpose(-3, -2).reshape(*k.shape[:-3], k.shape[-2], -1)
+
+
 def gather(pool_k, pool_v, bt, n):
     """K [H_kv, n, d] and V [H_kv, n, d] of positions 0..n-1 through one block-table row."""
+    pool_k = untile(pool_k)
     ks, vs = [], []
     for j in range(n):
         p = int(bt[j // 16])
@@ -43,7 +49,7 @@ def test_prefix_shared_pages_reproduce_system_then_context(spec):
         kb, vb = gather(b["ctx_k_pages"], b["ctx_v_pages"], b["block_tables"][r], c + L)
         kc, vc = gather(t["ctx_k_pages"], t["ctx_v_pages"], t["block_tables"][r], c)
         if L:
-            kc = torch.cat([t["sys_k"].reshape(H_kv, L, d), kc], 1)
+            kc = torch.cat([untile(t["sys_k"]).reshape(H_kv, -1, d)[:, :L], kc], 1)
             vc = torch.cat([sys_v, vc], 1)
         assert torch.equal(kb, kc) and torch.equal(vb, vc)
         # every request's table starts with the same shared page ids

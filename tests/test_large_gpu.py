@@ -35,7 +35,8 @@ def test_system_cache_past_4_gib(batch):
     t = R.to_device(w)
     g = torch.Generator(device="cuda").manual_seed(11)
     ntile = -(-L_SYS // 16)
-    sys_k = torch.randn((H_KV, L_SYS, D), generator=g, device="cuda").to(torch.bfloat16)
+    sys_k = torch.randn(R.key_tile_shape((H_KV, ntile), D, torch.bfloat16), generator=g,
+                        device="cuda").to(torch.bfloat16)   # key tiles (padding keys never read)
     sys_v = torch.randn((H_KV, ntile, D, 16), generator=g, device="cuda").to(torch.bfloat16)
     sys_v[:, -1, :, L_SYS % 16:] = 0   # the tail tile's padding keys
     assert sys_k.numel() * 2 > 2**32 and sys_v.numel() * 2 > 2**32
@@ -70,10 +71,11 @@ def test_context_pages_past_4_gib(batch):
     say(f"[parity] context pages past 4 GiB: batch={batch}")
     w = W.generate(spec)
     t = R.to_device(w)
-    nb, hkv, _, d = t["ctx_k_pages"].shape
+    nb, hkv = t["ctx_k_pages"].shape[:2]
+    d = t["ctx_v_pages"].shape[2]
     big = (2**32 // (hkv * 16 * d * 2)) + 4096   # pages: each tensor > 4 GiB
     g = torch.Generator(device="cuda").manual_seed(5)
-    pool_k = torch.randn((big, hkv, 16, d), generator=g, device="cuda").to(torch.bfloat16)
+    pool_k = torch.randn(R.key_tile_shape((big, hkv), d, torch.bfloat16), generator=g, device="cuda").to(torch.bfloat16)
     pool_v = torch.randn((big, hkv, d, 16), generator=g, device="cuda").to(torch.bfloat16)
     off = big - nb
     pool_k[off:] = t["ctx_k_pages"]

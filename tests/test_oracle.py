@@ -40,7 +40,7 @@ def dense_rows(w):
     s = w.spec
     g = s.num_q_heads // s.num_kv_heads
     q = w.values(w.q).astype(np.float64)
-    sk = w.values(w.sys_k).astype(np.float64)
+    sk = w.values(w.sys_k_keys()).astype(np.float64)
     sv = w.values(w.sys_v_dense).astype(np.float64)
     for b in range(s.batch):
         n_b = int(w.q_lens[b])
@@ -105,7 +105,7 @@ def sdpa_reference(w):
     s = w.spec
     g = s.group
     q = torch.from_numpy(w.values(w.q).astype(np.float64))
-    sk = torch.from_numpy(w.values(w.sys_k).astype(np.float64))          # [Hkv, Ls, d]
+    sk = torch.from_numpy(w.values(w.sys_k_keys()).astype(np.float64))   # [Hkv, Ls, d]
     sv = torch.from_numpy(w.values(w.sys_v_dense).astype(np.float64))    # [Hkv, Ls, d]
     outs, lses = [], []
     for b in range(s.batch):
@@ -177,12 +177,13 @@ def _hand_workload(q, sys_kv, ctx_kv, scale_dim):
     spec = tiny_spec(30, B=1, Hq=1, Hkv=1, d=d, Ls=Ls, lo=c, hi=c)
     w = W.generate(spec, keep_dense=True)
     w.q[0, 0, :] = q
+    G = W.k_chunk(spec.dtype, d)
     for j, (k, v) in enumerate(sys_kv):
-        w.sys_k[0, j, :] = k
+        w.sys_k[0, j // 16, :, j % 16, :] = np.reshape(k, (d // G, G))
         w.sys_v[0, j // 16, :, j % 16] = v
     for j, (k, v) in enumerate(ctx_kv):
         blk = w.block_tables[0, j // 16]
-        w.ctx_k_pages[blk, 0, j % 16, :] = k
+        w.ctx_k_pages[blk, 0, :, j % 16, :] = np.reshape(k, (d // G, G))
         w.ctx_v_pages[blk, 0, :, j % 16] = v
     return w
 

@@ -43,9 +43,10 @@ def assert_stored_close(spec, got, want, what):
 def gather_tokens(w, positions_of):
     """Raw K and V [T, H_kv, d] (storage dtype) of the listed (request, position) pairs."""
     ks, vs = [], []
+    ck = w.ctx_k_keys()
     for b, j in positions_of:
         p = int(w.block_tables[b, j // 16])
-        ks.append(w.ctx_k_pages[p, :, j % 16, :])
+        ks.append(ck[p, :, j % 16, :])
         vs.append(w.ctx_v_pages[p, :, :, j % 16])
     return np.stack(ks), np.stack(vs)
 
@@ -102,13 +103,14 @@ def test_append_then_relay_decode(spec):
     assert_stored_close(spec, host(q_rot), wr.q, "q")
     if L:
         assert_stored_close(spec, host(t["sys_k"]).reshape(wr.sys_k.shape), wr.sys_k, "system keys")
-    ck = host(t["ctx_k_pages"])
+    ck = W.k_untile(host(t["ctx_k_pages"]))                  # key-major [page, H_kv, slot, d]
     live = np.zeros(ck.shape[:1] + ck.shape[2:3], bool)       # [page, slot]
     for b, j in hist:
         live[int(w.block_tables[b, j // 16]), j % 16] = True
+    want = W.k_untile(wr.ctx_k_pages)
     assert_stored_close(spec, ck[live.nonzero()[0], :, live.nonzero()[1]],
-                        wr.ctx_k_pages[live.nonzero()[0], :, live.nonzero()[1]], "context keys")
-    assert np.array_equal(ck[~live.any(1)], w.ctx_k_pages[~live.any(1)]), "pages nobody owns were written"
+                        want[live.nonzero()[0], :, live.nonzero()[1]], "context keys")
+    assert np.array_equal(ck[~live.any(1)], w.ctx_k_keys()[~live.any(1)]), "pages nobody owns were written"
     assert np.array_equal(host(t["ctx_v_pages"]), w.ctx_v_pages), "values must be stored unchanged"
     ref, _ = Problem(wr).attention()
     check(out.cpu().numpy(), ref, spec.dtype, "decode on the embedded cache")

@@ -50,12 +50,13 @@ def brute_force(w, rows):
         c = int(w.ctx_lens[b])
         lo, hi = int(w.cu_q_lens[b]), int(w.cu_q_lens[b + 1])
         n = hi - lo
+        sk, ck = w.sys_k_keys(), w.ctx_k_keys()
         for hk in range(spec.num_kv_heads):
-            ks = [vals(w.sys_k[hk, j]) for j in range(L)]
+            ks = [vals(sk[hk, j]) for j in range(L)]
             vs = [vals(w.sys_v[hk, j // 16, :, j % 16]) for j in range(L)]
             for j in range(c):
                 p = int(w.block_tables[b, j // 16])
-                ks.append(vals(w.ctx_k_pages[p, hk, j % 16]))
+                ks.append(vals(ck[p, hk, j % 16]))
                 vs.append(vals(w.ctx_v_pages[p, hk, :, j % 16]))
             K = np.stack([np.asarray(rope.rotate(k, i), np.float32).astype(np.float64) for i, k in enumerate(ks)])
             V = np.stack(vs)
@@ -100,7 +101,11 @@ def test_prefill_oracle_against_brute_force(dtype):
     assert not back(sv).transpose(0, 1, 3, 2).reshape(Hkv, -1, d)[:, L:].any()
     qv = back(conv(rope.rotate(back(q), np.arange(L)[:, None])))
     kv = back(conv(rope.rotate(back(k), np.arange(L)[:, None])))
-    np.testing.assert_array_equal(back(sk), kv.transpose(1, 0, 2))
+    np.testing.assert_array_equal(back(W.sys_k_dense(sk, L)), kv.transpose(1, 0, 2))
+    assert not back(W.k_untile(sk)).reshape(Hkv, -1, d)[:, L:].any()
+    G = W.k_chunk(dtype, d)
+    for j, c in ((0, 0), (5, G - 1), (17, G), (36, d - 1)):   # key tiles by index arithmetic
+        assert back(sk[1, j // 16, c // G, j % 16, c % G]) == kv[j, 1, c]
     for t in (0, 1, 15, 16, 36):
         for h in range(Hq):
             s = kv[: t + 1, h // 2] @ qv[t, h] / np.sqrt(d)

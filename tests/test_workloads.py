@@ -50,15 +50,19 @@ def test_paging_structure_and_poison():
     used = w.block_tables[w.block_tables >= 0]
     assert len(np.unique(used)) == len(used)                  # pages are not shared
     assert w.num_blocks == len(used) + spec.batch             # one spare page per request
-    vals_k = w.values(w.ctx_k_pages)
+    ck = w.ctx_k_keys()
+    vals_k = w.values(ck)
     vals_v = w.values(w.ctx_v_pages)
+    G = W.k_chunk(spec.dtype, spec.head_dim)
     for b in range(spec.batch):
         c = int(w.ctx_lens[b])
         n = -(-c // 16)
         assert np.all(w.block_tables[b, :n] >= 0) and np.all(w.block_tables[b, n:] == -1)
         for j in range(c):
             blk = w.block_tables[b, j // 16]
-            np.testing.assert_array_equal(w.ctx_k_pages[blk, :, j % 16, :], w.ctx_k_dense[b][j])
+            np.testing.assert_array_equal(ck[blk, :, j % 16, :], w.ctx_k_dense[b][j])
+            for c in (0, G - 1, G, spec.head_dim - 1):   # key tiles: chunk-major, G per chunk
+                np.testing.assert_array_equal(w.ctx_k_pages[blk, :, c // G, j % 16, c % G], w.ctx_k_dense[b][j][:, c])
             np.testing.assert_array_equal(w.ctx_v_pages[blk, :, :, j % 16], w.ctx_v_dense[b][j])
         tail = w.block_tables[b, n - 1]
         assert np.all(np.isnan(vals_k[tail, :, c - (n - 1) * 16:, :]))
@@ -70,6 +74,11 @@ def test_paging_structure_and_poison():
     for j in (0, 15, 16, 36):
         np.testing.assert_array_equal(w.sys_v[:, j // 16, :, j % 16], w.sys_v_dense[:, j, :])
     assert np.all(np.isnan(sv[:, 2, :, 37 - 32:]))
+    # system K: the same tiles as the pages, poison in the tail tile's padding keys
+    sk = w.values(W.k_untile(w.sys_k))
+    assert sk.shape == (spec.num_kv_heads, 3, 16, spec.head_dim)
+    np.testing.assert_array_equal(w.sys_k_keys(), W.k_untile(w.sys_k).reshape(spec.num_kv_heads, 48, -1)[:, :37])
+    assert np.all(np.isnan(sk[:, 2, 37 - 32:, :]))
 
 
 def test_bf16_rounding_is_nearest_even():
@@ -83,6 +92,6 @@ def test_bf16_rounding_is_nearest_even():
 def test_gqa_k_channel_scale_applied():
     spec = W.config_spec(4).replace(batch=2, sys_len=64, ctx_median=20, ctx_cap=40)
     w = W.generate(spec)
-    ks = W.bf16_bits_to_f32(w.sys_k).astype(np.float64)
+    ks = W.bf16_bits_to_f32(w.sys_k_keys()).astype(np.float64)
     std = ks.reshape(-1, spec.head_dim).std(0)
     assert std.max() / std.min() > 2.0  # per-channel scale in [0.5, 2]
