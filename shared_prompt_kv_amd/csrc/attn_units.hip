@@ -1,14 +1,14 @@
 // Streaming attention units for gfx950: RelayAttention's system-attention and
 // context-attention steps as workgroup-sized work units.
 //
-// System unit (KV head h, key chunk, 16-row tile): the tile holds 16 of the
-// M = T_q * g query rows that use KV head h, stacked across all requests of the
-// batch, so the system K/V of the chunk serve every request's query at once
-// (RelayAttention paper, abstract; atyun.com article, section "RelayAttention":
-// matrix-vector products against the system prompt grouped into matrix-matrix
-// products).  When M > 16 the row tiles of one chunk are separate units placed on
-// the same XCD back to back, so the chunk leaves HBM once and the repeat reads hit
-// that XCD's L2.
+// System unit (KV head h, key chunk, row unit of one or two 16-row tiles): the
+// tiles hold 16 or 32 of the M = T_q * g query rows that use KV head h, stacked across
+// all requests of the batch, so the system K/V of the chunk serve every request's
+// query at once (RelayAttention paper, abstract; atyun.com article, section
+// "RelayAttention": matrix-vector products against the system prompt grouped into
+// matrix-matrix products).  When there are more rows than one unit holds, the row
+// units of one chunk are separate units placed on the same XCD back to back, so the
+// chunk leaves HBM once and the repeat reads hit that XCD's L2.
 //
 // Context unit (request b, KV head h, split, row block): causal attention of the
 // request's g * n_b query rows over one fixed-length run of its paged context.
@@ -40,30 +40,38 @@ __device__ inline void load_q_tile(u32x4* qf, const void* q, size_t row_index, b
     qf[kk] = valid ? ld16(qp + 64 * kk + 16 * q4) : u32x4{0u, 0u, 0u, 0u};
 }
 
-template <typename T, int D, int WK>
+// SRT row tiles (16 rows each) per unit: 2 when M <= 32 and the system step is long
+// enough to give every workgroup several units, so the chunk is read once for all 32
+// rows; 1 otherwise (more, shorter units).
+template <typename T, int D, int SRT, int WK>
 __device__ __forceinline__ void sys_unit(const UnitArgs& a, int u, float* lds) {
   constexpr int E = Elem<T>::kBytes;
   const int lane = lane_id();
   const int kl = threadIdx.x / kWave;
-  const int q4 = lane >> 4, r16 = lane & 15;
-  // unit id -> (row tile, chunk group): the row tiles of one chunk are 8 ids apart,
+  const int r16 = lane & 15;
+  // unit id -> (row unit, chunk group): the row units of one chunk are 8 ids apart,
   // i.e. on the same XCD (workgroup i runs on XCD i % 8) and dispatched together.
   const int slot = u >> 3;
-  const int rt = slot % a.sys_row_tiles;
+  const int ru = slot % a.sys_row_tiles;
   const int grp = (u & 7) + 8 * (slot / a.sys_row_tiles);
   const int chunk = grp % a.sys_chunks;
   const int h = grp / a.sys_chunks;
   if (h >= a.num_kv_heads) return;  // padding unit: uniform over the workgroup
 
   const int M = a.total_q * a.group;
-  const int row = rt * 16 + r16;
-  const int t = row / a.group, gi = row % a.group;
-  const size_t qrow = (size_t)t * a.num_q_heads + (size_t)h * a.group + gi;
-  u32x4 qf[1][StepK<T, D>::NCH];
-  load_q_tile<T, D>(qf[0], a.q, qrow, row < M);
-  RowState<D> st[1];
-  st[0].init();
-  const int last[1] = {a.sys_len - 1};
+  u32x4 qf[SRT][StepK<T, D>::NCH];
+  RowState<D> st[SRT];
+  int last[SRT];
+  size_t qrow[SRT];
+#pragma unroll
+  for (int r = 0; r < SRT; ++r) {
+    const int row = (ru * SRT + r) * 16 + r16;
+    const int t = row / a.group, gi = row % a.group;
+    qrow[r] = row < M ? (size_t)t * a.num_q_heads + (size_t)h * a.group + gi : ~(size_t)0;
+    load_q_tile<T, D>(qf[r], a.q, qrow[r], row < M);
+    st[r].init();
+    last[r] = a.sys_len - 1;
+  }
 
   const int Ls = a.sys_len;
   const int key_begin = chunk * a.sys_chunk_len;
@@ -90,20 +98,23 @@ __device__ __forceinline__ void sys_unit(const UnitArgs& a, int u, float* lds) {
     return r;
   };
   if (key_end - key_begin < kPSplitBelow)
-    stream_pipelined<T, D, 1, WK, true>(kl, nsteps, qf, st, key_begin, key_end, last, a.scale_log2, addr);
+    stream_pipelined<T, D, SRT, WK, true>(kl, nsteps, qf, st, key_begin, key_end, last, a.scale_log2, addr);
   else
-    stream_pipelined<T, D, 1, WK, false>(kl, nsteps, qf, st, key_begin, key_end, last, a.scale_log2, addr);
-  merge_key_lanes<D, 1, WK>(st, kl, lds);
+    stream_pipelined<T, D, SRT, WK, false>(kl, nsteps, qf, st, key_begin, key_end, last, a.scale_log2, addr);
+  merge_key_lanes<D, SRT, WK>(st, kl, lds);
 
   if (kl == 0) {
-    float* orow = nullptr;
-    float* lrow = nullptr;
-    if (row < M) {
-      const size_t r = (size_t)chunk * a.total_q * a.num_q_heads + qrow;
-      orow = a.sys_o + r * D;
-      lrow = a.sys_lse + r;
+#pragma unroll
+    for (int r = 0; r < SRT; ++r) {
+      float* orow = nullptr;
+      float* lrow = nullptr;
+      if (qrow[r] != ~(size_t)0) {
+        const size_t rr = (size_t)chunk * a.total_q * a.num_q_heads + qrow[r];
+        orow = a.sys_o + rr * D;
+        lrow = a.sys_lse + rr;
+      }
+      store_row_tile(st[r], orow, lrow);
     }
-    store_row_tile(st[0], orow, lrow);
   }
 }
 
@@ -243,9 +254,16 @@ __device__ __forceinline__ void ctx_unit(const UnitArgs& a, int v, CtxMeta m, fl
   }
 }
 
+// Row tiles of the widest unit a kernel runs: its context row tiles, and with four key
+// lanes also the two-tile system units.
+template <int RT, int WK>
+constexpr int merge_row_tiles() {
+  return (WK == 4 && RT < 2) ? 2 : RT;
+}
+
 template <int D, int RT, int WK>
 constexpr size_t units_lds_bytes() {
-  return WK > 1 ? sizeof(float) * (size_t)(WK / 2) * kMergeSlot<D, RT> : 0;
+  return WK > 1 ? sizeof(float) * (size_t)(WK / 2) * kMergeSlot<D, merge_row_tiles<RT, WK>()> : 0;
 }
 
 // ---- scheduling ---------------------------------------------------------------------
@@ -281,7 +299,10 @@ __device__ __forceinline__ void run_units(const UnitArgs& a, float* lds) {
   CtxMeta m = meta_for<WHAT>(a, u, ns, total);
   while (u != kNoUnit) {
     const CtxMeta mn = meta_for<WHAT>(a, un, ns, total);
-    if ((WHAT & kUnitsSys) && u < ns) sys_unit<T, D, WK>(a, u, lds);
+    if ((WHAT & kUnitsSys) && u < ns) {
+      if (WK == 4 && a.sys_rt == 2) sys_unit<T, D, merge_row_tiles<1, WK>(), WK>(a, u, lds);
+      else sys_unit<T, D, 1, WK>(a, u, lds);
+    }
     else if (WHAT & kUnitsCtx) ctx_unit<T, D, RT, WK>(a, u - ns, m, lds);
     sbase += G;
     soff = (soff + 8) % G;

@@ -37,6 +37,9 @@ int env_int(const char* name, int dflt) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// (head, chunk) groups from which system units take two row tiles (M <= 32).
+constexpr long long kSysTwoTileGroups = 384;
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 int round_up32(long long x) { return (int)(((x + 31) / 32) * 32); }
 
@@ -47,7 +50,7 @@ struct Plan {
   int sys_mfma = 0;  // sys_mode 2: 1 = sys_attn_mfma (bf16, d = 128), 0 = sys_attn_tiled
   int causal = 0;    // the offline prefill's causal system attention (sys_attn_mfma only)
   SysConfig sc{};
-  int sys_chunks = 0, sys_chunk_len = 0, sys_row_blocks = 0, sys_wgs = 0, xcd_remap = 0;
+  int sys_chunks = 0, sys_chunk_len = 0, sys_row_blocks = 0, sys_wgs = 0, xcd_remap = 0, sys_rt = 1;
   int sys_steps_per_head = 0, sys_total_steps = 0, sys_parts = 0;  // sys_attn_mfma
   int ctx_rt = 1, ctx_split_len = 0, ctx_max_splits = 0, ctx_row_blocks = 0, ctx_wgs = 0;
   int fuse_wgs = 0, launches = 0;
@@ -98,8 +101,14 @@ void make_plan(const relay_dims* d, int32_t sys_len, Plan* p, bool causal = fals
       const int chunk = round_up32(clamp_int(env_int("RELAY_SYS_CHUNK", 512), 32, 1 << 20));
       p->sys_chunk_len = chunk;
       p->sys_chunks = ceil_div(sys_len, chunk);
-      p->sys_row_blocks = ceil_div(M, 16);
       const long long groups = (long long)d->num_kv_heads * p->sys_chunks;
+      // Both 16-row tiles of M <= 32 rows in one unit (the chunk is read once, not once
+      // per tile) when there are enough (head, chunk) groups to keep every workgroup
+      // busy with such units; with few groups the smaller one-tile units balance better.
+      // Measured crossover (Llama-30B shape, batch 32): 208 groups even, 416 and more
+      // faster, 128 slower.
+      p->sys_rt = (M > 16 && M <= 32 && groups >= kSysTwoTileGroups && env_int("RELAY_KEY_LANES", 4) == 4) ? 2 : 1;
+      p->sys_row_blocks = ceil_div(M, 16 * p->sys_rt);
       p->sys_wgs = (int)(8LL * p->sys_row_blocks * ((groups + 7) / 8));
     } else if (d->in_dtype == RELAY_BF16 && d->head_dim == 128) {
       p->sys_mode = 2;
@@ -230,6 +239,7 @@ int launch_units(const relay_dims* d, const Plan& p, int what, const void* q, co
     a.sys_chunk_len = p.sys_chunk_len;
     a.sys_chunks = p.sys_chunks;
     a.sys_row_tiles = p.sys_row_blocks;
+    a.sys_rt = p.sys_rt;
     a.n_sys_units = p.sys_wgs;
   }
   if (what & relay::kUnitsCtx) {

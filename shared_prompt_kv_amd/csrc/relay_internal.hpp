@@ -63,17 +63,18 @@ struct UnitArgs {
   int group;
   float scale_log2;
   // system units: n_sys_units = 8 * sys_row_tiles * ceil(H_kv * sys_chunks / 8), or 0
-  const void* sys_k;   // [H_kv, L_s, d]
+  const void* sys_k;   // [H_kv, ceil(L_s/16), d/G, 16, G] key tiles
   const void* sys_v;   // [H_kv, ceil(L_s/16), d, 16]
   float* sys_o;        // [sys_chunks, T_q, H_q, d]
   float* sys_lse;      // [sys_chunks, T_q, H_q]
   int sys_len;
   int sys_chunk_len;   // multiple of 32
   int sys_chunks;
-  int sys_row_tiles;   // ceil(T_q * g / 16)
+  int sys_row_tiles;   // row units: ceil(T_q * g / (16 * sys_rt))
+  int sys_rt;          // 16-row tiles per system unit: 1, or 2 (four key lanes only)
   int n_sys_units;
   // context units: n_ctx_units = 8 * ctx_row_blocks * ceil(max_splits * H_kv * B / 8), or 0
-  const void* ctx_k;   // [num_blocks, H_kv, 16, d]
+  const void* ctx_k;   // [num_blocks, H_kv, d/G, 16, G] key tiles
   const void* ctx_v;   // [num_blocks, H_kv, d, 16]
   const int32_t* block_tables;
   const int32_t* ctx_lens;

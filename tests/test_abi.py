@@ -133,8 +133,10 @@ def test_plan_for_each_config(lib, cfg, sweep):
         assert plan["sys_chunks"] * plan["sys_chunk_len"] >= spec.sys_len
         assert (plan["sys_chunks"] - 1) * plan["sys_chunk_len"] < spec.sys_len
         assert plan["sys_mode"] == 1 and plan["launches"] == 2
-        assert plan["sys_row_blocks"] == -(-M // 16)
         groups = spec.num_kv_heads * plan["sys_chunks"]
+        # units of two 16-row tiles when M <= 32 and there are >= 384 (head, chunk) groups
+        rt = 2 if 16 < M <= 32 and groups >= 384 else 1
+        assert plan["sys_row_blocks"] == -(-M // (16 * rt))
         assert plan["sys_wgs"] == 8 * plan["sys_row_blocks"] * (-(-groups // 8))
     else:         # matrix-core system kernel: (row block, run of 64-key steps) workgroups
         assert plan["sys_mode"] == 2 and plan["launches"] == 3

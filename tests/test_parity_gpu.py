@@ -76,6 +76,12 @@ SMALL = [
     W.config_spec(5).replace(name="c5-f32", dtype="f32", batch=3, sys_len=40, ctx_lo=17, ctx_hi=99),
     W.config_spec(5).replace(name="c5-g8", batch=3, num_q_heads=32, num_kv_heads=4, sys_len=64,
                              ctx_lo=20, ctx_hi=90),
+    # 17..32 stacked rows over >= 384 (head, chunk) groups: system units of two row tiles
+    # (the second one ragged), a ragged last chunk
+    W.config_spec(3, 0).replace(name="c3-two-tile", batch=24, num_q_heads=16, num_kv_heads=16,
+                                sys_len=12000, ctx_lo=40, ctx_hi=40),
+    W.config_spec(1).replace(name="c1-two-tile-f32", batch=20, num_q_heads=24, num_kv_heads=24,
+                             sys_len=8200, ctx_lo=1, ctx_hi=40),
 ]
 SMALL_IDS = [f"{s.name}-B{s.batch}-L{s.sys_len}-d{s.head_dim}" for s in SMALL]
 
