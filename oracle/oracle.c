@@ -43,7 +43,8 @@
  *   sys_v        [H_kv, ceil(L_s/16), d, 16]   (16-key tiles, dim-major)
  *   ctx_k        [num_blocks, H_kv, d/G, 16, G]   (chunk-major within a page)
  *                G = elements per 16-byte chunk (8 bf16, 4 fp32; d when smaller): a key tile holds
- *                chunk 0 of its 16 keys, then chunk 1, ...
+ *                chunk 0 of its 16 keys, then chunk 1, ...; inside a chunk the keys are in
+ *                slot order 0,1,2,3,8,9,10,11,4,5,6,7,12,13,14,15
  *   ctx_v        [num_blocks, H_kv, d, 16]     (dim-major within a page)
  *   block_tables [B, max_blocks]  context key j of request b lives in page
  *                block_tables[b][j/16], slot j%16
@@ -108,11 +109,13 @@ static int request_of(const oracle_problem* p, int t) {
 }
 
 /* Index of element c of key r (0..15) inside one 16-key tile of keys (g elements per
- * 16-byte chunk; the whole row when d is smaller). */
+ * 16-byte chunk; the whole row when d is smaller).  Inside a chunk the keys sit in
+ * slot order: the key order with keys 4..7 and 8..11 exchanged. */
 static size_t key_in_tile(int r, int c, int dtype, int d) {
   int g = dtype == ORACLE_BF16 ? 8 : 4;
   if (g > d) g = d;
-  return ((size_t)(c / g) * ORACLE_BLOCK + r) * g + c % g;
+  int slot = (r >= 4 && r < 8) ? r + 4 : (r >= 8 && r < 12) ? r - 4 : r;
+  return ((size_t)(c / g) * ORACLE_BLOCK + slot) * g + c % g;
 }
 
 /* Element c of key j of the concatenated sequence for (request b, kv head hk). */

@@ -82,7 +82,8 @@ __device__ __forceinline__ void sys_unit(const UnitArgs& a, int u, float* lds) {
   const char* vbase = static_cast<const char*>(a.sys_v) + (size_t)h * ntile * D * kTile * E;
 
   // step s covers system tiles key_begin/16 + 2s and + 2s + 1; a page past the end of
-  // the keys re-reads the first (its keys are masked), K rows past the end are clamped
+  // the keys re-reads the first, and keys past the end (the tail tile's padding slots,
+  // in bounds) are masked
   const int npages = (key_end - key_begin + kTile - 1) / kTile;
   const int nsteps = (npages + 1) / 2;
   auto addr = [&](int st_) {
@@ -91,8 +92,6 @@ __device__ __forceinline__ void sys_unit(const UnitArgs& a, int u, float* lds) {
     StepAddr r;
     r.ka = kbase + (size_t)(ka / kTile) * kTile * D * E;
     r.kb = kbase + (size_t)(kb / kTile) * kTile * D * E;
-    r.ra = min(r16, Ls - 1 - ka);
-    r.rb = min(r16, Ls - 1 - kb);
     r.va = vbase + (size_t)(ka / kTile) * D * kTile * E;
     r.vb = vbase + (size_t)(kb / kTile) * D * kTile * E;
     return r;
@@ -227,7 +226,6 @@ __device__ __forceinline__ void ctx_unit(const UnitArgs& a, int v, CtxMeta m, fl
     r.kb = kbase + (size_t)bb * page_stride;
     r.va = vbase + (size_t)ba * page_stride;
     r.vb = vbase + (size_t)bb * page_stride;
-    r.ra = r.rb = r16;
     return r;
   };
   // the unit's first row sees the fewest of its keys (causal bound c - n_b + t): P is

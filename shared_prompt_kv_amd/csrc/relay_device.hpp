@@ -322,41 +322,30 @@ __device__ inline void store_row_tile(const RowState<D>& st, float* o_row, float
   if (q == 0) *lse_row = empty ? neg_inf() : (st.m + __builtin_amdgcn_logf(l)) * kLn2;
 }
 
-// ---- one 16-key step of the streaming units ------------------------------------------
+// ---- key tiles ------------------------------------------------------------------------
 //
-// Value fragments of one 16-key page for the two-page steps below: V^T for the 4 keys
-// 4q..4q+3 of lane group q, contiguous in the page's dimension-major tile.
-// V^T[dim][4q..4q+3] of one block.
-template <typename T> struct VFrag4;
-template <> struct VFrag4<bf16_t> {
-  u32x2 c;  // 4 bf16
-};
-template <> struct VFrag4<float> {
-  u32x4 c;  // 4 fp32
-};
+// A 16-key tile of keys is stored chunk-major, 16-byte chunk c of all its keys before
+// chunk c + 1, and inside a chunk the keys are in slot order: slot s holds key
+// key_slot(s), the key order with the middle two groups of four swapped (slots 0..7
+// hold keys 0..3 and 8..11, slots 8..15 keys 4..7 and 12..15).  key_slot is its own
+// inverse, so it also maps a key to its slot.
 
-__device__ inline void load_v4(VFrag4<bf16_t>& f, const char* p) { f.c = *reinterpret_cast<const u32x2*>(p); }
-__device__ inline void load_v4(VFrag4<float>& f, const char* p) { f.c = ld16(p); }
+__device__ inline int key_slot(int r) { return (r & ~12) | ((r >> 1) & 4) | ((r << 1) & 8); }
 
-// Zeroes the value elements of keys that do not exist (the first n of the four exist).
-__device__ inline void mask_v4(VFrag4<bf16_t>& f, int n) {
-  f.c.x = keep_bf16_pair(f.c.x, 0, n);
-  f.c.y = keep_bf16_pair(f.c.y, 2, n);
-}
-__device__ inline void mask_v4(VFrag4<float>& f, int n) {
-  f.c.x = 0 < n ? f.c.x : 0u;
-  f.c.y = 1 < n ? f.c.y : 0u;
-  f.c.z = 2 < n ? f.c.z : 0u;
-  f.c.w = 3 < n ? f.c.w : 0u;
-}
+// Byte offset of chunk c of the key in slot s of a key tile.
+__device__ inline int key_chunk_offset(int s, int c) { return (c * kTile + s) * 16; }
 
 // ---- two-page steps (32 keys) ----------------------------------------------------------
 //
-// A step covers pages a (keys k0..k0+15) and b (k0+16..k0+31).  Lane group q holds
-// the scores of keys 4q..4q+3 of each page (the score accumulator layout), i.e. 8
-// keys per lane: the k slots 8q..8q+7 of one v_mfma_f32_16x16x32_bf16 for P.V are
-// {a: 4q..4q+3, b: 4q..4q+3}, and V^T supplies the same keys, 8 bytes from each
-// page's dimension-major tile.  One softmax update serves 32 keys.
+// A step covers pages a (keys k0..k0+15) and b (k0+16..k0+31).  Its two 16x16 score
+// tiles take their 16 A-operand rows from slots 0..7 (tile A) and 8..15 (tile B) of
+// both pages: row m of tile A is slot m % 8 of page a (m < 8) or b.  The score
+// accumulators then give lane group q (lanes 16q..16q+15) the keys 8q..8q+3 of the
+// step in tile A and 8q+4..8q+7 in tile B: 8 consecutive keys of one page, the k slots
+// 8q..8q+7 of the P.V product, whose V^T is one 16-byte (bf16) read of the page's
+// dimension-major tile.  A lane's loads for one chunk of tile A are the 8 slots of one
+// page: 128 contiguous bytes, so every load reads whole cache lines.  One softmax
+// update serves 32 keys.
 //
 // K and V are issued separately so a step can be pipelined with a single set of
 // registers: once the score products have read K, the next step's K loads go out;
@@ -365,11 +354,11 @@ __device__ inline void mask_v4(VFrag4<float>& f, int n) {
 template <typename T, int D>
 struct StepK {
   static constexpr int NCH = D * Elem<T>::kBytes / 64;
-  u32x4 a[NCH], b[NCH];  // this lane's K rows of pages a and b
+  u32x4 a[NCH], b[NCH];  // this lane's K chunks of score tiles A and B
 };
 template <typename T, int D>
 struct StepV {
-  VFrag4<T> a[D / 16], b[D / 16];  // V^T fragments of pages a and b
+  VFrag<T> v[D / 16];  // V^T of this lane group's 8 keys, per 16-dimension tile
 };
 
 // P of one row tile for a step: bf16 hi (+ residual lo) in the k-slot order above,
@@ -402,59 +391,48 @@ __device__ __forceinline__ void make_pstep(PStep<float>& f, const float (&p)[8])
 }
 
 template <bool SPLIT>
-__device__ __forceinline__ void mfma_pstep(f32x4& acc, const VFrag4<bf16_t>& va, const VFrag4<bf16_t>& vb,
-                                           const PStep<bf16_t>& p) {
-  const u32x4 v = {va.c.x, va.c.y, vb.c.x, vb.c.y};
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), __builtin_bit_cast(bf16x8, p.c),
+__device__ __forceinline__ void mfma_pstep(f32x4& acc, const VFrag<bf16_t>& v, const PStep<bf16_t>& p) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v.c), __builtin_bit_cast(bf16x8, p.c),
                                                 acc, 0, 0, 0);
   if constexpr (SPLIT)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), __builtin_bit_cast(bf16x8, p.lo),
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v.c), __builtin_bit_cast(bf16x8, p.lo),
                                                   acc, 0, 0, 0);
 }
 template <bool SPLIT>
-__device__ __forceinline__ void mfma_pstep(f32x4& acc, const VFrag4<float>& va, const VFrag4<float>& vb,
-                                           const PStep<float>& p) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(va.c.x), p.p[0], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(va.c.y), p.p[1], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(va.c.z), p.p[2], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(va.c.w), p.p[3], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb.c.x), p.p[4], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb.c.y), p.p[5], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb.c.z), p.p[6], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb.c.w), p.p[7], acc, 0, 0, 0);
+__device__ __forceinline__ void mfma_pstep(f32x4& acc, const VFrag<float>& v, const PStep<float>& p) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c0.x), p.p[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c0.y), p.p[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c0.z), p.p[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c0.w), p.p[3], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c1.x), p.p[4], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c1.y), p.p[5], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c1.z), p.p[6], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.c1.w), p.p[7], acc, 0, 0, 0);
 }
 
-// Byte offset of 16-byte chunk c of key r inside a 16-key tile of keys.  Key tiles
-// are stored chunk-major: chunk 0 of the tile's 16 keys, then chunk 1, ...  The chunk a
-// lane needs for k slot group q4 of product kk is c = 4 kk + q4 (head dims 32 kk + 8 q4
-// .. + 7 for bf16), so for a whole tile the 64 lanes of one load read 1 KB contiguous.
-__device__ inline int key_chunk_offset(int r, int c) { return (c * kTile + r) * 16; }
-
-// Issues the K loads of a step: kpa/kpb are the two key tiles (pages), krow_a/krow_b
-// the key this lane reads (clamped where a tile is short).
+// Issues the K loads of a step: kpa/kpb are the two pages' key tiles (page b may
+// repeat page a past the end of the keys; its scores are masked).  Lane (r16, q) of
+// product kk reads chunk 4 kk + q of slot r16 % 8 (tile A) and 8 + r16 % 8 (tile B).
 template <typename T, int D>
-__device__ __forceinline__ void issue_k(StepK<T, D>& f, const char* kpa, const char* kpb, int krow_a, int krow_b) {
-  const int q4 = lane_id() >> 4;
-  const char* ra = kpa + key_chunk_offset(krow_a, q4);
-  const char* rb = kpb + key_chunk_offset(krow_b, q4);
+__device__ __forceinline__ void issue_k(StepK<T, D>& f, const char* kpa, const char* kpb) {
+  const int q4 = lane_id() >> 4, r16 = lane_id() & 15;
+  const char* base = (r16 < 8 ? kpa : kpb) + key_chunk_offset(r16 & 7, q4);
 #pragma unroll
   for (int kk = 0; kk < StepK<T, D>::NCH; ++kk) {
-    f.a[kk] = ld16(ra + 4 * kTile * 16 * kk);
-    f.b[kk] = ld16(rb + 4 * kTile * 16 * kk);
+    f.a[kk] = ld16(base + 4 * kTile * 16 * kk);
+    f.b[kk] = ld16(base + 4 * kTile * 16 * kk + 8 * 16);
   }
 }
 
-// Issues the V loads of a step from the two pages' dimension-major tiles.
+// Issues the V loads of a step: lane group q reads keys 8 (q % 2) .. + 7 of page a
+// (q < 2) or b, dimension 16 t + r16, from the page's dimension-major tile.
 template <typename T, int D>
 __device__ __forceinline__ void issue_v(StepV<T, D>& f, const char* vpa, const char* vpb) {
   constexpr int E = Elem<T>::kBytes;
   const int q4 = lane_id() >> 4, r16 = lane_id() & 15;
-  const int off = r16 * kTile * E + 4 * q4 * E;
+  const char* base = (q4 < 2 ? vpa : vpb) + r16 * kTile * E + 8 * (q4 & 1) * E;
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    load_v4(f.a[t], vpa + off + 16 * t * kTile * E);
-    load_v4(f.b[t], vpb + off + 16 * t * kTile * E);
-  }
+  for (int t = 0; t < D / 16; ++t) load_v(f.v[t], base + 16 * t * kTile * E);
 }
 
 // Rows whose running maximum grew by more than this (log2 units) rescale their
@@ -489,8 +467,9 @@ __device__ __forceinline__ void softmax_lazy(RowState<D>& st, float (&s)[N]) {
 }
 
 // Scores of a step for every row tile, folded into the row states; P out.  keyq: key
-// index of this lane group's first key of page a (page b: keyq + 16); keys at or past
-// kv_len do not exist; last[rt]: the last key the rows of tile rt may see.
+// index of this lane group's first key (tile A holds keyq .. keyq + 3, tile B
+// keyq + 4 .. keyq + 7); keys at or past kv_len do not exist; last[rt]: the last key the
+// rows of tile rt may see.
 template <typename T, int D, int RT, bool PSPLIT>
 __device__ __forceinline__ void step_scores(const StepK<T, D>& k, const u32x4 (&qf)[RT][StepK<T, D>::NCH],
                                             RowState<D> (&st)[RT], int keyq, int kv_len, const int (&last)[RT],
@@ -508,7 +487,7 @@ __device__ __forceinline__ void step_scores(const StepK<T, D>& k, const u32x4 (&
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sc[i] = (keyq + i <= lim) ? sa[i] * scale_log2 : neg_inf();
-      sc[4 + i] = (keyq + 16 + i <= lim) ? sb[i] * scale_log2 : neg_inf();
+      sc[4 + i] = (keyq + 4 + i <= lim) ? sb[i] * scale_log2 : neg_inf();
     }
     softmax_lazy(st[rt], sc);
     make_pstep<PSPLIT>(p[rt], sc);
@@ -520,18 +499,14 @@ __device__ __forceinline__ void step_scores(const StepK<T, D>& k, const u32x4 (&
 template <typename T, int D, int RT, bool PSPLIT>
 __device__ __forceinline__ void step_pv(StepV<T, D>& v, int keyq, int kv_len, RowState<D> (&st)[RT],
                                         const PStep<T> (&p)[RT]) {
-  if (keyq + 4 > kv_len) {
+  if (keyq + 8 > kv_len) {
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) mask_v4(v.a[t], kv_len - keyq);
-  }
-  if (keyq + 20 > kv_len) {
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) mask_v4(v.b[t], kv_len - keyq - 16);
+    for (int t = 0; t < D / 16; ++t) mask_v(v.v[t], kv_len - keyq);
   }
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) mfma_pstep<PSPLIT>(st[rt].o[t], v.a[t], v.b[t], p[rt]);
+    for (int t = 0; t < D / 16; ++t) mfma_pstep<PSPLIT>(st[rt].o[t], v.v[t], p[rt]);
   }
 }
 
@@ -543,13 +518,12 @@ constexpr int stream_depth() {
   return (Elem<T>::kBytes == 2 && RT == 1) ? 2 : 1;
 }
 
-// Page addresses of one step: K row bases and rows for pages a and b, V tile bases.
+// Page addresses of one step: the K and V tiles of pages a and b.
 struct StepAddr {
   const char* ka;
   const char* kb;
   const char* va;
   const char* vb;
-  int ra, rb;
 };
 
 // Streams steps kl, kl + WK, ... < nsteps: K(s) -> scores -> issue K(next) ->
@@ -562,11 +536,11 @@ __device__ __forceinline__ void stream_pipelined(int kl, int nsteps, const u32x4
   const int q4 = lane_id() >> 4;
   auto issue = [&](StepK<T, D>& k, StepV<T, D>& v, int s) {
     const StepAddr ad = addr(s);
-    issue_k(k, ad.ka, ad.kb, ad.ra, ad.rb);
+    issue_k(k, ad.ka, ad.kb);
     issue_v(v, ad.va, ad.vb);
   };
   auto run = [&](StepK<T, D>& k, StepV<T, D>& v, int s) {
-    const int keyq = key0 + 32 * s + 4 * q4;
+    const int keyq = key0 + 32 * s + 8 * q4;
     PStep<T> p[RT];
     step_scores<T, D, RT, PSPLIT>(k, qf, st, keyq, kv_len, last, scale_log2, p);
     step_pv<T, D, RT, PSPLIT>(v, keyq, kv_len, st, p);
@@ -592,13 +566,13 @@ __device__ __forceinline__ void stream_pipelined(int kl, int nsteps, const u32x4
     issue(k, v, kl);
     for (int s = kl; s < nsteps; s += WK) {
       const int sn = s + WK;
-      const int keyq = key0 + 32 * s + 4 * q4;
+      const int keyq = key0 + 32 * s + 8 * q4;
       PStep<T> p[RT];
       step_scores<T, D, RT, PSPLIT>(k, qf, st, keyq, kv_len, last, scale_log2, p);
       StepAddr ad;
       if (sn < nsteps) {
         ad = addr(sn);
-        issue_k(k, ad.ka, ad.kb, ad.ra, ad.rb);
+        issue_k(k, ad.ka, ad.kb);
       }
       step_pv<T, D, RT, PSPLIT>(v, keyq, kv_len, st, p);
       if (sn < nsteps) issue_v(v, ad.va, ad.vb);

@@ -21,10 +21,11 @@
 namespace relay {
 
 // Element index of head dimension c of key r (0..15) inside a 16-key tile of keys:
-// tiles are chunk-major, 16-byte chunks of 8 bf16 / 4 fp32 elements.
+// tiles are chunk-major (16-byte chunks of 8 bf16 / 4 fp32 elements), keys in slot
+// order (key_slot).
 __device__ __forceinline__ size_t key_tile_elem(int r, int c, int bf16) {
   const int g = bf16 ? 8 : 4;
-  return ((size_t)(c / g) * kTile + r) * g + c % g;
+  return ((size_t)(c / g) * kTile + key_slot(r)) * g + c % g;
 }
 
 __device__ __forceinline__ float rope_load(const void* p, size_t i, int bf16) {

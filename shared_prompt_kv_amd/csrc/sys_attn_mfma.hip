@@ -65,10 +65,11 @@ __device__ __forceinline__ int mf_key_of_row(int row) {
 }
 
 // Offset of 16-byte chunk c of the key held by LDS row `row` (0..63) of a step, from
-// the step's first key tile: key tiles are 16 keys x 256 bytes, chunk-major.
+// the step's first key tile: key tiles are 16 keys x 256 bytes, chunk-major, and the
+// key of LDS row r sits in slot r % 16 of its tile (mf_key_of_row and the tiles' slot
+// order are the same swap).
 __device__ __forceinline__ uint32_t mf_key_offset(int row, int c) {
-  const int k = mf_key_of_row(row);
-  return (uint32_t)((k >> 4) * (kTile * mf::D * 2) + key_chunk_offset(k & 15, c));
+  return (uint32_t)((row >> 4) * (kTile * mf::D * 2) + key_chunk_offset(row & 15, c));
 }
 
 // Issues the loads of the step whose first key is key0 straight into an LDS buffer:
@@ -86,7 +87,7 @@ __device__ __forceinline__ void mf_issue(char* buf, const char* kbase, const cha
     const int p = base + lane;
     const int row = p & 63, c = p >> 6;
     const int key = min(key0 + mf_key_of_row(row), Ls - 1);
-    const char* src = kbase + (size_t)(key / kTile) * (kTile * mf::D * 2) + key_chunk_offset(key % kTile, c);
+    const char* src = kbase + (size_t)(key / kTile) * (kTile * mf::D * 2) + key_chunk_offset(key_slot(key % kTile), c);
     __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(buf + base * 16), 16, 0, 0);
   }
 #pragma unroll

@@ -87,8 +87,8 @@ __global__ __launch_bounds__(kWave* WK* WR) void sys_attn_tiled_kernel(SysArgs a
     u32x4 kfa[NCH], kfb[NCH];
 #pragma unroll
     for (int kk = 0; kk < NCH; ++kk) {
-      kfa[kk] = ld16(kbase + (size_t)(ka / kTile) * kTile * D * E + key_chunk_offset(ka % kTile, 4 * kk + q4));
-      kfb[kk] = ld16(kbase + (size_t)(kb / kTile) * kTile * D * E + key_chunk_offset(kb % kTile, 4 * kk + q4));
+      kfa[kk] = ld16(kbase + (size_t)(ka / kTile) * kTile * D * E + key_chunk_offset(key_slot(ka % kTile), 4 * kk + q4));
+      kfb[kk] = ld16(kbase + (size_t)(kb / kTile) * kTile * D * E + key_chunk_offset(key_slot(kb % kTile), 4 * kk + q4));
     }
     // V^T fragments: keys key0 + 8*q4 .. +7 of every 16-dim tile
     const int vkey = key0 + 8 * q4;

@@ -33,7 +33,8 @@ Recipe (all integer ranges inclusive):
   so are the padding keys of the tail tile of ``sys_k``.
 * Key layout: keys are stored in 16-key tiles, each tile as ``[d/G, 16, G]`` with G the
   elements of one 16-byte chunk (8 bf16, 4 fp32; d itself when d is smaller): chunk c
-  of every key of the tile, then chunk c + 1.  ``k_tiles`` / ``k_untile`` convert from / to ``[..., 16, d]``.
+  of every key of the tile, then chunk c + 1; inside a chunk the keys are in slot order
+  (``KEY_SLOTS``: keys 4..7 and 8..11 exchanged).  ``k_tiles`` / ``k_untile`` convert from / to ``[..., 16, d]``.
 """
 from __future__ import annotations
 
@@ -218,17 +219,23 @@ def k_chunk(dtype: str, d: int) -> int:
     return min(8 if dtype == BF16 else 4, d)
 
 
+# Slot order of the keys inside a key tile: slot s holds key KEY_SLOTS[s] (keys 4..7
+# and 8..11 exchanged; the permutation is its own inverse).
+KEY_SLOTS = np.array([0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15])
+
+
 def k_tiles(k: np.ndarray, dtype: str) -> np.ndarray:
-    """Key-major 16-key tiles ``[..., 16, d]`` -> the cache's key layout ``[..., d/G, 16, G]``."""
+    """Key-major 16-key tiles ``[..., 16, d]`` -> the cache's key layout ``[..., d/G, 16, G]``
+    (slot s of every chunk holds key ``KEY_SLOTS[s]``)."""
     *lead, t, d = k.shape
     G = k_chunk(dtype, d)
-    return np.ascontiguousarray(k.reshape(*lead, t, d // G, G).swapaxes(-3, -2))
+    return np.ascontiguousarray(k[..., KEY_SLOTS, :].reshape(*lead, t, d // G, G).swapaxes(-3, -2))
 
 
 def k_untile(k: np.ndarray) -> np.ndarray:
     """The cache's key layout ``[..., d/G, 16, G]`` -> key-major ``[..., 16, d]``."""
     *lead, c, t, g = k.shape
-    return np.ascontiguousarray(k.swapaxes(-3, -2).reshape(*lead, t, c * g))
+    return np.ascontiguousarray(k.swapaxes(-3, -2).reshape(*lead, t, c * g)[..., KEY_SLOTS, :])
 
 
 def sys_k_dense(sys_k: np.ndarray, sys_len: int) -> np.ndarray:

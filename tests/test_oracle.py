@@ -179,11 +179,11 @@ def _hand_workload(q, sys_kv, ctx_kv, scale_dim):
     w.q[0, 0, :] = q
     G = W.k_chunk(spec.dtype, d)
     for j, (k, v) in enumerate(sys_kv):
-        w.sys_k[0, j // 16, :, j % 16, :] = np.reshape(k, (d // G, G))
+        w.sys_k[0, j // 16, :, W.KEY_SLOTS[j % 16], :] = np.reshape(k, (d // G, G))
         w.sys_v[0, j // 16, :, j % 16] = v
     for j, (k, v) in enumerate(ctx_kv):
         blk = w.block_tables[0, j // 16]
-        w.ctx_k_pages[blk, 0, :, j % 16, :] = np.reshape(k, (d // G, G))
+        w.ctx_k_pages[blk, 0, :, W.KEY_SLOTS[j % 16], :] = np.reshape(k, (d // G, G))
         w.ctx_v_pages[blk, 0, :, j % 16] = v
     return w
 

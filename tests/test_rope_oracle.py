@@ -104,8 +104,8 @@ def test_prefill_oracle_against_brute_force(dtype):
     np.testing.assert_array_equal(back(W.sys_k_dense(sk, L)), kv.transpose(1, 0, 2))
     assert not back(W.k_untile(sk)).reshape(Hkv, -1, d)[:, L:].any()
     G = W.k_chunk(dtype, d)
-    for j, c in ((0, 0), (5, G - 1), (17, G), (36, d - 1)):   # key tiles by index arithmetic
-        assert back(sk[1, j // 16, c // G, j % 16, c % G]) == kv[j, 1, c]
+    for j, c, slot in ((0, 0, 0), (5, G - 1, 9), (17, G, 1), (25, 3, 5), (36, d - 1, 8)):   # key tiles by index arithmetic
+        assert back(sk[1, j // 16, c // G, slot, c % G]) == kv[j, 1, c]
     for t in (0, 1, 15, 16, 36):
         for h in range(Hq):
             s = kv[: t + 1, h // 2] @ qv[t, h] / np.sqrt(d)

@@ -61,8 +61,9 @@ def test_paging_structure_and_poison():
         for j in range(c):
             blk = w.block_tables[b, j // 16]
             np.testing.assert_array_equal(ck[blk, :, j % 16, :], w.ctx_k_dense[b][j])
-            for c in (0, G - 1, G, spec.head_dim - 1):   # key tiles: chunk-major, G per chunk
-                np.testing.assert_array_equal(w.ctx_k_pages[blk, :, c // G, j % 16, c % G], w.ctx_k_dense[b][j][:, c])
+            slot = (j % 16) ^ 12 if 4 <= j % 16 < 12 else j % 16   # keys 4..7 and 8..11 exchanged
+            for c in (0, G - 1, G, spec.head_dim - 1):   # key tiles: chunk-major, G per chunk, slot order
+                np.testing.assert_array_equal(w.ctx_k_pages[blk, :, c // G, slot, c % G], w.ctx_k_dense[b][j][:, c])
             np.testing.assert_array_equal(w.ctx_v_pages[blk, :, :, j % 16], w.ctx_v_dense[b][j])
         tail = w.block_tables[b, n - 1]
         assert np.all(np.isnan(vals_k[tail, :, c - (n - 1) * 16:, :]))
