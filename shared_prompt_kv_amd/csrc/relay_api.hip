@@ -107,7 +107,10 @@ void make_plan(const relay_dims* d, int32_t sys_len, Plan* p, bool causal = fals
       // busy with such units; with few groups the smaller one-tile units balance better.
       // Measured crossover (Llama-30B shape, batch 32): 208 groups even, 416 and more
       // faster, 128 slower.
-      p->sys_rt = (M > 16 && M <= 32 && groups >= kSysTwoTileGroups && env_int("RELAY_KEY_LANES", 4) == 4) ? 2 : 1;
+      p->sys_rt = (M > 16 && M <= 32 && groups >= kSysTwoTileGroups) ? 2 : 1;
+      const int forced_rt = env_int("RELAY_SYS_ROW_TILES", 0);  // tuning: 1 or 2 tiles per unit
+      if (forced_rt == 1 || forced_rt == 2) p->sys_rt = forced_rt;
+      if (env_int("RELAY_KEY_LANES", 4) != 4) p->sys_rt = 1;  // two-tile units need four key lanes
       p->sys_row_blocks = ceil_div(M, 16 * p->sys_rt);
       p->sys_wgs = (int)(8LL * p->sys_row_blocks * ((groups + 7) / 8));
     } else if (d->in_dtype == RELAY_BF16 && d->head_dim == 128) {

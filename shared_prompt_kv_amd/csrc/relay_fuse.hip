@@ -20,7 +20,13 @@
 
 namespace relay {
 
-template <int D, int THREADS>
+// SKIP_EMPTY: an output row is loaded only when its LSE is finite.  With many partial
+// slots per row (long contexts split many ways, many system runs) a good share of the
+// slots are empty and their outputs need not be read; the LSEs of a batch are then
+// awaited before its outputs are loaded (one more memory latency per batch, covered
+// by the other rows' waves when there are many rows).  With a few slots, all of them
+// live, the outputs are loaded together with the LSEs.
+template <int D, int THREADS, bool SKIP_EMPTY>
 __global__ __launch_bounds__(THREADS) void relay_fuse_kernel(FuseArgs a) {
   constexpr int LPR = D / 4;           // lanes per row
   constexpr int RPW = THREADS / LPR;   // rows per workgroup
@@ -52,7 +58,12 @@ __global__ __launch_bounds__(THREADS) void relay_fuse_kernel(FuseArgs a) {
     for (int j = 0; j < kB; ++j) {
       const int i = min(i0 + j, n - 1);
       l[j] = *lse_at(i) * kLog2e;
-      o[j] = *o_at(i);
+      if constexpr (!SKIP_EMPTY) o[j] = *o_at(i);
+    }
+    if constexpr (SKIP_EMPTY) {
+#pragma unroll
+      for (int j = 0; j < kB; ++j)
+        o[j] = (i0 + j < n && l[j] != neg_inf()) ? *o_at(i0 + j) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float bm = m;
 #pragma unroll
@@ -83,14 +94,21 @@ __global__ __launch_bounds__(THREADS) void relay_fuse_kernel(FuseArgs a) {
   if (a.lse_out && c4 == 0) a.lse_out[row] = (z > 0.f) ? (m + __builtin_amdgcn_logf(z)) * kLn2 : neg_inf();
 }
 
+template <int D, bool SKIP>
+static void launch_fuse_d(const FuseArgs& a, bool wide, int nwg, hipStream_t stream) {
+  if (wide) hipLaunchKernelGGL((relay_fuse_kernel<D, 256, SKIP>), dim3(nwg), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((relay_fuse_kernel<D, 64, SKIP>), dim3(nwg), dim3(64), 0, stream, a);
+}
+
 hipError_t launch_relay_fuse(const FuseArgs& a, int head_dim, int nwg, hipStream_t stream) {
   const bool wide = fuse_threads(head_dim, a.n_rows) == 256;
+  const bool skip = fuse_skips_empty(a.a_count + a.b_count);
   if (head_dim == 64) {
-    if (wide) hipLaunchKernelGGL((relay_fuse_kernel<64, 256>), dim3(nwg), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((relay_fuse_kernel<64, 64>), dim3(nwg), dim3(64), 0, stream, a);
+    if (skip) launch_fuse_d<64, true>(a, wide, nwg, stream);
+    else launch_fuse_d<64, false>(a, wide, nwg, stream);
   } else {
-    if (wide) hipLaunchKernelGGL((relay_fuse_kernel<128, 256>), dim3(nwg), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((relay_fuse_kernel<128, 64>), dim3(nwg), dim3(64), 0, stream, a);
+    if (skip) launch_fuse_d<128, true>(a, wide, nwg, stream);
+    else launch_fuse_d<128, false>(a, wide, nwg, stream);
   }
   return hipGetLastError();
 }

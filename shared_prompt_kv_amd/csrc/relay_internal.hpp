@@ -165,6 +165,8 @@ inline int fuse_threads(int head_dim, long long n_rows) {
   return n_rows >= 2LL * 256 * (256 / (head_dim / 4)) ? 256 : 64;
 }
 inline int fuse_rows_per_wg(int head_dim, long long n_rows) { return fuse_threads(head_dim, n_rows) / (head_dim / 4); }
+// More partial slots per row than one batch of loads: outputs of empty slots are skipped.
+inline bool fuse_skips_empty(int slots) { return slots > 8; }
 hipError_t launch_relay_fuse(const FuseArgs& a, int head_dim, int nwg, hipStream_t stream);
 
 
