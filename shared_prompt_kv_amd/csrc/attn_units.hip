@@ -310,23 +310,31 @@ __device__ __forceinline__ void run_units(const UnitArgs& a, float* lds) {
   }
 }
 
+// Waves per SIMD the unit kernels are built for: two for bf16 (one or two row tiles fit
+// 256 registers without spilling, and a second workgroup per CU keeps the memory
+// streams of two units in flight), one for fp32 with one step in registers.
+template <typename T, int RT>
+constexpr int units_waves_per_simd() {
+  return Elem<T>::kBytes == 2 ? 2 : stream_depth<T, RT>();
+}
+
 // The system-attention step alone (at most 64 stacked rows: row tiles as units).
 template <typename T, int D, int WK>
-__global__ __launch_bounds__(kWave* WK, (stream_depth<T, 1>())) void sys_attn_kernel(UnitArgs a) {
+__global__ __launch_bounds__(kWave* WK, (units_waves_per_simd<T, 1>())) void sys_attn_kernel(UnitArgs a) {
   extern __shared__ float lds[];
   run_units<T, D, 1, WK, kUnitsSys>(a, lds);
 }
 
 // The context-attention step alone.
 template <typename T, int D, int RT, int WK>
-__global__ __launch_bounds__(kWave* WK, (stream_depth<T, RT>())) void ctx_attn_kernel(UnitArgs a) {
+__global__ __launch_bounds__(kWave* WK, (units_waves_per_simd<T, RT>())) void ctx_attn_kernel(UnitArgs a) {
   extern __shared__ float lds[];
   run_units<T, D, RT, WK, kUnitsCtx>(a, lds);
 }
 
 // Both steps in one launch.
 template <typename T, int D, int RT, int WK>
-__global__ __launch_bounds__(kWave* WK, (stream_depth<T, RT>())) void sys_ctx_attn_kernel(UnitArgs a) {
+__global__ __launch_bounds__(kWave* WK, (units_waves_per_simd<T, RT>())) void sys_ctx_attn_kernel(UnitArgs a) {
   extern __shared__ float lds[];
   run_units<T, D, RT, WK, kUnitsBoth>(a, lds);
 }

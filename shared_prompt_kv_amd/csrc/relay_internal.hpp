@@ -10,7 +10,7 @@ namespace relay {
 // sys_attn_tiled (large M): one launch over (row block, chunk, KV head) workgroups.
 struct SysArgs {
   const void* q;        // [T_q, H_q, d]
-  const void* sys_k;    // [H_kv, L_s, d]
+  const void* sys_k;    // [H_kv, ceil(L_s/16), d/G, 16, G] key tiles
   const void* sys_v;    // [H_kv, ceil(L_s/16), d, 16]
   float* o_part;        // [n_chunks, T_q, H_q, d]
   float* lse_part;      // [n_chunks, T_q, H_q]
