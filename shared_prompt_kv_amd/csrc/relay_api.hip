@@ -165,7 +165,11 @@ void make_plan(const relay_dims* d, int32_t sys_len, Plan* p, bool causal = fals
   const int R = d->max_q_len * g;
   p->ctx_rt = relay::ctx_rt_for(R);
   p->ctx_row_blocks = ceil_div(R, 16 * p->ctx_rt);
-  const int split = env_int("RELAY_CTX_SPLIT", 512);
+  // Context split: 512 keys while every context fits one split; 768 for longer contexts,
+  // where 512 left many empty trailing splits (each a unit that only marks its rows
+  // empty) and 768 measured 3-6% faster on the context step (Llama-3-8B GQA shape,
+  // long-prompt multi-token shape).
+  const int split = env_int("RELAY_CTX_SPLIT", d->max_ctx_len > 512 ? 768 : 512);
   p->ctx_split_len = round_up32(clamp_int(split, 32, 1024));
   p->ctx_max_splits = ceil_div(d->max_ctx_len, p->ctx_split_len);
   const long long cgroups = (long long)p->ctx_max_splits * d->num_kv_heads * d->batch;
