@@ -150,8 +150,27 @@ def test_plan_for_each_config(lib, cfg, sweep):
         sph = steps // spec.num_kv_heads
         assert plan["sys_chunks"] == max(part_of(h * sph + sph - 1) - part_of(h * sph) + 1
                                          for h in range(spec.num_kv_heads))
-    assert plan["ctx_split_len"] <= 1024
+    # context split: 512 keys while every context fits one, else 768
+    assert plan["ctx_split_len"] == (768 if s["max_ctx"] > 512 else 512)
+    assert plan["ctx_max_splits"] == -(-s["max_ctx"] // plan["ctx_split_len"])
     assert 0 < plan["ctx_wgs"] < 2**31 and 0 < plan["sys_wgs"] < 2**31
+
+
+@pytest.mark.parametrize("env,rows", [({}, 2), ({"RELAY_SYS_ROW_TILES": "2"}, 1),
+                                      ({"RELAY_SYS_ROW_TILES": "2", "RELAY_KEY_LANES": "8"}, 2),
+                                      ({"RELAY_CTX_SPLIT": "256"}, 2)])
+def test_plan_tuning_knobs(lib, monkeypatch, env, rows):
+    """The environment knobs the plan reads: two-tile system units on request (never with
+    eight key lanes), and the context split."""
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    spec = W.config_spec(2, 0)
+    s = W.expected_sizes(spec)
+    d = R.relay_dims(spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, 16,
+                     -(-s["max_ctx"] // 16), 1000, s["total_q"], 1, s["max_ctx"], spec.scale, 1, 0)
+    plan = R.relay_get_plan(d, spec.sys_len)
+    assert plan["sys_row_blocks"] == rows          # M = 32 rows: two one-tile units or one two-tile unit
+    assert plan["ctx_split_len"] == int(env.get("RELAY_CTX_SPLIT", 512))
 
 
 def test_validate_accepts_generated_workloads_and_rejects_bad_data(lib):
