@@ -383,6 +383,7 @@ static int decode_impl(const relay_dims* dims, const void* q, const void* sys_k,
   f.a_o = reinterpret_cast<const float*>(ws + p.off_sys_o);
   f.a_lse = reinterpret_cast<const float*>(ws + p.off_sys_lse);
   f.a_count = p.sys_chunks;
+  f.a_sparse = p.sys_mode == 2;
   f.b_o = reinterpret_cast<const float*>(ws + p.off_ctx_o);
   f.b_lse = reinterpret_cast<const float*>(ws + p.off_ctx_lse);
   f.b_count = p.ctx_max_splits;
@@ -438,6 +439,7 @@ int relay_sys_attn(const relay_dims* dims, const void* q, const void* sys_k, con
   f.a_o = reinterpret_cast<const float*>(ws + p.off_sys_o);
   f.a_lse = reinterpret_cast<const float*>(ws + p.off_sys_lse);
   f.a_count = p.sys_chunks;
+  f.a_sparse = p.sys_mode == 2;
   f.out = o_sys;
   f.lse_out = lse_sys;
   f.n_rows = (long long)dims->total_q * dims->num_q_heads;
@@ -475,6 +477,7 @@ int relay_prefill_attn(const relay_dims* dims, const void* q, const void* sys_k,
   f.a_o = reinterpret_cast<const float*>(ws + p.off_sys_o);
   f.a_lse = reinterpret_cast<const float*>(ws + p.off_sys_lse);
   f.a_count = p.sys_chunks;
+  f.a_sparse = 1;  // causal runs past a row block's tokens are empty
   f.out = out;
   f.out_bf16 = out_dtype == RELAY_BF16;
   f.lse_out = lse_out;

@@ -20,9 +20,9 @@
 
 namespace relay {
 
-// SKIP_EMPTY: an output row is loaded only when its LSE is finite.  With many partial
-// slots per row (long contexts split many ways, many system runs) a good share of the
-// slots are empty and their outputs need not be read; the LSEs of a batch are then
+// SKIP_EMPTY: an output row is loaded only when its LSE is finite.  With many slots that
+// may be empty (long contexts split many ways, system runs of the matrix-core kernel)
+// a good share of them are, and their outputs need not be read; the LSEs of a batch are then
 // awaited before its outputs are loaded (one more memory latency per batch, covered
 // by the other rows' waves when there are many rows).  With a few slots, all of them
 // live, the outputs are loaded together with the LSEs.
@@ -102,7 +102,7 @@ static void launch_fuse_d(const FuseArgs& a, bool wide, int nwg, hipStream_t str
 
 hipError_t launch_relay_fuse(const FuseArgs& a, int head_dim, int nwg, hipStream_t stream) {
   const bool wide = fuse_threads(head_dim, a.n_rows) == 256;
-  const bool skip = fuse_skips_empty(a.a_count + a.b_count);
+  const bool skip = fuse_skips_empty(a);
   if (head_dim == 64) {
     if (skip) launch_fuse_d<64, true>(a, wide, nwg, stream);
     else launch_fuse_d<64, false>(a, wide, nwg, stream);

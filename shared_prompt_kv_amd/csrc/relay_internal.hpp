@@ -112,6 +112,7 @@ struct FuseArgs {
   long long n_rows;
   int a_count;
   int b_count;
+  int a_sparse;    // group A slots may be empty (runs of the matrix-core system kernel)
   int out_bf16;
 };
 
@@ -165,8 +166,12 @@ inline int fuse_threads(int head_dim, long long n_rows) {
   return n_rows >= 2LL * 256 * (256 / (head_dim / 4)) ? 256 : 64;
 }
 inline int fuse_rows_per_wg(int head_dim, long long n_rows) { return fuse_threads(head_dim, n_rows) / (head_dim / 4); }
-// More partial slots per row than one batch of loads: outputs of empty slots are skipped.
-inline bool fuse_skips_empty(int slots) { return slots > 8; }
+// Rows with many slots that may be empty (every context split past the first; group A
+// slots when they are runs that need not touch a head): outputs of empty slots are
+// skipped.  Chunks of the streaming system units always hold keys for every row.
+inline bool fuse_skips_empty(const FuseArgs& a) {
+  return (a.a_sparse ? a.a_count : 0) + (a.b_count > 1 ? a.b_count - 1 : 0) > 4;
+}
 hipError_t launch_relay_fuse(const FuseArgs& a, int head_dim, int nwg, hipStream_t stream);
 
 
