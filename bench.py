@@ -309,6 +309,34 @@ def _time_graph(torch, calls, n_sets, steps, res):
     del full, part
 
 
+def measured_hbm(torch):
+    """What plain torch kernels reach on this GPU: a 1 GiB read (sum of a bf16 tensor)
+    and a 512 MiB device copy (read + write), GB/s.  Context for the roofline fraction
+    (the 8 TB/s peak is a spec figure); not part of the decode step."""
+    x = torch.ones(2**29, dtype=torch.bfloat16, device="cuda")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def rate(fn, nbytes, n=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(nbytes / (e0.elapsed_time(e1) / n * 1e-3) / 1e9, 1)
+
+    out = {"read_GBps": rate(lambda: x.sum(), x.numel() * 2),
+           "copy_GBps": rate(lambda: dst.copy_(src), 2 * COPY_BYTES),
+           "note": "torch sum over 1 GiB bf16 (read) and device copy of 512 MiB (read + write)"}
+    del x, src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -557,6 +585,8 @@ def main():
         line["no_relay_baseline"] = no_relay_baseline(torch, relay, w, args, ms)
         line["rope_append"] = rope_append_time(torch, relay, w, args)
         line["system_prefill"] = [prefill_time(torch, relay, workloads.config_spec(c, 0), args) for c in (2, 4)]
+    if not args.no_sweep:
+        line["hbm_measured"] = measured_hbm(torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
