@@ -81,7 +81,7 @@ def sys_scaling(torch, relay, steps):
     untimed calls then `steps` timed ones.  Prints one JSON line per case; under
     rocprofv3 the system kernel's dispatches come in the same order, 3 + steps per
     case."""
-    from shared_prompt_kv_amd import workloads
+    import workloads
     for name, cfg, batches in SYS_SCALING:
         for B in batches:
             spec = workloads.config_spec(cfg, 0).replace(batch=B)
@@ -161,11 +161,10 @@ def work_of(w):
     return {
         "step_bytes": kv_sys + kv_ctx + rows * d * (E + 4) + tables,
         "step_flops": 4 * Hq * d * (Tq * s.sys_len + vis),
-        "sys_attn": kv_sys + q_bytes + part_row,
-        "ctx_attn": kv_ctx + q_bytes + tables + part_row,
-        # both steps in one launch: every input once, both intermediate outputs
-        "sys_ctx_attn": kv_sys + kv_ctx + q_bytes + tables + 2 * part_row,
-        "relay_fuse": 2 * part_row + rows * d * 4,
+        "sys_attn": kv_sys + q_bytes,
+        # the streaming launch: context (and, at <= 64 stacked rows per KV head, system) K/V
+        "stream_attn": (kv_sys if w.total_q * s.group <= 64 else 0) + kv_ctx + q_bytes + tables,
+        "relay_merge": 2 * part_row + rows * d * 4,
         "sys_flops": 4 * Hq * d * Tq * s.sys_len,
         "ctx_flops": 4 * Hq * d * vis,
     }
@@ -258,14 +257,14 @@ def measure(torch, relay, w, steps, warmup, per_kernel=True, graph=True, prep=No
         # launch names: a separate (tiled) system launch, then the attention launch
         # (both steps together when sys_mode == 1), then relay_fuse
         mode = res["plan"]["sys_mode"]
-        names = ("sys_attn", "ctx_attn" if mode != 1 else "sys_ctx_attn", "relay_fuse")
+        names = ("sys_attn", "stream_attn", "relay_merge")
         acc = dict.fromkeys(names, 0.0)
         for i in range(steps):
             e = evs[4 * i:4 * i + 4]
             for j, k in enumerate(names):
                 acc[k] += he.elapsed_ms(e[j], e[j + 1])
         he.destroy(evs)
-        res["kernel_us"] = {k: 1000.0 * v / steps for k, v in acc.items() if mode == 2 or k != "sys_attn"}
+        res["kernel_us"] = {k: 1000.0 * v / steps for k, v in acc.items() if mode >= 2 or k != "sys_attn"}
     del calls, sets, outs, ws
     torch.cuda.empty_cache()
     return res
@@ -489,7 +488,7 @@ def prefill_time(torch, relay, spec, args):
 
 
 def workloads_generate(spec):
-    from shared_prompt_kv_amd import workloads
+    import workloads
     return workloads.generate(spec)
 
 
@@ -501,7 +500,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
-    from shared_prompt_kv_amd import relay, workloads
+    import workloads
+    from shared_prompt_kv_amd import relay
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:

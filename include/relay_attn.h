@@ -53,17 +53,19 @@
  *   q            [T_q, H_q, d]               tokens of request b are rows
  *                                            cu_q_lens[b] .. cu_q_lens[b+1]-1
  *   sys_k        [H_kv, ceil(L_s/16), d/G, 16, G]  system keys in 16-key tiles,
- *                                            chunk-major inside a tile (the tail
- *                                            tile's padding keys are ignored)
+ *                                            chunk-major, keys in slot order inside a
+ *                                            chunk (below; the tail tile's padding keys
+ *                                            are ignored)
  *   sys_v        [H_kv, ceil(L_s/16), d, 16] system values in 16-key tiles,
  *                                            dimension-major inside a tile (the
  *                                            tail tile's padding is ignored)
  *   ctx_k_pages  [num_blocks, H_kv, d/G, 16, G]  paged context keys, 16 tokens a
- *                                            page, chunk-major inside a page
+ *                                            page, chunk-major, keys in slot order
  *   ctx_v_pages  [num_blocks, H_kv, d, 16]   paged context values, dimension-major
  *                                            inside a page
- *   block_tables int32 [B, max_blocks_per_seq]  context token j of request b is in
- *                                            page block_tables[b][j/16], slot j%16;
+ *   block_tables int32 [B, max_blocks_per_seq]  context token j of request b is
+ *                                            key j%16 of page block_tables[b][j/16]
+ *                                            (its K stored in slot slot(j%16));
  *                                            entries past ceil(c_b/16) are unused
  *   ctx_lens     int32 [B]                   c_b
  *   cu_q_lens    int32 [B+1] prefix sums of n_b (cu_q_lens[0] = 0), or NULL when
@@ -75,9 +77,14 @@
  * Values are stored dimension-major (d before the 16 keys of a tile/page) so that
  * the keys a matrix-core lane reduces over are contiguous in memory.  Keys are stored
  * chunk-major: G = 16 / E elements (8 bf16, 4 fp32) make one 16-byte chunk, and a
- * tile/page holds chunk 0 of its 16 keys, then chunk 1, ...  Element c of key r of a
- * tile is at ((c / G) * 16 + r) * G + c % G.  The 64 lanes that load one matrix-core
- * operand of a 16-key tile then read 1 KB of contiguous memory.
+ * tile/page holds chunk 0 of its 16 keys, then chunk 1, ...  Inside a chunk the keys
+ * are in slot order: slot s holds key slot(s), where slot() exchanges keys 4..7 with
+ * keys 8..11 (slot(r) = 0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15 for
+ * r = 0..15; it is its own inverse).  Element c of key r of a tile is at
+ *     ((c / G) * 16 + slot(r)) * G + c % G.
+ * The 64 lanes that load one matrix-core operand of a 16-key tile then read 1 KB of
+ * contiguous memory, and slots 0..7 / 8..15 of a step's two pages are the score tiles
+ * whose lanes hold 8 consecutive keys of one page.
  */
 #ifndef RELAY_ATTN_H
 #define RELAY_ATTN_H
@@ -89,7 +96,8 @@
 extern "C" {
 #endif
 
-#define RELAY_ATTN_ABI_VERSION 2  /* 2: keys stored in chunk-major 16-key tiles */
+#define RELAY_ATTN_ABI_VERSION 3  /* 3: keys in slot order inside each 16-byte chunk of a tile; plan
+                                     fields of the streaming launch */
 
 /* element types */
 #define RELAY_F32 0  /* IEEE float32 */
@@ -120,20 +128,22 @@ typedef struct {
   int32_t out_dtype;          /* RELAY_F32 or RELAY_BF16: out of relay_attn_decode */
 } relay_dims;
 
-/* How a call is split into work units (for benchmarks and tests). */
+/* How a call is split into launches (for benchmarks and tests). */
 typedef struct {
-  int32_t sys_chunks;      /* system keys are processed in this many chunks */
-  int32_t sys_chunk_len;   /* keys per chunk (a multiple of 32) */
-  int32_t sys_row_blocks;  /* query-row blocks per KV head in the system step */
-  int32_t sys_wgs;         /* workgroups of one system-attention launch */
-  int32_t ctx_split_len;   /* context keys per split (a multiple of 32) */
-  int32_t ctx_max_splits;  /* ceil(max_ctx_len / ctx_split_len) */
-  int32_t ctx_row_blocks;  /* query-row blocks per (request, KV head) */
-  int32_t ctx_wgs;         /* context-attention work units (workgroups; some exit at once) */
-  int32_t fuse_wgs;        /* workgroups of one fusion launch */
-  int32_t sys_mode;        /* 0: no system step; 1: single-wave units, launched together with
-                              the context units; 2: tiled kernel (many stacked query rows) */
-  int32_t launches;        /* kernel launches of one relay_attn_decode call */
+  int32_t sys_mode;            /* 0: no system step; 1: system streams inside the streaming launch
+                                  (at most 64 stacked query rows per KV head); 2: the matrix-core
+                                  system kernel runs first (bf16, head_dim 128); 3: the tiled system
+                                  kernel runs first (fp32 or head_dim 64) */
+  int32_t sys_row_tiles;       /* sys_mode 1: 16-row tiles of one system stream */
+  int32_t sys_runs;            /* sys_mode 2, 3: partial slots per row written by the system kernel */
+  int32_t sys_wgs;             /* sys_mode 2, 3: workgroups of the system kernel */
+  int32_t ctx_row_tiles;       /* 16-row tiles of one context stream */
+  int32_t ctx_row_blocks;      /* context streams per (request, KV head) */
+  int32_t stream_waves;        /* waves of one streaming launch; each streams an equal share of the steps */
+  int32_t stream_launches;     /* streaming launches (requests in groups of stream_max_requests) */
+  int32_t stream_max_requests; /* requests per streaming launch */
+  int32_t merge_wgs;           /* workgroups of the merge launch */
+  int32_t launches;            /* kernel launches of one relay_attn_decode call */
 } relay_plan;
 
 /* ABI version compiled into the library (RELAY_ATTN_ABI_VERSION). */

@@ -28,7 +28,7 @@ import copy
 
 import numpy as np
 
-from shared_prompt_kv_amd import workloads as W  # the seeded generator only (no arithmetic)
+import workloads as W  # the seeded generator only (no arithmetic)
 
 ROPE_BASE = 10000.0
 

@@ -2,6 +2,7 @@
 // carving and the kernel launches.  Declarations and the contract of every entry
 // point are in include/relay_attn.h.
 #include <math.h>
+#include <atomic>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -12,6 +13,8 @@
 namespace {
 
 using relay::FuseArgs;
+using relay::MergeArgs;
+using relay::StreamArgs;
 using relay::SysArgs;
 using relay::SysConfig;
 
@@ -25,36 +28,56 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-constexpr int kNumCUs = 256;  // MI355X
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxDevices = 64;
+constexpr int kDefaultCUs = 256;  // MI355X, assumed when no device can be queried (planning on a host)
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  char* end = nullptr;
-  long x = strtol(v, &end, 10);
-  return (end && *end == 0 && x > 0 && x < (1L << 30)) ? (int)x : dflt;
+// Compute units of the current device, queried once per device (a process-wide cache).
+int device_cus() {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = kDefaultCUs;
+  }
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// (head, chunk) groups from which system units take two row tiles (M <= 32).
-constexpr long long kSysTwoTileGroups = 384;
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 int round_up32(long long x) { return (int)(((x + 31) / 32) * 32); }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// What a call computes.
+enum Need { kDecode, kSysOnly, kCtxOnly, kPrefill };
+
 struct Plan {
-  int sys_mode = 0;  // 0: no system step, 1: streaming units, 2: matrix-core kernel
-  int sys_mfma = 0;  // sys_mode 2: 1 = sys_attn_mfma (bf16, d = 128), 0 = sys_attn_tiled
+  int sys_mode = 0;  // 0: none, 1: system streams in the streaming launch, 2: sys_attn_mfma, 3: sys_attn_tiled
   int causal = 0;    // the offline prefill's causal system attention (sys_attn_mfma only)
+  // sys_mode 1
+  int rts = 0, sys_steps = 0;
+  // sys_mode 2 / 3
   SysConfig sc{};
-  int sys_chunks = 0, sys_chunk_len = 0, sys_row_blocks = 0, sys_wgs = 0, xcd_remap = 0, sys_rt = 1;
-  int sys_steps_per_head = 0, sys_total_steps = 0, sys_parts = 0;  // sys_attn_mfma
-  int ctx_rt = 1, ctx_split_len = 0, ctx_max_splits = 0, ctx_row_blocks = 0, ctx_wgs = 0;
-  int fuse_wgs = 0, launches = 0;
-  size_t off_sys_o = 0, off_sys_lse = 0, off_ctx_o = 0, off_ctx_lse = 0, ws_bytes = 0;
+  int sys_chunks = 0, sys_chunk_len = 0, sys_row_blocks = 0, sys_wgs = 0, xcd_remap = 0;
+  int sys_steps_per_head = 0, sys_total_steps = 0, sys_parts = 0;
+  // streaming launches
+  int rtc = 1, ctx_rb = 1, grid = 0, workers = 0, chunk_req = 0, n_chunks = 0;
+  long long sys_slots = 0, ctx_slots_per_chunk = 0, ctx_slots = 0;
+  int merge_wgs = 0, launches = 0;
+  size_t off_sys_o = 0, off_sys_lse = 0, off_sys_desc = 0, off_ctx_o = 0, off_ctx_lse = 0, off_rowdesc = 0;
+  size_t ws_bytes = 0;
 };
 
 int check_dims(const relay_dims* d, int32_t sys_len) {
@@ -82,112 +105,136 @@ int check_dims(const relay_dims* d, int32_t sys_len) {
   if (!(isfinite(d->scale))) return fail(RELAY_ERR_INVALID, "scale must be finite");
   if (sys_len < 0) return fail(RELAY_ERR_INVALID, "sys_len must be >= 0 (got %d)", sys_len);
   const long long rows = (long long)d->total_q * d->num_q_heads;
-  if (rows * d->head_dim > (1LL << 40) || (long long)sys_len * d->num_kv_heads > (1LL << 36) || (long long)d->total_q * (d->num_q_heads / d->num_kv_heads) > (1 << 30))
+  if (rows * d->head_dim > (1LL << 40) || (long long)sys_len * d->num_kv_heads > (1LL << 36) ||
+      (long long)d->total_q * (d->num_q_heads / d->num_kv_heads) > (1 << 30) ||
+      (long long)d->max_q_len * (d->num_q_heads / d->num_kv_heads) > (1 << 20))
     return fail(RELAY_ERR_INVALID, "problem too large");
   return RELAY_OK;
 }
 
 int clamp_int(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-void make_plan(const relay_dims* d, int32_t sys_len, Plan* p, bool causal = false) {
-  p->causal = causal ? 1 : 0;
+// The system kernel's plan (M > 64 stacked rows per KV head).
+void plan_system_kernel(const relay_dims* d, int32_t sys_len, int M, Plan* p) {
+  if (d->in_dtype == RELAY_BF16 && d->head_dim == 128) {
+    p->sys_mode = 2;
+    p->sys_row_blocks = ceil_div(M, relay::kSysMfmaRows);
+    // the 64-key steps of all heads, cut into `parts` equal runs so the row blocks
+    // times the parts fill the resident workgroup slots once
+    p->sys_steps_per_head = ceil_div(sys_len, relay::kSysMfmaStep);
+    const long long S = (long long)p->sys_steps_per_head * d->num_kv_heads;
+    p->sys_total_steps = (int)S;
+    long long parts = relay::kSysMfmaSlots / p->sys_row_blocks;
+    // causal: a row block's work grows with its tokens, so the runs are cut finer
+    // and the workgroups of early row blocks, which finish first, free their slots
+    if (p->causal) parts *= relay::kSysCausalRunsPerSlot;
+    if (parts < 1) parts = 1;
+    if (parts > S) parts = S;
+    p->sys_parts = (int)parts;
+    // slots: the most parts any one head is spread over
+    int slots = 1;
+    for (int h = 0; h < d->num_kv_heads; ++h) {
+      const long long x0 = (long long)h * p->sys_steps_per_head;
+      const long long x1 = x0 + p->sys_steps_per_head - 1;
+      const int n = relay::lean_part_of(x1, (int)S, (int)parts) - relay::lean_part_of(x0, (int)S, (int)parts) + 1;
+      if (n > slots) slots = n;
+    }
+    p->sys_chunks = slots;
+    p->sys_chunk_len = (int)(((S + parts - 1) / parts) * relay::kSysMfmaStep);  // keys per part
+    const long long wgs = (long long)p->sys_row_blocks * parts;
+    p->sys_wgs = (int)((wgs + 7) / 8 * 8);
+    p->xcd_remap = 1;
+  } else {
+    p->sys_mode = 3;
+    p->sc = relay::sys_config(M);
+    p->sys_row_blocks = ceil_div(M, p->sc.wr * p->sc.rt * 16);
+    const long long target = 2LL * device_cus();
+    const long long per = (long long)sys_len * d->num_kv_heads * p->sys_row_blocks / target;
+    int chunk = round_up32(per < 1 ? 1 : per);
+    if (chunk < 32 * p->sc.wk) chunk = 32 * p->sc.wk;
+    p->sys_chunk_len = chunk;
+    p->sys_chunks = ceil_div(sys_len, p->sys_chunk_len);
+    p->sys_wgs = p->sys_row_blocks * p->sys_chunks * d->num_kv_heads;
+    p->xcd_remap = (p->sys_row_blocks > 1 && p->sys_wgs % 8 == 0) ? 1 : 0;
+  }
+}
+
+// Fills *p for dims and sys_len (need: what the call computes).  Returns RELAY_OK or
+// an error for sizes one streaming launch cannot index.
+int make_plan(const relay_dims* d, int32_t sys_len, Plan* p, Need need = kDecode) {
+  p->causal = need == kPrefill ? 1 : 0;
   const int g = d->num_q_heads / d->num_kv_heads;
   const long long rows = (long long)d->total_q * d->num_q_heads;
-  // ---- system step
+  const int D = d->head_dim;
   const int M = d->total_q * g;
+  size_t off = 0;
+  if (need == kPrefill) {  // the causal system kernel and the merge of its runs
+    plan_system_kernel(d, sys_len, M, p);
+    p->off_sys_o = off;
+    off += align256((size_t)p->sys_chunks * rows * D * sizeof(float));
+    p->off_sys_lse = off;
+    off += align256((size_t)p->sys_chunks * rows * sizeof(float));
+    p->ws_bytes = off;
+    p->launches = 2;
+    return RELAY_OK;
+  }
+  const int cus = device_cus();
+  p->grid = cus;
+  p->workers = cus * relay::kStreamWaves;
+  // ---- system step
   if (sys_len > 0) {
-    if (M <= relay::kUnitMaxRows) {
+    if (M <= relay::kStreamSysMaxRows) {
       p->sys_mode = 1;
-      const int chunk = round_up32(clamp_int(env_int("RELAY_SYS_CHUNK", 512), 32, 1 << 20));
-      p->sys_chunk_len = chunk;
-      p->sys_chunks = ceil_div(sys_len, chunk);
-      const long long groups = (long long)d->num_kv_heads * p->sys_chunks;
-      // Both 16-row tiles of M <= 32 rows in one unit (the chunk is read once, not once
-      // per tile) when there are enough (head, chunk) groups to keep every workgroup
-      // busy with such units; with few groups the smaller one-tile units balance better.
-      // Measured crossover (Llama-30B shape, batch 32): 208 groups even, 416 and more
-      // faster, 128 slower.
-      p->sys_rt = (M > 16 && M <= 32 && groups >= kSysTwoTileGroups) ? 2 : 1;
-      const int forced_rt = env_int("RELAY_SYS_ROW_TILES", 0);  // tuning: 1 or 2 tiles per unit
-      if (forced_rt == 1 || forced_rt == 2) p->sys_rt = forced_rt;
-      if (env_int("RELAY_KEY_LANES", 4) != 4) p->sys_rt = 1;  // two-tile units need four key lanes
-      p->sys_row_blocks = ceil_div(M, 16 * p->sys_rt);
-      p->sys_wgs = (int)(8LL * p->sys_row_blocks * ((groups + 7) / 8));
-    } else if (d->in_dtype == RELAY_BF16 && d->head_dim == 128) {
-      p->sys_mode = 2;
-      p->sys_mfma = 1;
-      p->sys_row_blocks = ceil_div(M, relay::kSysMfmaRows);
-      // the 64-key steps of all heads, cut into `parts` equal runs so the row blocks
-      // times the parts fill the resident workgroup slots once
-      p->sys_steps_per_head = ceil_div(sys_len, relay::kSysMfmaStep);
-      const long long S = (long long)p->sys_steps_per_head * d->num_kv_heads;
-      p->sys_total_steps = (int)S;
-      long long parts = relay::kSysMfmaSlots / p->sys_row_blocks;
-      // causal: a row block's work grows with its tokens, so the runs are cut finer
-      // and the workgroups of early row blocks, which finish first, free their slots
-      if (causal) parts *= relay::kSysCausalRunsPerSlot;
-      const int forced = env_int("RELAY_SYS_PARTS", 0);
-      if (forced > 0) parts = forced;
-      if (parts < 1) parts = 1;
-      if (parts > S) parts = S;
-      p->sys_parts = (int)parts;
-      // slots: the most parts any one head is spread over
-      int slots = 1;
-      for (int h = 0; h < d->num_kv_heads; ++h) {
-        const long long x0 = (long long)h * p->sys_steps_per_head;
-        const long long x1 = x0 + p->sys_steps_per_head - 1;
-        const int n = relay::lean_part_of(x1, (int)S, (int)parts) - relay::lean_part_of(x0, (int)S, (int)parts) + 1;
-        if (n > slots) slots = n;
-      }
-      p->sys_chunks = slots;
-      p->sys_chunk_len = (int)(((S + parts - 1) / parts) * relay::kSysMfmaStep);  // keys per part
-      const long long wgs = (long long)p->sys_row_blocks * parts;
-      p->sys_wgs = (int)((wgs + 7) / 8 * 8);
-      p->xcd_remap = 1;
+      const int tiles = ceil_div(M, 16);
+      p->rts = tiles <= 2 ? tiles : 4;
+      p->sys_steps = ceil_div(sys_len, 32);
+      p->sys_slots = (long long)d->num_kv_heads + p->workers;
     } else {
-      p->sys_mode = 2;
-      p->sc = relay::sys_config(M);
-      p->sys_row_blocks = ceil_div(M, p->sc.wr * p->sc.rt * 16);
-      const int target = env_int("RELAY_SYS_TARGET_WGS", 2 * kNumCUs);
-      int chunk = env_int("RELAY_SYS_CHUNK", 0);
-      if (chunk <= 0) {
-        const long long per = (long long)sys_len * d->num_kv_heads * p->sys_row_blocks / target;
-        chunk = round_up32(per < 1 ? 1 : per);
-        if (chunk < 32 * p->sc.wk) chunk = 32 * p->sc.wk;
-      }
-      p->sys_chunk_len = round_up32(chunk);
-      p->sys_chunks = ceil_div(sys_len, p->sys_chunk_len);
-      p->sys_wgs = p->sys_row_blocks * p->sys_chunks * d->num_kv_heads;
-      p->xcd_remap = (p->sys_row_blocks > 1 && p->sys_wgs % 8 == 0) ? 1 : 0;
+      plan_system_kernel(d, sys_len, M, p);
     }
   }
-  // ---- context step
-  const int R = d->max_q_len * g;
-  p->ctx_rt = relay::ctx_rt_for(R);
-  p->ctx_row_blocks = ceil_div(R, 16 * p->ctx_rt);
-  // Context split: 512 keys while every context fits one split; 768 for longer contexts,
-  // where 512 left many empty trailing splits (each a unit that only marks its rows
-  // empty) and 768 measured 3-6% faster on the context step (Llama-3-8B GQA shape,
-  // long-prompt multi-token shape).
-  const int split = env_int("RELAY_CTX_SPLIT", d->max_ctx_len > 512 ? 768 : 512);
-  p->ctx_split_len = round_up32(clamp_int(split, 32, 1024));
-  p->ctx_max_splits = ceil_div(d->max_ctx_len, p->ctx_split_len);
-  const long long cgroups = (long long)p->ctx_max_splits * d->num_kv_heads * d->batch;
-  p->ctx_wgs = (int)(8LL * p->ctx_row_blocks * ((cgroups + 7) / 8));
-  // ---- fusion
-  p->fuse_wgs = ceil_div(rows, relay::fuse_rows_per_wg(d->head_dim, rows));
-  p->launches = (p->sys_mode == 2 ? 3 : 2);
-  // ---- workspace
-  size_t off = 0;
-  p->off_sys_o = off;
-  off += align256((size_t)p->sys_chunks * rows * d->head_dim * sizeof(float));
-  p->off_sys_lse = off;
-  off += align256((size_t)p->sys_chunks * rows * sizeof(float));
+  // ---- context streams: (request, KV head, row block), requests in groups of at most
+  // chunk_req per streaming launch so that a launch's step count fits 31 bits
+  const long long R = (long long)d->max_q_len * g;
+  p->rtc = relay::ctx_rt_for((int)R);
+  p->ctx_rb = ceil_div(R, 16 * p->rtc);
+  const int cap = d->max_ctx_len < d->max_blocks_per_seq * 16 ? d->max_ctx_len : d->max_blocks_per_seq * 16;
+  const long long per_req = (long long)ceil_div(cap, 32) * d->num_kv_heads * p->ctx_rb;
+  long long chunk = relay::kStreamMaxRequests;
+  if (chunk > d->batch) chunk = d->batch;
+  if (chunk * per_req > 0x7fffffffLL - 1) chunk = (0x7fffffffLL - 1) / per_req;
+  if (p->sys_mode == 1 && (long long)d->num_kv_heads * p->sys_steps + chunk * per_req > 0x7fffffffLL)
+    chunk = (0x7fffffffLL - (long long)d->num_kv_heads * p->sys_steps) / per_req;
+  if (chunk < 1) return fail(RELAY_ERR_UNSUPPORTED, "one request's context is too long for a streaming launch");
+  p->chunk_req = (int)chunk;
+  p->n_chunks = ceil_div(d->batch, chunk);
+  p->ctx_slots_per_chunk = chunk * d->num_kv_heads * p->ctx_rb + p->workers;
+  p->ctx_slots = p->ctx_slots_per_chunk * p->n_chunks;
+  // ---- merge
+  p->merge_wgs = ceil_div(rows, relay::merge_threads(D, rows) / (D / 4));
+  p->launches = (p->sys_mode >= 2 ? 1 : 0) + p->n_chunks + 1;
+  // ---- workspace (fp32 partials, 256-byte aligned regions)
+  if (p->sys_mode == 1) {
+    p->off_sys_o = off;
+    off += align256((size_t)p->sys_slots * 16 * p->rts * D * sizeof(float));
+    p->off_sys_lse = off;
+    off += align256((size_t)p->sys_slots * 16 * p->rts * sizeof(float));
+    p->off_sys_desc = off;
+    off += align256((size_t)d->num_kv_heads * 2 * sizeof(int));
+  } else if (p->sys_mode >= 2) {
+    p->off_sys_o = off;
+    off += align256((size_t)p->sys_chunks * rows * D * sizeof(float));
+    p->off_sys_lse = off;
+    off += align256((size_t)p->sys_chunks * rows * sizeof(float));
+  }
   p->off_ctx_o = off;
-  off += align256((size_t)p->ctx_max_splits * rows * d->head_dim * sizeof(float));
+  off += align256((size_t)p->ctx_slots * 16 * p->rtc * D * sizeof(float));
   p->off_ctx_lse = off;
-  off += align256((size_t)p->ctx_max_splits * rows * sizeof(float));
+  off += align256((size_t)p->ctx_slots * 16 * p->rtc * sizeof(float));
+  p->off_rowdesc = off;
+  off += align256((size_t)rows * 4 * sizeof(int));
   p->ws_bytes = off;
+  return RELAY_OK;
 }
 
 int grid_ok(long long n) { return n > 0 && n < (1LL << 31); }
@@ -196,8 +243,9 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(RELAY_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-int launch_sys_tiled(const relay_dims* d, const Plan& p, const void* q, const void* sys_k,
-                     const void* sys_v, int32_t sys_len, char* ws, hipStream_t s) {
+// The system kernel (sys_mode 2 or 3): one launch writing per-row run partials.
+int launch_sys_kernel(const relay_dims* d, const Plan& p, const void* q, const void* sys_k, const void* sys_v,
+                      int32_t sys_len, char* ws, hipStream_t s) {
   if (!grid_ok(p.sys_wgs)) return fail(RELAY_ERR_INVALID, "system grid too large");
   SysArgs a;
   a.q = q;
@@ -218,57 +266,97 @@ int launch_sys_tiled(const relay_dims* d, const Plan& p, const void* q, const vo
   a.total_steps = p.sys_total_steps;
   a.parts = p.sys_parts;
   a.causal = p.causal;
-  hipError_t e = p.sys_mfma ? relay::launch_sys_attn_mfma(a, p.sys_wgs, s)
-                            : relay::launch_sys_attn_tiled(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s);
+  hipError_t e = p.sys_mode == 2 ? relay::launch_sys_attn_mfma(a, p.sys_wgs, s)
+                                 : relay::launch_sys_attn_tiled(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s);
   return e == hipSuccess ? RELAY_OK : hip_fail(e, "system attention launch");
 }
 
-// Launches single-wave units: what = relay::kUnitsSys / kUnitsCtx / kUnitsBoth.
-int launch_units(const relay_dims* d, const Plan& p, int what, const void* q, const void* sys_k,
-                 const void* sys_v, int32_t sys_len, const void* ck, const void* cv, const int32_t* bt,
-                 const int32_t* cl, const int32_t* cu, char* ws, hipStream_t s) {
-  relay::UnitArgs a{};
+// The streaming launches: the system streams (sys_mode 1, with_sys) and the context
+// streams (with_ctx) of every request group.
+int launch_streams(const relay_dims* d, const Plan& p, bool with_sys, bool with_ctx, const void* q,
+                   const void* sys_k, const void* sys_v, int32_t sys_len, const void* ck, const void* cv,
+                   const int32_t* bt, const int32_t* cl, const int32_t* cu, char* ws, hipStream_t s) {
+  const bool sys = with_sys && p.sys_mode == 1;
+  if (!sys && !with_ctx) return RELAY_OK;
+  StreamArgs a{};
   a.q = q;
   a.total_q = d->total_q;
   a.num_q_heads = d->num_q_heads;
   a.num_kv_heads = d->num_kv_heads;
   a.group = d->num_q_heads / d->num_kv_heads;
   a.scale_log2 = d->scale * kLog2e;
-  a.key_lanes = env_int("RELAY_KEY_LANES", 4);
-  a.grid = env_int("RELAY_GRID", 0);
-
-  if (what & relay::kUnitsSys) {
+  a.M = d->total_q * a.group;
+  a.n_workers = p.workers;
+  if (sys) {
     a.sys_k = sys_k;
     a.sys_v = sys_v;
+    a.sys_len = sys_len;
+    a.sys_steps = p.sys_steps;
     a.sys_o = reinterpret_cast<float*>(ws + p.off_sys_o);
     a.sys_lse = reinterpret_cast<float*>(ws + p.off_sys_lse);
-    a.sys_len = sys_len;
-    a.sys_chunk_len = p.sys_chunk_len;
-    a.sys_chunks = p.sys_chunks;
-    a.sys_row_tiles = p.sys_row_blocks;
-    a.sys_rt = p.sys_rt;
-    a.n_sys_units = p.sys_wgs;
+    a.sys_desc = reinterpret_cast<int*>(ws + p.off_sys_desc);
   }
-  if (what & relay::kUnitsCtx) {
-    a.ctx_k = ck;
-    a.ctx_v = cv;
-    a.block_tables = bt;
-    a.ctx_lens = cl;
-    a.cu_q_lens = cu;
-    a.ctx_o = reinterpret_cast<float*>(ws + p.off_ctx_o);
-    a.ctx_lse = reinterpret_cast<float*>(ws + p.off_ctx_lse);
-    a.batch = d->batch;
-    a.num_blocks = d->num_blocks;
-    a.max_blocks_per_seq = d->max_blocks_per_seq;
-    a.max_ctx_len = d->max_ctx_len;
-    a.ctx_split_len = p.ctx_split_len;
-    a.ctx_max_splits = p.ctx_max_splits;
-    a.ctx_row_blocks = p.ctx_row_blocks;
-    a.n_ctx_units = p.ctx_wgs;
+  a.ctx_on = with_ctx ? 1 : 0;
+  a.ctx_k = ck;
+  a.ctx_v = cv;
+  a.block_tables = bt;
+  a.ctx_lens = cl;
+  a.cu_q_lens = cu;
+  a.batch = d->batch;
+  a.num_blocks = d->num_blocks;
+  a.max_blocks_per_seq = d->max_blocks_per_seq;
+  a.max_ctx_len = d->max_ctx_len;
+  a.ctx_rb = p.ctx_rb;
+  a.ctx_o = reinterpret_cast<float*>(ws + p.off_ctx_o);
+  a.ctx_lse = reinterpret_cast<float*>(ws + p.off_ctx_lse);
+  a.ctx_rowdesc = reinterpret_cast<int*>(ws + p.off_rowdesc);
+  const int launches = with_ctx ? p.n_chunks : 1;
+  for (int c = 0; c < launches; ++c) {
+    StreamArgs ac = a;
+    ac.b_begin = c * p.chunk_req;
+    ac.n_req = with_ctx ? (d->batch - ac.b_begin < p.chunk_req ? d->batch - ac.b_begin : p.chunk_req) : 0;
+    ac.slot_base = (long long)c * p.ctx_slots_per_chunk;
+    if (c > 0) ac.sys_steps = 0;  // the system streams go with the first request group
+    const int rts = ac.sys_steps > 0 ? p.rts : 0;
+    hipError_t e = relay::launch_stream_attn(ac, rts, p.rtc, d->in_dtype, d->head_dim, p.grid, s);
+    if (e != hipSuccess) return hip_fail(e, "streaming attention launch");
   }
-  if (!grid_ok((long long)a.n_sys_units + a.n_ctx_units)) return fail(RELAY_ERR_INVALID, "grid too large");
-  hipError_t e = relay::launch_attn_units(a, p.ctx_rt, what, d->in_dtype, d->head_dim, s);
-  return e == hipSuccess ? RELAY_OK : hip_fail(e, "attention units launch");
+  return RELAY_OK;
+}
+
+// The merge: every row's output (and LSE when lse_out is given) from its parts.
+int launch_merge(const relay_dims* d, const Plan& p, bool with_sys, bool with_ctx, char* ws, void* out, int out_bf16,
+                 float* lse_out, hipStream_t s) {
+  MergeArgs m{};
+  m.n_rows = (long long)d->total_q * d->num_q_heads;
+  m.num_q_heads = d->num_q_heads;
+  m.group = d->num_q_heads / d->num_kv_heads;
+  if (with_sys && p.sys_mode == 1) {
+    m.sys_src = 1;
+    m.sys_o = reinterpret_cast<const float*>(ws + p.off_sys_o);
+    m.sys_lse = reinterpret_cast<const float*>(ws + p.off_sys_lse);
+    m.sys_desc = reinterpret_cast<const int*>(ws + p.off_sys_desc);
+    m.sys_rows = 16 * p.rts;
+    m.sys_slots = p.sys_slots;
+  } else if (with_sys && p.sys_mode >= 2) {
+    m.sys_src = 2;
+    m.sys_o = reinterpret_cast<const float*>(ws + p.off_sys_o);
+    m.sys_lse = reinterpret_cast<const float*>(ws + p.off_sys_lse);
+    m.sys_runs = p.sys_chunks;
+  }
+  if (with_ctx) {
+    m.ctx_on = 1;
+    m.ctx_o = reinterpret_cast<const float*>(ws + p.off_ctx_o);
+    m.ctx_lse = reinterpret_cast<const float*>(ws + p.off_ctx_lse);
+    m.ctx_rowdesc = reinterpret_cast<const int*>(ws + p.off_rowdesc);
+    m.ctx_rows = 16 * p.rtc;
+    m.ctx_slots = p.ctx_slots;
+  }
+  m.out = out;
+  m.lse_out = lse_out;
+  m.out_bf16 = out_bf16;
+  hipError_t e = relay::launch_relay_merge(m, d->head_dim, s);
+  return e == hipSuccess ? RELAY_OK : hip_fail(e, "merge launch");
 }
 
 int launch_fuse(FuseArgs& a, int head_dim, hipStream_t s) {
@@ -324,7 +412,7 @@ const char* relay_last_error(void) { return g_err; }
 size_t relay_workspace_size(const relay_dims* dims, int32_t sys_len) {
   if (check_dims(dims, sys_len) != RELAY_OK) return 0;
   Plan p;
-  make_plan(dims, sys_len, &p);
+  if (make_plan(dims, sys_len, &p) != RELAY_OK) return 0;
   return p.ws_bytes;
 }
 
@@ -333,17 +421,17 @@ int relay_get_plan(const relay_dims* dims, int32_t sys_len, relay_plan* out) {
   if (rc != RELAY_OK) return rc;
   if (!out) return fail(RELAY_ERR_INVALID, "plan is NULL");
   Plan p;
-  make_plan(dims, sys_len, &p);
-  out->sys_chunks = p.sys_chunks;
-  out->sys_chunk_len = p.sys_chunk_len;
-  out->sys_row_blocks = p.sys_row_blocks;
-  out->sys_wgs = p.sys_wgs;
-  out->ctx_split_len = p.ctx_split_len;
-  out->ctx_max_splits = p.ctx_max_splits;
-  out->ctx_row_blocks = p.ctx_row_blocks;
-  out->ctx_wgs = p.ctx_wgs;
-  out->fuse_wgs = p.fuse_wgs;
+  if ((rc = make_plan(dims, sys_len, &p)) != RELAY_OK) return rc;
   out->sys_mode = p.sys_mode;
+  out->sys_row_tiles = p.rts;
+  out->sys_runs = p.sys_mode >= 2 ? p.sys_chunks : 0;
+  out->sys_wgs = p.sys_mode >= 2 ? p.sys_wgs : 0;
+  out->ctx_row_tiles = p.rtc;
+  out->ctx_row_blocks = p.ctx_rb;
+  out->stream_waves = p.workers;
+  out->stream_launches = p.n_chunks;
+  out->stream_max_requests = p.chunk_req;
+  out->merge_wgs = p.merge_wgs;
   out->launches = p.launches;
   return RELAY_OK;
 }
@@ -363,35 +451,19 @@ static int decode_impl(const relay_dims* dims, const void* q, const void* sys_k,
       !aligned16(ctx_v_pages) || !aligned16(out))
     return fail(RELAY_ERR_INVALID, "arrays must be 16-byte aligned");
   Plan p;
-  make_plan(dims, sys_len, &p);
+  if ((rc = make_plan(dims, sys_len, &p)) != RELAY_OK) return rc;
   if ((rc = check_ws(p, workspace, workspace_bytes)) != RELAY_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if ((rc = record(events, 0, s)) != RELAY_OK) return rc;
-  int units = relay::kUnitsCtx;
-  if (p.sys_mode == 2) {
-    if ((rc = launch_sys_tiled(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
-  } else if (p.sys_mode == 1) {
-    units = relay::kUnitsBoth;  // both steps in one launch
-  }
+  if (p.sys_mode >= 2 && (rc = launch_sys_kernel(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
   if ((rc = record(events, 1, s)) != RELAY_OK) return rc;
-  if ((rc = launch_units(dims, p, units, q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables,
-                         ctx_lens, cu_q_lens, ws, s)) != RELAY_OK)
+  if ((rc = launch_streams(dims, p, true, true, q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables,
+                           ctx_lens, cu_q_lens, ws, s)) != RELAY_OK)
     return rc;
   if ((rc = record(events, 2, s)) != RELAY_OK) return rc;
-  FuseArgs f{};
-  f.a_o = reinterpret_cast<const float*>(ws + p.off_sys_o);
-  f.a_lse = reinterpret_cast<const float*>(ws + p.off_sys_lse);
-  f.a_count = p.sys_chunks;
-  f.a_sparse = p.sys_mode == 2;
-  f.b_o = reinterpret_cast<const float*>(ws + p.off_ctx_o);
-  f.b_lse = reinterpret_cast<const float*>(ws + p.off_ctx_lse);
-  f.b_count = p.ctx_max_splits;
-  f.out = out;
-  f.lse_out = nullptr;
-  f.n_rows = (long long)dims->total_q * dims->num_q_heads;
-  f.out_bf16 = dims->out_dtype == RELAY_BF16;
-  if ((rc = launch_fuse(f, dims->head_dim, s)) != RELAY_OK) return rc;
+  if ((rc = launch_merge(dims, p, sys_len > 0, true, ws, out, dims->out_dtype == RELAY_BF16, nullptr, s)) != RELAY_OK)
+    return rc;
   return record(events, 3, s);
 }
 
@@ -415,8 +487,6 @@ int relay_attn_decode_timed(const relay_dims* dims, const void* q, const void* s
                      cu_q_lens, out, workspace, workspace_bytes, stream, events);
 }
 
-
-
 int relay_sys_attn(const relay_dims* dims, const void* q, const void* sys_k, const void* sys_v,
                    int32_t sys_len, float* o_sys, float* lse_sys, void* workspace,
                    size_t workspace_bytes, void* stream) {
@@ -427,29 +497,24 @@ int relay_sys_attn(const relay_dims* dims, const void* q, const void* sys_k, con
   if (!aligned16(q) || !aligned16(sys_k) || !aligned16(sys_v) || !aligned16(o_sys))
     return fail(RELAY_ERR_INVALID, "arrays must be 16-byte aligned");
   Plan p;
-  make_plan(dims, sys_len, &p);
+  if ((rc = make_plan(dims, sys_len, &p)) != RELAY_OK) return rc;
   if ((rc = check_ws(p, workspace, workspace_bytes)) != RELAY_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  if (p.sys_mode == 2 && (rc = launch_sys_tiled(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
-  if (p.sys_mode == 1 && (rc = launch_units(dims, p, relay::kUnitsSys, q, sys_k, sys_v, sys_len, nullptr, nullptr,
-                                            nullptr, nullptr, nullptr, ws, s)) != RELAY_OK)
-    return rc;
-  FuseArgs f{};
-  f.a_o = reinterpret_cast<const float*>(ws + p.off_sys_o);
-  f.a_lse = reinterpret_cast<const float*>(ws + p.off_sys_lse);
-  f.a_count = p.sys_chunks;
-  f.a_sparse = p.sys_mode == 2;
-  f.out = o_sys;
-  f.lse_out = lse_sys;
-  f.n_rows = (long long)dims->total_q * dims->num_q_heads;
-  return launch_fuse(f, dims->head_dim, s);
+  if (p.sys_mode >= 2) {
+    if ((rc = launch_sys_kernel(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
+  } else if (p.sys_mode == 1) {
+    if ((rc = launch_streams(dims, p, true, false, q, sys_k, sys_v, sys_len, nullptr, nullptr, nullptr, nullptr,
+                             nullptr, ws, s)) != RELAY_OK)
+      return rc;
+  }
+  return launch_merge(dims, p, sys_len > 0, false, ws, o_sys, 0, lse_sys, s);
 }
 
 size_t relay_prefill_workspace_size(const relay_dims* dims, int32_t sys_len) {
   if (check_dims(dims, sys_len) != RELAY_OK) return 0;
   Plan p;
-  make_plan(dims, sys_len, &p, true);
+  if (make_plan(dims, sys_len, &p, kPrefill) != RELAY_OK) return 0;
   return p.ws_bytes;
 }
 
@@ -464,15 +529,16 @@ int relay_prefill_attn(const relay_dims* dims, const void* q, const void* sys_k,
   if (out_dtype != RELAY_F32 && out_dtype != RELAY_BF16) return fail(RELAY_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
   if (!aligned16(q) || !aligned16(sys_k) || !aligned16(sys_v) || !aligned16(out))
     return fail(RELAY_ERR_INVALID, "arrays must be 16-byte aligned");
-  Plan p;
-  make_plan(dims, sys_len, &p, true);
-  if (!p.sys_mfma)
+  const int M = dims->total_q * (dims->num_q_heads / dims->num_kv_heads);
+  if (dims->in_dtype != RELAY_BF16 || dims->head_dim != 128 || M <= relay::kStreamSysMaxRows)
     return fail(RELAY_ERR_UNSUPPORTED, "the prefill runs on the matrix-core system kernel: bf16, head_dim 128 and "
-                                       "more than %d query rows per KV head", relay::kUnitMaxRows);
+                                       "more than %d query rows per KV head", relay::kStreamSysMaxRows);
+  Plan p;
+  if ((rc = make_plan(dims, sys_len, &p, kPrefill)) != RELAY_OK) return rc;
   if ((rc = check_ws(p, workspace, workspace_bytes)) != RELAY_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  if ((rc = launch_sys_tiled(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
+  if ((rc = launch_sys_kernel(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
   FuseArgs f{};
   f.a_o = reinterpret_cast<const float*>(ws + p.off_sys_o);
   f.a_lse = reinterpret_cast<const float*>(ws + p.off_sys_lse);
@@ -497,21 +563,14 @@ int relay_ctx_attn(const relay_dims* dims, const void* q, const void* ctx_k_page
   if (!aligned16(q) || !aligned16(ctx_k_pages) || !aligned16(ctx_v_pages) || !aligned16(o_ctx))
     return fail(RELAY_ERR_INVALID, "arrays must be 16-byte aligned");
   Plan p;
-  make_plan(dims, 0, &p);
+  if ((rc = make_plan(dims, 0, &p)) != RELAY_OK) return rc;
   if ((rc = check_ws(p, workspace, workspace_bytes)) != RELAY_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  if ((rc = launch_units(dims, p, relay::kUnitsCtx, q, nullptr, nullptr, 0, ctx_k_pages, ctx_v_pages,
-                         block_tables, ctx_lens, cu_q_lens, ws, s)) != RELAY_OK)
+  if ((rc = launch_streams(dims, p, false, true, q, nullptr, nullptr, 0, ctx_k_pages, ctx_v_pages, block_tables,
+                           ctx_lens, cu_q_lens, ws, s)) != RELAY_OK)
     return rc;
-  FuseArgs f{};
-  f.b_o = reinterpret_cast<const float*>(ws + p.off_ctx_o);
-  f.b_lse = reinterpret_cast<const float*>(ws + p.off_ctx_lse);
-  f.b_count = p.ctx_max_splits;
-  f.out = o_ctx;
-  f.lse_out = lse_ctx;
-  f.n_rows = (long long)dims->total_q * dims->num_q_heads;
-  return launch_fuse(f, dims->head_dim, s);
+  return launch_merge(dims, p, false, true, ws, o_ctx, 0, lse_ctx, s);
 }
 
 int relay_fuse(int64_t n_rows, int32_t head_dim, const float* o_sys, const float* lse_sys,

@@ -356,6 +356,18 @@ struct StepK {
   static constexpr int NCH = D * Elem<T>::kBytes / 64;
   u32x4 a[NCH], b[NCH];  // this lane's K chunks of score tiles A and B
 };
+// Loads the B operand of S^T = K Q^T for one 16-row tile: lane (r16, q) of product kk
+// takes 16 bytes of its query row at byte offset 64 kk + 16 q (zeros for a padding row).
+template <typename T, int D>
+__device__ inline void load_q_tile(u32x4* qf, const void* q, size_t row_index, bool valid) {
+  constexpr int E = Elem<T>::kBytes;
+  const int q4 = lane_id() >> 4;
+  const char* qp = static_cast<const char*>(q) + row_index * D * E;
+#pragma unroll
+  for (int kk = 0; kk < StepK<T, D>::NCH; ++kk)
+    qf[kk] = valid ? ld16(qp + 64 * kk + 16 * q4) : u32x4{0u, 0u, 0u, 0u};
+}
+
 template <typename T, int D>
 struct StepV {
   VFrag<T> v[D / 16];  // V^T of this lane group's 8 keys, per 16-dimension tile

@@ -1,4 +1,4 @@
-// Internal interface between the C-ABI host code and the three kernels.
+// Internal interface between the C-ABI host code and the kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,68 +35,99 @@ struct SysArgs {
   int causal;
 };
 
-// Tile configuration of sys_attn: rt row tiles (16 rows each) per wave, wk waves
+// Tile configuration of sys_attn_tiled: rt row tiles (16 rows each) per wave, wk waves
 // sharing the rows over different keys, wr row groups per workgroup.
 struct SysConfig {
   int rt, wk, wr;
 };
 
-// Up to this many stacked query rows per KV head the system step runs as
-// single-wave units (HBM-bound); above it as the tiled kernel (matrix-core-bound).
-constexpr int kUnitMaxRows = 64;
+// Up to this many stacked query rows per KV head the system step streams together with
+// the context step (HBM-bound, one stream per KV head); above it the matrix-core system
+// kernel runs first (compute-bound).
+constexpr int kStreamSysMaxRows = 64;
 
-// The tiled configuration used for M = T_q * g stacked query rows per KV head.
-inline SysConfig sys_config(int M) {
-  if (M <= 16) return {1, 8, 1};
-  if (M <= 32) return {2, 4, 1};
-  if (M <= 64) return {4, 2, 1};
-  return {2, 1, 4};
-}
+// The tiled kernel's configuration (it runs only above kStreamSysMaxRows stacked rows).
+inline SysConfig sys_config(int) { return {2, 1, 4}; }
 
-// Single-wavefront units (attn_units.hip): system units over 16-row tiles and
-// context units, launched alone or together.
-struct UnitArgs {
+// stream_attn (stream_attn.hip): the system and context steps as one launch of equal
+// contiguous step ranges, one per wave.
+constexpr int kStreamWaves = 4;          // waves per workgroup, one workgroup per CU
+constexpr int kStreamMaxRequests = 3968; // requests per streaming launch: 4 LDS tables + scan <= 64 KiB
+
+struct StreamArgs {
   const void* q;       // [T_q, H_q, d]
   int total_q;
   int num_q_heads;
   int num_kv_heads;
   int group;
-  float scale_log2;
-  // system units: n_sys_units = 8 * sys_row_tiles * ceil(H_kv * sys_chunks / 8), or 0
+  float scale_log2;    // scale * log2(e)
+  // system streams: one per KV head over its M <= 64 stacked rows (sys_steps = 0: none)
   const void* sys_k;   // [H_kv, ceil(L_s/16), d/G, 16, G] key tiles
   const void* sys_v;   // [H_kv, ceil(L_s/16), d, 16]
-  float* sys_o;        // [sys_chunks, T_q, H_q, d]
-  float* sys_lse;      // [sys_chunks, T_q, H_q]
   int sys_len;
-  int sys_chunk_len;   // multiple of 32
-  int sys_chunks;
-  int sys_row_tiles;   // row units: ceil(T_q * g / (16 * sys_rt))
-  int sys_rt;          // 16-row tiles per system unit: 1, or 2 (four key lanes only)
-  int n_sys_units;
-  // context units: n_ctx_units = 8 * ctx_row_blocks * ceil(max_splits * H_kv * B / 8), or 0
+  int sys_steps;       // ceil(L_s / 32)
+  int M;               // stacked rows per KV head (T_q * g)
+  float* sys_o;        // [H_kv + n_workers slots][16 RTS rows][d]
+  float* sys_lse;      // [slots][16 RTS]
+  int* sys_desc;       // [H_kv][2]: first slot, number of pieces
+  // context streams (request, KV head, row block) of requests [b_begin, b_begin + n_req)
+  int ctx_on;
   const void* ctx_k;   // [num_blocks, H_kv, d/G, 16, G] key tiles
   const void* ctx_v;   // [num_blocks, H_kv, d, 16]
   const int32_t* block_tables;
   const int32_t* ctx_lens;
   const int32_t* cu_q_lens;  // NULL: one query per request
-  float* ctx_o;        // [max_splits, T_q, H_q, d]
-  float* ctx_lse;      // [max_splits, T_q, H_q]
   int batch;
+  int b_begin;
+  int n_req;
   int num_blocks;
   int max_blocks_per_seq;
-  int max_ctx_len;     // clamp for c_b (keeps splits inside the workspace)
-  int ctx_split_len;   // multiple of 32, at most 1024
-  int ctx_max_splits;
-  int ctx_row_blocks;  // ceil(max_q_len * g / (16 * ctx_rt))
-  int n_ctx_units;
-  int key_lanes;       // waves per unit: 4, or 8 with one row tile
-  int grid;            // > 0: workgroups of the persistent launch; 0: as many as fit
+  int max_ctx_len;     // clamp for c_b
+  int ctx_rb;          // row blocks (16 RTC rows each) per (request, KV head)
+  long long slot_base; // first context slot of this launch's pieces
+  float* ctx_o;        // [slots][16 RTC][d]
+  float* ctx_lse;      // [slots][16 RTC]
+  int* ctx_rowdesc;    // [T_q * H_q][4]: first slot, number of pieces, row in the piece
+  int n_workers;       // waves of the launch (grid * kStreamWaves)
 };
 
-constexpr int kUnitsSys = 1, kUnitsCtx = 2, kUnitsBoth = 3;
+size_t stream_lds_bytes(int n_req, int ctx_on);
+hipError_t launch_stream_attn(const StreamArgs& a, int rts, int rtc, int in_dtype, int head_dim, int grid,
+                              hipStream_t stream);
 
-// Row tiles per context unit for up to R query rows per request.
+// Row tiles per context stream for up to R query rows per (request, KV head).
 inline int ctx_rt_for(int rows_per_request) { return rows_per_request <= 16 ? 1 : 2; }
+
+// relay_merge (relay_fuse.hip): each row's output from the pieces of its system stream
+// (or the runs of the system kernel) and of its context stream.
+struct MergeArgs {
+  long long n_rows;    // T_q * H_q
+  int num_q_heads;
+  int group;
+  // system part: 0 none, 1 stream pieces (sys_desc), 2 system-kernel runs (slot i of
+  // row r at sys_o[(i n_rows + r) d], LSE = -inf marks an empty run)
+  int sys_src;
+  const float* sys_o;
+  const float* sys_lse;
+  const int* sys_desc;
+  int sys_rows;        // rows per stream slot (16 RTS)
+  long long sys_slots; // stream slots (clamp)
+  int sys_runs;        // sys_src 2: run slots per row
+  // context part: stream pieces located by ctx_rowdesc
+  int ctx_on;
+  const float* ctx_o;
+  const float* ctx_lse;
+  const int* ctx_rowdesc;
+  int ctx_rows;        // rows per context slot (16 RTC)
+  long long ctx_slots; // context slots (clamp)
+  void* out;
+  float* lse_out;      // may be NULL
+  int out_bf16;
+};
+hipError_t launch_relay_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
+inline int merge_threads(int head_dim, long long n_rows) {
+  return n_rows >= 2LL * 256 * (256 / (head_dim / 4)) ? 256 : 64;
+}
 
 // relay_fuse: LSE-weighted merge of two groups of partials per row: group A
 // (system chunks) a_count partials, partial i of row r at a_o[i*rows + r]; group B
@@ -158,8 +189,6 @@ inline __host__ __device__ int lean_part_of(long long x, int total, int parts) {
   return (int)(((x + 1) * parts + total - 1) / total) - 1;
 }
 hipError_t launch_sys_attn_mfma(const SysArgs& a, int nwg, hipStream_t stream);
-hipError_t launch_attn_units(const UnitArgs& a, int ctx_rt, int what, int in_dtype, int head_dim,
-                             hipStream_t stream);
 // relay_fuse workgroup size: one wave, or four once there are enough rows for two
 // four-wave workgroups per CU (D/4 lanes per row).
 inline int fuse_threads(int head_dim, long long n_rows) {

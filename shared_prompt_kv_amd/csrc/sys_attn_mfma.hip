@@ -33,6 +33,10 @@ namespace relay {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// A decode step adds P's bf16 rounding residual when some row's largest probability in
+// it exceeds 1 / kSplitShare of the row's running sum.
+constexpr float kSplitShare = 32.f;
+
 namespace mf {
 constexpr int D = 128;
 constexpr int kRowsPerWave = 32;
@@ -104,37 +108,37 @@ __device__ __forceinline__ void mf_issue(char* buf, const char* kbase, const cha
 // Per-lane byte offsets of one step's loads relative to its first key key0: both
 // layouts hold 256 bytes per key (a 16-key tile of 128-dim bf16 keys or values is 4096
 // bytes), and steps start at multiples of 64 keys, so every load of a step is
-// base + 256 key0 + a constant of the lane.  Steps that end inside the prompt use
-// these; the step holding the prompt's end goes through mf_issue (clamped rows).
+// base + 256 key0 + a constant of the lane.  Load j of a lane lands at LDS position
+// p = 256 j + 64 wave + lane: K row p % 64 = lane, chunk p / 64 = 4 j + wave; V row
+// d = 32 j + 8 wave + lane / 8, chunk (lane % 8) ^ (d % 8) with d % 8 = (lane / 8) % 8.
+// Both offsets are base + 1024 j, so a lane keeps two bases.  Steps that end inside
+// the prompt use these; the step holding the prompt's end goes through mf_issue
+// (clamped rows).
 struct MfLaneOffsets {
-  uint32_t k[mf::kChunks];
-  uint32_t v[mf::kChunks];
+  uint32_t k, v;
 };
 
 __device__ __forceinline__ MfLaneOffsets mf_lane_offsets(int wave) {
   const int lane = lane_id();
   MfLaneOffsets o;
-#pragma unroll
-  for (int j = 0; j < mf::kChunks; ++j) {
-    const int p = mf::kThreads * j + kWave * wave + lane;
-    o.k[j] = mf_key_offset(p & 63, p >> 6);
-    const int d = p >> 3, cv = (p & 7) ^ (d & 7);
-    o.v[j] = (uint32_t)((cv >> 1) * (mf::D * kTile * 2) + d * (kTile * 2) + (cv & 1) * 16);
-  }
+  o.k = mf_key_offset(lane, wave);
+  const int d = 8 * wave + (lane >> 3), cv = (lane & 7) ^ (d & 7);
+  o.v = (uint32_t)((cv >> 1) * (mf::D * kTile * 2) + d * (kTile * 2) + (cv & 1) * 16);
   return o;
 }
 
 __device__ __forceinline__ void mf_issue_full(char* buf, const char* kstep, const char* vstep, int wave,
                                               const MfLaneOffsets& o) {
+  static_assert(mf::kChunks * mf::kThreads * 16 == mf::kTileBytes, "loads per tile");
 #pragma unroll
   for (int j = 0; j < mf::kChunks; ++j) {
     const int base = mf::kThreads * j + kWave * wave;
-    __builtin_amdgcn_global_load_lds(kstep + o.k[j], (lds_ptr_t)(buf + base * 16), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(kstep + o.k + 1024 * j, (lds_ptr_t)(buf + base * 16), 16, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < mf::kChunks; ++j) {
     const int base = mf::kThreads * j + kWave * wave;
-    __builtin_amdgcn_global_load_lds(vstep + o.v[j], (lds_ptr_t)(buf + mf::kTileBytes + base * 16), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vstep + o.v + 1024 * j, (lds_ptr_t)(buf + mf::kTileBytes + base * 16), 16, 0, 0);
   }
 }
 
@@ -250,42 +254,40 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
       const bool more = s + 1 < nsteps;
       if (more) issue(lds_raw + ((s + 1) & 1) * mf::kBufBytes, key0 + mf::kKB);
 
-      // ---- scores of the 64 keys: two 32-key blocks
-      f32x16 sacc[2];
+      // ---- scores of the 64 keys (two 32-key blocks) from the K tile in LDS; lane (row,
+      // hh) holds keys 32 kb2 + 16 (j / 8) + 8 hh + j % 8 as sc[16 kb2 + j].  Scale-free
+      // with the scale's sign folded in; causal steps that token t_lo does not wholly see
+      // mask keys past t (and past the prompt) to -inf, so their exponentials are 0 (scale
+      // > 0).  Otherwise no masking: in the step holding the prompt's end, rows past it
+      // hold copies of the last key (mf_issue clamps them), whose scores leave the
+      // maximum unchanged, and their values are zero in LDS, so they add nothing to O;
+      // only the row sum leaves them out.
+      auto raw_scores = [&](float (&sc)[32]) {
+        f32x16 sacc[2];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        sacc[kb2] = f32x16{};
-        const char* krow = buf + (32 * kb2 + r32) * 16;  // LDS row 32 kb2 + r32, chunk-major
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          sacc[kb2] = f32x16{};
+          const char* krow = buf + (32 * kb2 + r32) * 16;  // LDS row 32 kb2 + r32, chunk-major
 #pragma unroll
-        for (int kk = 0; kk < mf::D / 16; ++kk) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(krow + (2 * kk + hh) * (mf::kKB * 16));
-          sacc[kb2] = mfma32(ka, qf[kk], sacc[kb2]);
+          for (int kk = 0; kk < mf::D / 16; ++kk) {
+            const u32x4 ka = *reinterpret_cast<const u32x4*>(krow + (2 * kk + hh) * (mf::kKB * 16));
+            sacc[kb2] = mfma32(ka, qf[kk], sacc[kb2]);
+          }
         }
-      }
-      // raw scores; lane (row, hh) holds keys 32 kb2 + 16 (j / 8) + 8 hh + j % 8
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) sc[16 * kb2 + j] = negative_scale ? -sacc[kb2][j] : sacc[kb2][j];
+        }
+        if (CAUSAL && key0 + mf::kKB - 1 > t_lo) {
+          const int lim_c = min(t + 1, Ls) - key0 - 8 * hh;
+#pragma unroll
+          for (int i = 0; i < 32; ++i)
+            if (16 * (i >> 3) + (i & 7) >= lim_c) sc[i] = neg_inf();
+        }
+      };
       float sc[32];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sc[16 * kb2 + j] = sacc[kb2][j];
-      }
-      if (negative_scale) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) sc[i] = -sc[i];
-      }
-      // causal steps some token of the workgroup does not wholly see: score i of the
-      // lane (key 16 (i / 8) + 8 hh + i % 8 of the step) is masked unless that key is
-      // <= t and < Ls; with scale > 0 a masked score's exponential is exactly 0
-      if (CAUSAL && key0 + mf::kKB - 1 > t_lo) {
-        const int lim_c = min(t + 1, Ls) - key0 - 8 * hh;
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-          if (16 * (i >> 3) + (i & 7) >= lim_c) sc[i] = neg_inf();
-      }
-      // Otherwise no masking before the exponentials: in the step holding the prompt's end, rows
-      // past it hold copies of the last key (mf_issue clamps them), whose scores leave
-      // the maximum unchanged, and their values are zero in LDS, so they add nothing to
-      // O; only the row sum below leaves them out.
+      raw_scores(sc);
       // ---- online softmax on scale-free scores (lanes l and l ^ 32 hold the same row):
       // the reference m is kept scaled, p = 2^(|scale| s - m) is one FMA and an exp
       float mx = sc[0];
@@ -318,47 +320,46 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
 #pragma unroll
         for (int i = 0; i < 32; ++i) lsum += sc[i];
       }
-      // ---- P (bf16) per 16-key block kb: k slots 0..7 = keys 0..7 (lanes hh = 0),
-      // 8..15 = keys 8..15 (hh = 1), i.e. sc[8 kb .. 8 kb + 7]; then O^T += V^T P^T
-      u32x4 pb[4], pl[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const float* p = sc + 8 * kb;
-        pb[kb] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                       pack_bf16x2(p[6], p[7])};
-        if constexpr (CAUSAL) {  // P = hi + lo, both bf16: lo is what rounding left out
-          const u32x4 h = pb[kb];
-          pl[kb] = psplit ? u32x4{pack_bf16x2(p[0] - bf16_lo_as_float(h[0]), p[1] - bf16_hi_as_float(h[0])),
-                                  pack_bf16x2(p[2] - bf16_lo_as_float(h[1]), p[3] - bf16_hi_as_float(h[1])),
-                                  pack_bf16x2(p[4] - bf16_lo_as_float(h[2]), p[5] - bf16_hi_as_float(h[2])),
-                                  pack_bf16x2(p[6] - bf16_lo_as_float(h[3]), p[7] - bf16_hi_as_float(h[3]))}
-                          : u32x4{0u, 0u, 0u, 0u};
-        }
-      }
+      // ---- O^T += V^T P^T per 16-key block kb: k slots 0..7 = keys 0..7 (lanes hh = 0),
+      // 8..15 = keys 8..15 (hh = 1), i.e. sc[8 kb .. 8 kb + 7].  P enters as bf16; its
+      // rounding costs up to 2^-9 of each probability.  Where that could matter, the
+      // rounding residual lo = P - bf16(P) (also bf16) goes in as a second product:
+      //  * causal segments that some token sees little of (psplit, known per segment);
+      //  * decode steps in which some row's largest probability exceeds 1 / kSplitShare
+      //    of the row's running sum, i.e. a key that may hold a large share of the row's
+      //    weight.  Keys below that share round once: their errors are small and
+      //    independent.
       const char* vt = buf + mf::kTileBytes;
-      if (CAUSAL && psplit) {  // a second product per fragment with the low parts
+      const int vsw = (hh ^ (r32 & 7)) << 4;  // V chunk 2 kb + hh of row d sits at (2 kb + hh) ^ (d % 8); d % 8 = r32 % 8
+      auto pv = [&](const float (&pp)[32], bool hi_part, bool lo_part) {
 #pragma unroll
-        for (int db = 0; db < mf::D / 32; ++db) {
-          const int d = 32 * db + r32;
-          const char* vrow = vt + d * 128;
+        for (int kb = 0; kb < 4; ++kb) {
+          const float* p = pp + 8 * kb;
+          const u32x4 hi = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                 pack_bf16x2(p[6], p[7])};
+          u32x4 lo = hi;
+          if (lo_part)
+            lo = u32x4{pack_bf16x2(p[0] - bf16_lo_as_float(hi[0]), p[1] - bf16_hi_as_float(hi[0])),
+                       pack_bf16x2(p[2] - bf16_lo_as_float(hi[1]), p[3] - bf16_hi_as_float(hi[1])),
+                       pack_bf16x2(p[4] - bf16_lo_as_float(hi[2]), p[5] - bf16_hi_as_float(hi[2])),
+                       pack_bf16x2(p[6] - bf16_lo_as_float(hi[3]), p[7] - bf16_hi_as_float(hi[3]))};
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(vrow + (((2 * kb + hh) ^ (d & 7)) << 4));
-            o[db] = mfma32(v, pb[kb], o[db]);
-            o[db] = mfma32(v, pl[kb], o[db]);
+          for (int db = 0; db < mf::D / 32; ++db) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(vt + (32 * db + r32) * 128 + (((2 * kb) << 4) ^ vsw));
+            if (hi_part) o[db] = mfma32(v, hi, o[db]);
+            if (lo_part) o[db] = mfma32(v, lo, o[db]);
           }
         }
+      };
+      if constexpr (CAUSAL) {
+        if (psplit) pv(sc, true, true);
+        else pv(sc, true, false);
       } else {
-#pragma unroll
-        for (int db = 0; db < mf::D / 32; ++db) {
-          const int d = 32 * db + r32;
-          const char* vrow = vt + d * 128;
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(vrow + (((2 * kb + hh) ^ (d & 7)) << 4));
-            o[db] = mfma32(v, pb[kb], o[db]);
-          }
-        }
+        float la, lb;
+        swap32(lsum, la, lb);
+        const bool split = __builtin_amdgcn_ballot_w64(fast_exp2(mx - m_use) * kSplitShare > la + lb) != 0;
+        if (split) pv(sc, true, true);
+        else pv(sc, true, false);
       }
       if (more) __builtin_amdgcn_s_waitcnt(0);  // the next step's tiles have landed
       __syncthreads();  // (also: the buffers are free for the next segment)

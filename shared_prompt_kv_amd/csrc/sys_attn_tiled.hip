@@ -185,18 +185,15 @@ static hipError_t launch_sys_t(const SysArgs& a, int nwg, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Small M is bound by HBM: P goes to the output product as bf16 hi + lo for free.
-// Large M is bound by the matrix cores: a single bf16 P (its rounding error is
-// averaged over the many keys of a long system prompt).
+// The tiled kernel runs the system step for more than 64 stacked rows per KV head when
+// the inputs are fp32 or head_dim is 64 (bf16 at head_dim 128 has sys_attn_mfma): row
+// groups of 2 tiles, 4 per workgroup.  bf16 P goes to the output product as hi + lo: a
+// single rounding costs up to 2^-9 of a probability, too much where one key holds much
+// of a row's weight.
 template <typename T, int D>
 static hipError_t launch_sys_d(const SysArgs& a, const SysConfig& c, int nwg, hipStream_t s) {
-  if (c.wr == 1) {
-    if (c.rt == 1) return launch_sys_t<T, D, 1, 8, 1, true>(a, nwg, s);
-    if (c.rt == 2) return launch_sys_t<T, D, 2, 4, 1, true>(a, nwg, s);
-    return launch_sys_t<T, D, 4, 2, 1, true>(a, nwg, s);
-  }
-  if (a.sys_len < 1024) return launch_sys_t<T, D, 2, 1, 4, true>(a, nwg, s);
-  return launch_sys_t<T, D, 2, 1, 4, false>(a, nwg, s);
+  if (c.rt != 2 || c.wk != 1 || c.wr != 4) return hipErrorInvalidValue;
+  return launch_sys_t<T, D, 2, 1, 4, true>(a, nwg, s);
 }
 
 hipError_t launch_sys_attn_tiled(const SysArgs& a, const SysConfig& c, int in_dtype, int head_dim,

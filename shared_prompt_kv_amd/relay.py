@@ -41,8 +41,8 @@ class relay_dims(ctypes.Structure):
 
 class relay_plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "sys_chunks", "sys_chunk_len", "sys_row_blocks", "sys_wgs", "ctx_split_len",
-        "ctx_max_splits", "ctx_row_blocks", "ctx_wgs", "fuse_wgs", "sys_mode", "launches")]
+        "sys_mode", "sys_row_tiles", "sys_runs", "sys_wgs", "ctx_row_tiles", "ctx_row_blocks",
+        "stream_waves", "stream_launches", "stream_max_requests", "merge_wgs", "launches")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -144,6 +144,86 @@ def _require_device(*ts):
             raise ValueError("all tensors must be contiguous")
 
 
+def _elems16(dt: torch.dtype) -> int:
+    return 8 if dt == torch.bfloat16 else 4
+
+
+def _check_system_cache(q, sys_k, sys_v, sys_len: int, num_kv_heads: int):
+    """sys_k / sys_v must be the system cache layouts of q's dtype covering sys_len keys."""
+    if sys_len < 0:
+        raise ValueError(f"sys_len must be >= 0 (got {sys_len})")
+    if sys_len == 0:
+        return
+    d = q.shape[-1]
+    g = min(_elems16(q.dtype), d)
+    tiles = -(-sys_len // 16)
+    for name, x in (("sys_k", sys_k), ("sys_v", sys_v)):
+        if x is None:
+            raise ValueError(f"{name} is required when sys_len > 0")
+        if x.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {x.dtype} differs from q's {q.dtype}")
+    want_k = (num_kv_heads, tiles, d // g, 16, g)
+    want_v = (num_kv_heads, tiles, d, 16)
+    # the kernels step from one KV head's tiles to the next by ceil(sys_len / 16) tiles
+    if tuple(sys_k.shape) != want_k:
+        raise ValueError(f"sys_k must be key tiles {want_k} for sys_len {sys_len}, got {tuple(sys_k.shape)}")
+    if tuple(sys_v.shape) != want_v:
+        raise ValueError(f"sys_v must be value tiles {want_v} for sys_len {sys_len}, got {tuple(sys_v.shape)}")
+
+
+def _check_context(q, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens):
+    """Paged context cache, block tables and lengths: layouts, dtypes and batch size."""
+    if q.dim() != 3:
+        raise ValueError("q must be [T_q, H_q, d]")
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"unsupported dtype {q.dtype} (float32 or bfloat16)")
+    Tq, Hq, d = q.shape
+    g = min(_elems16(q.dtype), d)
+    if ctx_k_pages.dim() != 5 or ctx_k_pages.shape[2] * ctx_k_pages.shape[4] != d or ctx_k_pages.shape[3] != 16 \
+            or ctx_k_pages.shape[4] != g:
+        raise ValueError(f"ctx_k_pages must be key tiles [num_blocks, H_kv, {d // g}, 16, {g}], "
+                         f"got {tuple(ctx_k_pages.shape)}")
+    nb, Hkv = ctx_k_pages.shape[:2]
+    if tuple(ctx_v_pages.shape) != (nb, Hkv, d, 16):
+        raise ValueError(f"ctx_v_pages must be [{nb}, {Hkv}, {d}, 16], got {tuple(ctx_v_pages.shape)}")
+    for name, x in (("ctx_k_pages", ctx_k_pages), ("ctx_v_pages", ctx_v_pages)):
+        if x.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {x.dtype} differs from q's {q.dtype}")
+    if Hq % Hkv:
+        raise ValueError(f"H_q ({Hq}) must be a multiple of H_kv ({Hkv})")
+    if block_tables.dim() != 2 or block_tables.dtype != torch.int32:
+        raise ValueError("block_tables must be int32 [B, max_blocks_per_seq]")
+    B = block_tables.shape[0]
+    if ctx_lens.dtype != torch.int32 or tuple(ctx_lens.shape) != (B,):
+        raise ValueError(f"ctx_lens must be int32 [{B}]")
+    if cu_q_lens is None:
+        if Tq != B:
+            raise ValueError(f"without cu_q_lens every request has one query token: q has {Tq} rows, batch {B}")
+    elif cu_q_lens.dtype != torch.int32 or tuple(cu_q_lens.shape) != (B + 1,):
+        raise ValueError(f"cu_q_lens must be int32 [{B + 1}]")
+
+
+def _check_out(q, out, out_dtype):
+    if out is None:
+        return
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}, got {tuple(out.shape)}")
+    if out.dtype != out_dtype:
+        raise ValueError(f"out dtype {out.dtype} differs from out_dtype {out_dtype}")
+
+
+def check_decode_args(q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens,
+                      cu_q_lens=None, out=None, out_dtype=torch.float32):
+    """Shapes, dtypes and sizes of a relay_attn_decode call (no device needed; raises
+    ValueError).  The C library cannot see tensor extents, so an output or cache too
+    small for the dims would be written or read out of bounds: the binding refuses it."""
+    _check_context(q, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens)
+    _check_system_cache(q, sys_k, sys_v, int(sys_len), ctx_k_pages.shape[1])
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"unsupported out_dtype {out_dtype}")
+    _check_out(q, out, out_dtype)
+
+
 def make_dims(q: torch.Tensor, ctx_k_pages: torch.Tensor, block_tables: torch.Tensor, *,
               scale: float, max_ctx_len: int, max_q_len: int = 1,
               out_dtype: torch.dtype = torch.float32) -> relay_dims:
@@ -190,6 +270,8 @@ def relay_attn_decode(q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_
                       stream=None) -> torch.Tensor:
     """RelayAttention decode step (system + context attention + relay fusion)."""
     _require_device(q, sys_k, sys_v, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens, out)
+    check_decode_args(q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens,
+                      out, out_dtype)
     dims = make_dims(q, ctx_k_pages, block_tables, scale=scale, max_ctx_len=max_ctx_len,
                      max_q_len=max_q_len, out_dtype=out_dtype)
     if out is None:
@@ -206,6 +288,10 @@ def relay_attn_decode_timed(t: dict, out, workspace_buf, events, out_dtype=torch
                             stream=None):
     """relay_attn_decode on a ``to_device`` dict, recording 4 raw hipEvent_t handles
     (ints) between the kernels."""
+    _require_device(t["q"], t["sys_k"], t["sys_v"], t["ctx_k_pages"], t["ctx_v_pages"], t["block_tables"],
+                    t["ctx_lens"], t["cu_q_lens"], out, workspace_buf)
+    check_decode_args(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], t["ctx_k_pages"], t["ctx_v_pages"],
+                      t["block_tables"], t["ctx_lens"], t["cu_q_lens"], out, out_dtype)
     dims = dims_of(t, out_dtype)
     ev = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) if e else None for e in events])
     _check(load_library().relay_attn_decode_timed(
@@ -218,6 +304,10 @@ def relay_attn_decode_timed(t: dict, out, workspace_buf, events, out_dtype=torch
 def relay_sys_attn(q, sys_k, sys_v, sys_len, dims: relay_dims, *, workspace_buf=None, stream=None):
     """System-attention step alone -> (o_sys float32 [T_q,H_q,d], lse_sys float32 [T_q,H_q])."""
     _require_device(q, sys_k, sys_v)
+    if q.dim() != 3 or tuple(q.shape) != (dims.total_q, dims.num_q_heads, dims.head_dim) \
+            or _dtype_code(q.dtype) != dims.in_dtype:
+        raise ValueError("q does not match dims")
+    _check_system_cache(q, sys_k, sys_v, int(sys_len), dims.num_kv_heads)
     o = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     ws = workspace_buf if workspace_buf is not None else workspace(dims, sys_len, q.device)
@@ -268,6 +358,7 @@ def relay_ctx_attn(q, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_len
                    *, workspace_buf=None, stream=None):
     """Context-attention step alone -> (o_ctx, lse_ctx)."""
     _require_device(q, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens)
+    _check_context(q, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens)
     o = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     ws = workspace_buf if workspace_buf is not None else workspace(dims, 0, q.device)
@@ -282,6 +373,11 @@ def relay_fuse(o_sys, lse_sys, o_ctx, lse_ctx, *, out_dtype=torch.float32, with_
                stream=None):
     """Relay fusion alone -> (out, lse or None)."""
     _require_device(o_sys, lse_sys, o_ctx, lse_ctx)
+    for x in (o_sys, lse_sys, o_ctx, lse_ctx):
+        if x.dtype != torch.float32:
+            raise ValueError("relay_fuse partials are float32")
+    if o_ctx.shape != o_sys.shape or lse_sys.shape != lse_ctx.shape or tuple(o_sys.shape[:-1]) != tuple(lse_sys.shape):
+        raise ValueError("o_sys / o_ctx must be [..., d] and lse_sys / lse_ctx the matching [...]")
     d = o_sys.shape[-1]
     n = lse_sys.numel()
     out = torch.empty(o_sys.shape, dtype=out_dtype, device=o_sys.device)
@@ -420,6 +516,8 @@ class DecodeCall:
                  timed_events=None):
         _require_device(t["q"], t["sys_k"], t["sys_v"], t["ctx_k_pages"], t["ctx_v_pages"],
                         t["block_tables"], t["ctx_lens"], t["cu_q_lens"], out, workspace_buf)
+        check_decode_args(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], t["ctx_k_pages"], t["ctx_v_pages"],
+                          t["block_tables"], t["ctx_lens"], t["cu_q_lens"], out, out_dtype)
         self.dims = dims_of(t, out_dtype)
         need = relay_workspace_size(self.dims, t["sys_len"])
         if workspace_buf.numel() < need:

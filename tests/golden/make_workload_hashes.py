@@ -8,7 +8,7 @@ import os
 import sys
 
 sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__)))))
-from shared_prompt_kv_amd import workloads as W  # noqa: E402
+import workloads as W  # noqa: E402
 from tests.test_workloads import _hash_specs  # noqa: E402
 
 if __name__ == "__main__":

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from shared_prompt_kv_amd import relay as R
-from shared_prompt_kv_amd import workloads as W
+import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "relay_attn.h")
@@ -51,7 +51,7 @@ def test_library_is_gfx950_only(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert R.relay_abi_version() == 2
+    assert R.relay_abi_version() == 3
     assert lib.relay_strerror(0) == b"ok"
     assert lib.relay_strerror(-3) == b"workspace too small"
 
@@ -107,17 +107,31 @@ def test_pointer_and_workspace_errors(lib):
     assert lib.relay_fuse(0, 128, None, None, None, None, None, 0, None, None) == 0
 
 
+CUS = 256          # no GPU here: the library plans for 256 compute units
+WAVES = 4 * CUS    # one four-wave workgroup per compute unit
+
+
+def a256(x):
+    return -(-x // 256) * 256
+
+
 def test_workspace_covers_the_plan(lib):
-    d = base_dims()
+    """Workspace = the partial regions of the streaming launch, laid out as the header says:
+    system pieces (H_kv + waves slots of 16 * sys_row_tiles rows), their descriptors,
+    context pieces (B H_kv row_blocks + waves slots per request group) and row descriptors."""
+    d = base_dims()               # B 4, H_q 8 / H_kv 2 -> M = 16 stacked rows per KV head
     plan = R.relay_get_plan(d, 1000)
-    rows = 4 * 8
-    need = R.relay_workspace_size(d, 1000)
-    parts = (plan["sys_chunks"] + plan["ctx_max_splits"]) * rows * (128 + 1) * 4
-    assert need >= parts and need <= parts + 4 * 256
-    assert plan["sys_chunks"] * plan["sys_chunk_len"] >= 1000
-    assert plan["sys_chunk_len"] % 32 == 0 and plan["ctx_split_len"] % 32 == 0
-    assert plan["ctx_max_splits"] * plan["ctx_split_len"] >= 128
-    assert R.relay_get_plan(d, 0)["sys_chunks"] == 0
+    assert plan["sys_mode"] == 1 and plan["sys_row_tiles"] == 1
+    assert plan["ctx_row_tiles"] == 1 and plan["ctx_row_blocks"] == 1
+    assert plan["stream_waves"] == WAVES and plan["stream_launches"] == 1 and plan["launches"] == 2
+    rows, D, H = 4 * 8, 128, 2
+    sys_slots, ctx_slots = H + WAVES, 4 * H * 1 + WAVES
+    expect = (a256(sys_slots * 16 * D * 4) + a256(sys_slots * 16 * 4) + a256(H * 2 * 4)
+              + a256(ctx_slots * 16 * D * 4) + a256(ctx_slots * 16 * 4) + a256(rows * 16))
+    assert R.relay_workspace_size(d, 1000) == expect
+    p0 = R.relay_get_plan(d, 0)
+    assert p0["sys_mode"] == 0 and p0["launches"] == 2
+    assert R.relay_workspace_size(d, 0) == expect - a256(sys_slots * 16 * D * 4) - a256(sys_slots * 16 * 4) - a256(H * 8)
 
 
 @pytest.mark.parametrize("cfg,sweep", [(1, 0), (2, 0), (3, 0), (3, 5), (4, 0), (5, 0)])
@@ -129,48 +143,136 @@ def test_plan_for_each_config(lib, cfg, sweep):
                      spec.scale, 1 if spec.dtype == "bf16" else 0, 0)
     plan = R.relay_get_plan(d, spec.sys_len)
     M = s["total_q"] * spec.group
-    if M <= 64:   # single-wave system units, launched together with the context units
-        assert plan["sys_chunks"] * plan["sys_chunk_len"] >= spec.sys_len
-        assert (plan["sys_chunks"] - 1) * plan["sys_chunk_len"] < spec.sys_len
+    if M <= 64:   # system streams (all M rows of a KV head) in the streaming launch
         assert plan["sys_mode"] == 1 and plan["launches"] == 2
-        groups = spec.num_kv_heads * plan["sys_chunks"]
-        # units of two 16-row tiles when M <= 32 and there are >= 384 (head, chunk) groups
-        rt = 2 if 16 < M <= 32 and groups >= 384 else 1
-        assert plan["sys_row_blocks"] == -(-M // (16 * rt))
-        assert plan["sys_wgs"] == 8 * plan["sys_row_blocks"] * (-(-groups // 8))
+        tiles = -(-M // 16)
+        assert plan["sys_row_tiles"] == (tiles if tiles <= 2 else 4)
+        assert plan["sys_runs"] == 0 and plan["sys_wgs"] == 0
     else:         # matrix-core system kernel: (row block, run of 64-key steps) workgroups
         assert plan["sys_mode"] == 2 and plan["launches"] == 3
-        assert plan["sys_row_blocks"] * 128 >= M
+        row_blocks = -(-M // 128)
         steps = spec.num_kv_heads * -(-spec.sys_len // 64)
-        parts = min(max(512 // plan["sys_row_blocks"], 1), steps)
-        assert plan["sys_wgs"] == -(-plan["sys_row_blocks"] * parts // 8) * 8 <= max(512, plan["sys_wgs"])
-        assert plan["sys_chunk_len"] == -(-steps // parts) * 64
+        parts = min(max(512 // row_blocks, 1), steps)
+        assert plan["sys_wgs"] == -(-row_blocks * parts // 8) * 8
         # slots: the most runs one head's steps fall into
         part_of = lambda x: ((x + 1) * parts + steps - 1) // steps - 1
         sph = steps // spec.num_kv_heads
-        assert plan["sys_chunks"] == max(part_of(h * sph + sph - 1) - part_of(h * sph) + 1
-                                         for h in range(spec.num_kv_heads))
-    # context split: 512 keys while every context fits one, else 768
-    assert plan["ctx_split_len"] == (768 if s["max_ctx"] > 512 else 512)
-    assert plan["ctx_max_splits"] == -(-s["max_ctx"] // plan["ctx_split_len"])
-    assert 0 < plan["ctx_wgs"] < 2**31 and 0 < plan["sys_wgs"] < 2**31
+        assert plan["sys_runs"] == max(part_of(h * sph + sph - 1) - part_of(h * sph) + 1
+                                       for h in range(spec.num_kv_heads))
+    R_ = int(s["q_lens"].max()) * spec.group      # query rows per (request, KV head)
+    assert plan["ctx_row_tiles"] == (1 if R_ <= 16 else 2)
+    assert plan["ctx_row_blocks"] == -(-R_ // (16 * plan["ctx_row_tiles"]))
+    assert plan["stream_waves"] == WAVES and plan["stream_launches"] == 1
+    assert plan["stream_max_requests"] == spec.batch
 
 
-@pytest.mark.parametrize("env,rows", [({}, 2), ({"RELAY_SYS_ROW_TILES": "2"}, 1),
-                                      ({"RELAY_SYS_ROW_TILES": "2", "RELAY_KEY_LANES": "8"}, 2),
-                                      ({"RELAY_CTX_SPLIT": "256"}, 2)])
-def test_plan_tuning_knobs(lib, monkeypatch, env, rows):
-    """The environment knobs the plan reads: two-tile system units on request (never with
-    eight key lanes), and the context split."""
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
-    spec = W.config_spec(2, 0)
-    s = W.expected_sizes(spec)
-    d = R.relay_dims(spec.batch, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, 16,
-                     -(-s["max_ctx"] // 16), 1000, s["total_q"], 1, s["max_ctx"], spec.scale, 1, 0)
-    plan = R.relay_get_plan(d, spec.sys_len)
-    assert plan["sys_row_blocks"] == rows          # M = 32 rows: two one-tile units or one two-tile unit
-    assert plan["ctx_split_len"] == int(env.get("RELAY_CTX_SPLIT", 512))
+def test_requests_in_groups_of_one_streaming_launch(lib):
+    """More requests than one launch's tables hold: the context streams run as several
+    launches over request groups (3968 requests each)."""
+    d = base_dims(batch=9000, total_q=9000, num_blocks=90000, max_ctx_len=100, max_blocks_per_seq=7)
+    plan = R.relay_get_plan(d, 500)
+    assert plan["sys_mode"] == 2 and plan["stream_max_requests"] == 3968
+    assert plan["stream_launches"] == 3 and plan["launches"] == 5
+    ws = R.relay_workspace_size(d, 500)
+    assert ws >= 3 * (3968 * 2 + WAVES) * 16 * 129 * 4
+
+
+def test_key_tile_layout_matches_the_header_formula():
+    """The key layout the header documents (element c of key r at ((c/G)*16 + slot(r))*G
+    + c%G, slot() read from the header text) is the layout the generator writes."""
+    text = open(HEADER).read()
+    m = re.search(r"slot\(r\) = ([\d, ]+) for\s*\n?\s*\*?\s*r = 0\.\.15", text)
+    assert m, "slot() table not found in the header"
+    slot = [int(x) for x in m.group(1).replace(" ", "").split(",") if x]
+    assert sorted(slot) == list(range(16)) and all(slot[slot[r]] == r for r in range(16))
+    rng = np.random.default_rng(5)
+    for dtype, G, d in (("bf16", 8, 128), ("f32", 4, 128), ("bf16", 8, 64), ("f32", 4, 64)):
+        tile = rng.integers(0, 60000, size=(16, d)).astype(np.uint16 if dtype == "bf16" else np.float32)
+        flat = np.empty(16 * d, tile.dtype)
+        for r in range(16):
+            for c in range(d):
+                flat[((c // G) * 16 + slot[r]) * G + c % G] = tile[r, c]
+        assert np.array_equal(W.k_tiles(tile[None], dtype).reshape(-1), flat), dtype
+        assert np.array_equal(W.k_untile(W.k_tiles(tile[None], dtype))[0], tile)
+
+
+def test_prefill_workspace_holds_only_the_system_runs(lib):
+    """The offline prefill's workspace is its causal system runs (at most a few per row),
+    not the decode plan's context partials: bounded at the long-prompt shape."""
+    L, Hq, Hkv, D = 65536, 32, 8, 128
+    d = R.relay_dims(1, Hq, Hkv, D, 16, L // 16, L // 16, L, L, L, D ** -0.5, 1, 0)
+    n = R.load_library().relay_prefill_workspace_size(ctypes.byref(d), L)
+    rows = L * Hq
+    assert 0 < n <= 4 * rows * (D + 1) * 4 + 4096
+    d2 = R.relay_dims(1, 32, 32, D, 16, 512, 512, 8192, 8192, 8192, D ** -0.5, 1, 0)
+    n2 = R.load_library().relay_prefill_workspace_size(ctypes.byref(d2), 8192)
+    assert 0 < n2 <= 8 * 8192 * 32 * (D + 1) * 4
+
+
+def meta(shape, dtype):
+    import torch
+    return torch.empty(shape, dtype=dtype, device="meta")
+
+
+def decode_args(**o):
+    """Well-formed relay_attn_decode tensors (meta: shapes and dtypes only): B 3, H_q 8,
+    H_kv 2, d 128, bf16, sys_len 40 (3 tiles), 10 pages."""
+    import torch
+    bf = torch.bfloat16
+    a = dict(q=meta((3, 8, 128), bf), sys_k=meta((2, 3, 16, 16, 8), bf), sys_v=meta((2, 3, 128, 16), bf),
+             sys_len=40, ctx_k_pages=meta((10, 2, 16, 16, 8), bf), ctx_v_pages=meta((10, 2, 128, 16), bf),
+             block_tables=meta((3, 4), torch.int32), ctx_lens=meta((3,), torch.int32), cu_q_lens=None,
+             out=meta((3, 8, 128), torch.float32), out_dtype=torch.float32)
+    a.update(o)
+    return a
+
+
+def test_binding_accepts_well_formed_decode_arguments():
+    R.check_decode_args(**decode_args())
+    import torch
+    R.check_decode_args(**decode_args(out=meta((3, 8, 128), torch.bfloat16), out_dtype=torch.bfloat16))
+    R.check_decode_args(**decode_args(sys_len=0, sys_k=meta((16,), torch.bfloat16), sys_v=meta((16,), torch.bfloat16)))
+    R.check_decode_args(**decode_args(cu_q_lens=meta((4,), torch.int32)))
+
+
+@pytest.mark.parametrize("bad,match", [
+    (dict(out="bf16"), "out dtype"),                       # bf16 buffer for a float32 output
+    (dict(out="short"), "shape"),
+    (dict(sys_len=49), "sys_k must be"),                   # longer than the cache's 3 tiles
+    (dict(sys_k="f32"), "sys_k dtype"),
+    (dict(ctx_v_pages="f32"), "ctx_v_pages dtype"),
+    (dict(ctx_v_pages="shape"), "ctx_v_pages must be"),
+    (dict(block_tables="i64"), "block_tables"),
+    (dict(ctx_lens="short"), "ctx_lens"),
+    (dict(cu_q_lens="short"), "cu_q_lens"),
+    (dict(q="rows"), "one query token"),
+])
+def test_binding_refuses_inconsistent_decode_arguments(bad, match):
+    """The C library cannot see extents: the binding refuses what would be read or written
+    out of bounds (a bf16 out with a float32 out_dtype, a sys_len past the cache, ...)."""
+    import torch
+    subst = {"bf16": meta((3, 8, 128), torch.bfloat16), "short": None, "f32": None, "shape": None,
+             "i64": meta((3, 4), torch.int64), "rows": meta((4, 8, 128), torch.bfloat16)}
+    kw = {}
+    for k, v in bad.items():
+        if k == "out" and v == "short":
+            kw[k] = meta((3, 8, 64), torch.float32)
+        elif k == "sys_k" and v == "f32":
+            kw[k] = meta((2, 3, 32, 16, 4), torch.float32)
+        elif k == "ctx_v_pages" and v == "f32":
+            kw[k] = meta((10, 2, 128, 16), torch.float32)
+        elif k == "ctx_v_pages" and v == "shape":
+            kw[k] = meta((10, 2, 16, 128), torch.bfloat16)
+        elif k == "ctx_lens":
+            kw[k] = meta((2,), torch.int32)
+        elif k == "cu_q_lens":
+            kw[k] = meta((3,), torch.int32)
+        elif k == "sys_len":
+            kw[k] = v
+        else:
+            kw[k] = subst[v]
+    with pytest.raises(ValueError, match=match):
+        R.check_decode_args(**decode_args(**kw))
 
 
 def test_validate_accepts_generated_workloads_and_rejects_bad_data(lib):
@@ -219,7 +321,7 @@ def test_prefill_entry_rejects_what_it_does_not_run(lib):
     assert call(base_dims(**big), out_dtype=5) == -2
     d = base_dims(**big)
     need = lib.relay_prefill_workspace_size(ctypes.byref(d), 300)
-    assert need >= lib.relay_workspace_size(ctypes.byref(d), 300) > 0
+    assert need > 0
     assert call(d, n=need - 1) == -3
 
 

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from shared_prompt_kv_amd import baseline, relay as R
-from shared_prompt_kv_amd import workloads as W
+import workloads as W
 
 SPECS = [
     W.config_spec(2).replace(batch=3, sys_len=48, ctx_lo=5, ctx_hi=40),

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from shared_prompt_kv_amd import baseline, relay as R
-from shared_prompt_kv_amd import workloads as W
+import workloads as W
 from tests.test_parity_gpu import check, say
 
 pytestmark = pytest.mark.gpu

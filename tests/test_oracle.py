@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 import torch
 
-from shared_prompt_kv_amd import workloads as W
+import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 

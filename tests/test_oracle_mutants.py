@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
-from shared_prompt_kv_amd import workloads as W
+import workloads as W
 from tests.test_oracle import (_hand_workload, brute_attention, dense_rows, sdpa_reference,
                                tiny_spec, GOLDEN)
 

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from shared_prompt_kv_amd import relay as R
-from shared_prompt_kv_amd import workloads as W
+import workloads as W
 
 pytestmark = pytest.mark.gpu
 
@@ -82,6 +82,18 @@ SMALL = [
                                 sys_len=12000, ctx_lo=40, ctx_hi=40),
     W.config_spec(1).replace(name="c1-two-tile-f32", batch=20, num_q_heads=24, num_kv_heads=24,
                              sys_len=8200, ctx_lo=1, ctx_hi=40),
+    # a single request (one stacked row per KV head), MHA and GQA
+    W.config_spec(2).replace(name="c2-B1", batch=1),
+    W.config_spec(4).replace(name="c4-B1", batch=1, sys_len=3000),
+    # 33..64 stacked rows: system streams of four row tiles
+    W.config_spec(2).replace(name="c2-B48", batch=48, sys_len=700, ctx_lo=16, ctx_hi=200),
+    # more than 64 stacked rows per KV head at head_dim 64 or fp32: the tiled system kernel
+    W.config_spec(4).replace(name="c4-d64-bf16", head_dim=64, batch=20, sys_len=333, ctx_median=60, ctx_cap=200),
+    W.config_spec(4).replace(name="c4-d64-f32", dtype="f32", head_dim=64, batch=20, sys_len=333,
+                             ctx_median=60, ctx_cap=200),
+    W.config_spec(4).replace(name="c4-d128-f32", dtype="f32", batch=20, sys_len=150, ctx_median=40, ctx_cap=100),
+    # MHA with more than 64 stacked rows (g = 1): the matrix-core system kernel at batch 128
+    W.config_spec(2).replace(name="c2-B128", batch=128),
 ]
 SMALL_IDS = [f"{s.name}-B{s.batch}-L{s.sys_len}-d{s.head_dim}" for s in SMALL]
 
@@ -235,9 +247,11 @@ def test_bf16_output():
 
 
 # ------------------------------------------------------------------------------------------
-# full configuration sizes (sampled rows where the oracle would take minutes)
+# full configuration sizes: every row, except the long-prompt multi-token workload (about
+# 40 s of oracle per row block of rows), where 2000 sampled rows are checked
 
-FULL = [(1, 0, None), (2, 0, None), (3, 0, None), (3, 5, 400), (4, 0, 600), (5, 0, 160)]
+FULL = [(1, 0, None), (2, 0, None)] + [(3, i, None) for i in range(len(W.CONFIG3_SYS_LENS))] + \
+    [(4, 0, None), (5, 0, 2000)]
 
 
 @pytest.mark.parametrize("cfg,sweep,n_rows", FULL, ids=[f"c{c}s{s}" for c, s, _ in FULL])
@@ -319,23 +333,76 @@ def test_multi_split_shapes(spec):
     check(a.numpy(), expect, spec.dtype, "multi-split")
 
 
-@pytest.mark.parametrize("parts", [1, 3, 7, 13])
-def test_system_runs_across_heads(parts, monkeypatch):
-    """Matrix-core system step with its key runs forced to cross KV-head boundaries
-    (each run one partial per head it touches, unused slots empty)."""
-    spec = W.config_spec(5).replace(batch=5, sys_len=290, ctx_lo=64, ctx_hi=300)
-    monkeypatch.setenv("RELAY_SYS_PARTS", str(parts))
-    say(f"[parity] system runs across heads, parts={parts} {spec}")
+# shapes whose matrix-core system runs cross KV-head boundaries: (batch, sys_len); 1 query
+# token per request, 32 / 8 heads, so M = 4 B stacked rows per KV head in ceil(M / 128) row
+# blocks and 512 // row_blocks runs over the 8 heads' 64-key steps
+CROSSING = [(75, 1920), (150, 2560), (200, 1000)]
+
+
+def _runs_cross_heads(batch, sys_len, hkv=8, g=4):
+    rb = -(-batch * g // 128)
+    sph = -(-sys_len // 64)
+    S = hkv * sph
+    parts = min(max(512 // rb, 1), S)
+    return any((p * S // parts) % sph for p in range(1, parts))
+
+
+@pytest.mark.parametrize("batch,sys_len", CROSSING, ids=[f"B{b}-L{l}" for b, l in CROSSING])
+def test_system_runs_across_heads(batch, sys_len):
+    """Matrix-core system step whose key runs cross KV-head boundaries (each run one
+    partial per head it touches, unused slots empty), step alone and whole decode."""
+    assert _runs_cross_heads(batch, sys_len)
+    spec = W.config_spec(4).replace(batch=batch, sys_len=sys_len, ctx_median=60, ctx_cap=300)
+    say(f"[parity] system runs across heads {spec}")
     w = workload(spec)
     t = upload(w)
     plan = R.relay_get_plan(R.dims_of(t), t["sys_len"])
-    assert plan["sys_mode"] == 2
+    assert plan["sys_mode"] == 2 and plan["sys_runs"] >= 2
     o, lse = R.relay_sys_attn(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], R.dims_of(t))
     out = R.decode_workload(t)
     torch.cuda.synchronize()
-    ro, rl = oracle.Problem(w).system_part()
+    P = oracle.Problem(w)
+    ro, rl = P.system_part()
     check(o.cpu().numpy(), ro, spec.dtype, "o_sys")
     check(lse.cpu().numpy(), rl, spec.dtype, "lse_sys")
+    ref, _ = P.attention()
+    check(out.cpu().numpy(), ref, spec.dtype, "out")
+
+
+def test_steps_full_size_gqa():
+    """System step and context step alone at the full Llama-3-8B GQA size (256 requests,
+    8192 system keys, lognormal contexts): every row against the oracle's parts."""
+    spec = W.config_spec(4)
+    say(f"[parity] per-step full size {spec}")
+    w = W.generate(spec)
+    t = upload(w)
+    dims = R.dims_of(t)
+    o_s, l_s = R.relay_sys_attn(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], dims)
+    o_c, l_c = R.relay_ctx_attn(t["q"], t["ctx_k_pages"], t["ctx_v_pages"], t["block_tables"], t["ctx_lens"],
+                                t["cu_q_lens"], dims)
+    torch.cuda.synchronize()
+    P = oracle.Problem(w)
+    ro, rl = P.system_part()
+    check(o_s.cpu().numpy(), ro, spec.dtype, "o_sys")
+    check(l_s.cpu().numpy(), rl, spec.dtype, "lse_sys")
+    ro, rl = P.context_part()
+    check(o_c.cpu().numpy(), ro, spec.dtype, "o_ctx")
+    check(l_c.cpu().numpy(), rl, spec.dtype, "lse_ctx")
+    del t
+    torch.cuda.empty_cache()
+
+
+def test_many_requests_in_several_streaming_launches():
+    """More requests than one streaming launch takes (3968): the context streams run as
+    several launches over request groups; every row against the oracle."""
+    spec = W.config_spec(4).replace(name="c4-B4100", batch=4100, sys_len=100, ctx_median=20, ctx_cap=40)
+    say(f"[parity] request groups {spec}")
+    w = workload(spec)
+    t = upload(w)
+    plan = R.relay_get_plan(R.dims_of(t), t["sys_len"])
+    assert plan["stream_launches"] == 2
+    out = R.decode_workload(t)
+    torch.cuda.synchronize()
     ref, _ = oracle.Problem(w).attention()
     check(out.cpu().numpy(), ref, spec.dtype, "out")
 

@@ -9,7 +9,7 @@ import torch
 
 from oracle import rope
 from shared_prompt_kv_amd import prefill, relay as R
-from shared_prompt_kv_amd import workloads as W
+import workloads as W
 from tests.test_parity_gpu import check, say
 from tests.test_rope_gpu import assert_stored_close, upload
 

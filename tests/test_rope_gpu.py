@@ -11,7 +11,7 @@ import torch
 
 from oracle import Problem, rope
 from shared_prompt_kv_amd import relay as R
-from shared_prompt_kv_amd import workloads as W
+import workloads as W
 from tests.test_parity_gpu import check, say
 
 pytestmark = pytest.mark.gpu

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from oracle import rope, Problem
-from shared_prompt_kv_amd import workloads as W
+import workloads as W
 
 
 def rng(seed=0):

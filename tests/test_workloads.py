@@ -5,7 +5,7 @@ import os
 import numpy as np
 import pytest
 
-from shared_prompt_kv_amd import workloads as W
+import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
