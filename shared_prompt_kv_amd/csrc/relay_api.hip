@@ -178,9 +178,6 @@ int make_plan(const relay_dims* d, int32_t sys_len, Plan* p, Need need = kDecode
     p->launches = 2;
     return RELAY_OK;
   }
-  const int cus = device_cus();
-  p->grid = cus;
-  p->workers = cus * relay::kStreamWaves;
   // ---- system step
   if (sys_len > 0) {
     if (M <= relay::kStreamSysMaxRows) {
@@ -188,7 +185,6 @@ int make_plan(const relay_dims* d, int32_t sys_len, Plan* p, Need need = kDecode
       const int tiles = ceil_div(M, 16);
       p->rts = tiles <= 2 ? tiles : 4;
       p->sys_steps = ceil_div(sys_len, 32);
-      p->sys_slots = (long long)d->num_kv_heads + p->workers;
     } else {
       plan_system_kernel(d, sys_len, M, p);
     }
@@ -198,6 +194,10 @@ int make_plan(const relay_dims* d, int32_t sys_len, Plan* p, Need need = kDecode
   const long long R = (long long)d->max_q_len * g;
   p->rtc = relay::ctx_rt_for((int)R);
   p->ctx_rb = ceil_div(R, 16 * p->rtc);
+  // one or two workgroups per CU (what the launch's instantiation is built for)
+  p->grid = relay::stream_grid(device_cus(), d->in_dtype == RELAY_BF16 ? 2 : 4, D, p->rts, p->rtc);
+  p->workers = p->grid * relay::kStreamWaves;
+  if (p->sys_mode == 1) p->sys_slots = (long long)d->num_kv_heads + p->grid;
   const int cap = d->max_ctx_len < d->max_blocks_per_seq * 16 ? d->max_ctx_len : d->max_blocks_per_seq * 16;
   const long long per_req = (long long)ceil_div(cap, 32) * d->num_kv_heads * p->ctx_rb;
   long long chunk = relay::kStreamMaxRequests;

@@ -51,8 +51,25 @@ inline SysConfig sys_config(int) { return {2, 1, 4}; }
 
 // stream_attn (stream_attn.hip): the system and context steps as one launch of equal
 // contiguous step ranges, one per wave.
-constexpr int kStreamWaves = 4;          // waves per workgroup, one workgroup per CU
-constexpr int kStreamMaxRequests = 3968; // requests per streaming launch: 4 LDS tables + scan <= 64 KiB
+constexpr int kStreamWaves = 4;  // waves per workgroup
+
+// Workgroups per CU a streaming instantiation is built for: two (two waves per SIMD,
+// so one wave's arithmetic hides under the other's loads) wherever its registers fit
+// 256 without spilling, else one.
+constexpr int stream_wgs_per_cu(int elem_bytes, int head_dim, int rts, int rtc) {
+  if (elem_bytes == 2) return (head_dim == 128 && rts == 4) ? 1 : 2;
+  if (head_dim == 128) return (rts >= 2 || rtc == 2) ? 1 : 2;
+  return rts == 4 ? 1 : 2;
+}
+
+// LDS of the system pieces' four-wave merge: two waves' states of one 16-row tile.
+constexpr int stream_merge_lds_bytes(int head_dim) { return 2 * 64 * (2 + head_dim / 4) * 4; }
+
+// Requests per streaming launch: their four LDS tables, the scan scratch and the merge
+// area fit 64 KiB.
+constexpr int kStreamMaxRequests = 2880;
+static_assert(((4 * (4 * kStreamMaxRequests + 1 + 256) + 15) / 16) * 16 + stream_merge_lds_bytes(128) <= 65536,
+              "streaming LDS over 64 KiB");
 
 struct StreamArgs {
   const void* q;       // [T_q, H_q, d]
@@ -67,7 +84,7 @@ struct StreamArgs {
   int sys_len;
   int sys_steps;       // ceil(L_s / 32)
   int M;               // stacked rows per KV head (T_q * g)
-  float* sys_o;        // [H_kv + n_workers slots][16 RTS rows][d]
+  float* sys_o;        // [H_kv + workgroups slots][16 RTS rows][d]
   float* sys_lse;      // [slots][16 RTS]
   int* sys_desc;       // [H_kv][2]: first slot, number of pieces
   // context streams (request, KV head, row block) of requests [b_begin, b_begin + n_req)
@@ -91,7 +108,12 @@ struct StreamArgs {
   int n_workers;       // waves of the launch (grid * kStreamWaves)
 };
 
-size_t stream_lds_bytes(int n_req, int ctx_on);
+// Workgroups of one streaming launch for this instantiation on a device with `cus` CUs.
+inline int stream_grid(int cus, int elem_bytes, int head_dim, int rts, int rtc) {
+  return cus * stream_wgs_per_cu(elem_bytes, head_dim, rts, rtc);
+}
+
+size_t stream_lds_bytes(int n_req, int ctx_on, int sys_on, int head_dim);
 hipError_t launch_stream_attn(const StreamArgs& a, int rts, int rtc, int in_dtype, int head_dim, int grid,
                               hipStream_t stream);
 

@@ -14,21 +14,25 @@
 //     of b sits at context position c_b - n_b + t).
 //
 // System streams come first, then the context streams in (request, head, row block)
-// order.  With T steps in all and W waves in the launch, wave v streams the contiguous
+// order.  With T steps in all and W waves in the launch, wave v owns the contiguous
 // steps [v T / W, (v + 1) T / W) (W = min(waves, T), so no range is empty): every wave
-// moves the same number of K/V bytes, and it
-// keeps two steps in flight from the first step of its range to the last, across the
-// boundaries between streams.  (One workgroup of four waves per CU, one wave per SIMD:
-// each wave can hold two steps, its query rows and its accumulators in registers.)
+// moves the same number of K/V bytes.  The system steps owned by the four waves of a
+// workgroup form one contiguous range, which the four stream together (wave k takes
+// every fourth step from the k-th) and merge through LDS at the end of each KV head's
+// part, so a system piece belongs to a workgroup, not a wave: four times fewer system
+// partials to write and to merge.  Each wave then streams the context steps of its own
+// range, with its next steps in flight across the boundaries between streams.  Two
+// workgroups share a CU where the registers allow (two waves per SIMD).
 //
-// The part of a stream that one wave processes is a piece; each piece writes one
-// partial (O normalised by its own sum, and its log-sum-exp) for the stream's rows
-// into slot (stream id + v) of the partial array.  Pieces are ordered like their
-// streams, so these slots are distinct.  The wave holding a stream's first step also
-// writes where the stream's pieces are (first slot and count), per KV head for system
-// streams and per output row for context streams; the merge (relay_fuse.hip) reads those
-// and combines the pieces of a row with the same log-sum-exp identity that relay fusion
-// uses.
+// The part of a context stream that one wave processes is a piece, and so is the part
+// of a system stream that one workgroup processes; each piece writes one partial (O
+// normalised by its own sum, and its log-sum-exp) for the stream's rows, into slot
+// (stream id + v) of the context partials (v the wave) or slot (h + w) of the system
+// partials (w the workgroup).  Pieces are ordered like their streams, so these slots
+// are distinct.  The holder of a stream's first step also writes where the stream's
+// pieces are (first slot and count), per KV head for system streams and per output row
+// for context streams; the merge (relay_fuse.hip) reads those and combines the pieces
+// of a row with the same log-sum-exp identity that relay fusion uses.
 #include "relay_device.hpp"
 #include "relay_internal.hpp"
 
@@ -53,12 +57,13 @@ __device__ __forceinline__ int part_of64(long long x, long long total, int parts
 // second product costs matrix-core time that hides under the memory stream.
 constexpr bool kStreamPSplit = true;
 
-// Steps held in registers at once: two for bf16 with up to two row tiles (the next
-// step's loads are in flight while one computes), else one (fp32 steps are twice the
-// bytes; four row tiles of queries and accumulators leave no room for a second step).
-template <typename T, int RT>
+// Steps held in registers at once: two for bf16 with one row tile, or two row tiles
+// at one workgroup per CU (the next step's loads are in flight while one computes),
+// else one (fp32 steps are twice the bytes; more row tiles of queries and accumulators
+// leave no room for a second step within the registers of the occupancy).
+template <typename T, int RT, int OCC>
 constexpr int stream_depth_of() {
-  return (Elem<T>::kBytes == 2 && RT <= 2) ? 2 : 1;
+  return (Elem<T>::kBytes == 2 && (RT <= 1 || (OCC == 1 && RT <= 2))) ? 2 : 1;
 }
 
 // ---- per-launch request tables (LDS) --------------------------------------------------
@@ -122,11 +127,12 @@ __device__ void build_tables(const StreamArgs& a, const ReqTables& t, int* scrat
 
 // ---- one stream, one piece: depth-pipelined steps with fixed addresses ---------------
 
-// Streams steps 0 .. nsteps - 1 (addr(s) gives step s's tiles); DEPTH steps in flight.
+// Streams steps 0 .. nsteps - 1 (addr(s) gives step s's tiles, whose first key is
+// key0 + s * key_stride); DEPTH steps in flight.
 template <typename T, int D, int RT, bool PSPLIT, int DEPTH, class Addr>
 __device__ __forceinline__ void run_steps(int nsteps, const u32x4 (&qf)[RT][StepK<T, D>::NCH], RowState<D> (&st_)[RT],
-                                          int key0, int kv_len, const int (&last)[RT], float scale_log2,
-                                          Addr&& addr) {
+                                          int key0, int key_stride, int kv_len, const int (&last)[RT],
+                                          float scale_log2, Addr&& addr) {
   const int q4 = lane_id() >> 4;
   auto issue = [&](StepK<T, D>& k, StepV<T, D>& v, int s) {
     const StepAddr ad = addr(s);
@@ -134,7 +140,7 @@ __device__ __forceinline__ void run_steps(int nsteps, const u32x4 (&qf)[RT][Step
     issue_v(v, ad.va, ad.vb);
   };
   auto run = [&](StepK<T, D>& k, StepV<T, D>& v, int s) {
-    const int keyq = key0 + kStep * s + 8 * q4;
+    const int keyq = key0 + key_stride * s + 8 * q4;
     PStep<T> p[RT];
     step_scores<T, D, RT, PSPLIT>(k, qf, st_, keyq, kv_len, last, scale_log2, p);
     step_pv<T, D, RT, PSPLIT>(v, keyq, kv_len, st_, p);
@@ -161,7 +167,7 @@ __device__ __forceinline__ void run_steps(int nsteps, const u32x4 (&qf)[RT][Step
     StepV<T, D> v;
     issue(k, v, 0);
     for (int s = 0; s < nsteps; ++s) {
-      const int keyq = key0 + kStep * s + 8 * q4;
+      const int keyq = key0 + key_stride * s + 8 * q4;
       PStep<T> p[RT];
       step_scores<T, D, RT, PSPLIT>(k, qf, st_, keyq, kv_len, last, scale_log2, p);
       StepAddr ad;
@@ -175,9 +181,13 @@ __device__ __forceinline__ void run_steps(int nsteps, const u32x4 (&qf)[RT][Step
   }
 }
 
-// System piece: steps [j0, j1) of KV head h's stream, all M stacked rows (RTS tiles).
-template <typename T, int D, int RTS>
-__device__ void system_piece(const StreamArgs& a, int h, int j0, int j1, int v, long long total, int W) {
+// System piece: steps [j0, j1) of KV head h's stream, all M stacked rows (RTS tiles),
+// streamed by the four waves of workgroup w (wave k takes steps j0 + k, j0 + k + 4, ...)
+// and merged through LDS (mlds: stream_merge_lds_bytes of this workgroup).  Every wave
+// of the workgroup calls it with the same arguments (it holds barriers).
+template <typename T, int D, int RTS, int OCC>
+__device__ void system_piece(const StreamArgs& a, int h, int j0, int j1, int w, int wk, long long total, int W,
+                             float* mlds) {
   constexpr int E = Elem<T>::kBytes;
   const int lane = lane_id(), r16 = lane & 15;
   u32x4 qf[RTS][StepK<T, D>::NCH];
@@ -193,15 +203,16 @@ __device__ void system_piece(const StreamArgs& a, int h, int j0, int j1, int v, 
     last[rt] = a.sys_len - 1;
   }
   const int Ls = a.sys_len;
-  const int key_begin = j0 * kStep;
   const int key_end = min(j1 * kStep, Ls);
   const int ntile = (Ls + kTile - 1) / kTile;
   const char* kbase = static_cast<const char*>(a.sys_k) + (size_t)h * ntile * kTile * D * E;
   const char* vbase = static_cast<const char*>(a.sys_v) + (size_t)h * ntile * D * kTile * E;
-  // step s: system tiles key_begin / 16 + 2 s and + 1 (a tile past the prompt's end
-  // repeats the previous one; its keys are masked)
+  // this wave's steps: j0 + wk + 4 s; step j covers system tiles 2 j and 2 j + 1 (a tile
+  // past the prompt's end repeats the previous one; its keys are masked)
+  const int mine = j1 - j0 > wk ? (j1 - j0 - wk + strm::kWaves - 1) / strm::kWaves : 0;
+  const int key0 = (j0 + wk) * kStep;
   auto addr = [&](int s) {
-    const int ka = key_begin + kStep * s;
+    const int ka = key0 + strm::kWaves * kStep * s;
     const int kb = ka + kTile < Ls ? ka + kTile : ka;
     StepAddr r;
     r.ka = kbase + (size_t)(ka / kTile) * kTile * D * E;
@@ -210,10 +221,16 @@ __device__ void system_piece(const StreamArgs& a, int h, int j0, int j1, int v, 
     r.vb = vbase + (size_t)(kb / kTile) * D * kTile * E;
     return r;
   };
-  constexpr int DEPTH = stream_depth_of<T, RTS>();
-  run_steps<T, D, RTS, kStreamPSplit, DEPTH>(j1 - j0, qf, rs, key_begin, key_end, last, a.scale_log2, addr);
+  constexpr int DEPTH = stream_depth_of<T, RTS, OCC>();
+  run_steps<T, D, RTS, kStreamPSplit, DEPTH>(mine, qf, rs, key0, strm::kWaves * kStep, key_end, last, a.scale_log2,
+                                              addr);
+  // the four waves' states, one row tile at a time (fixed tree order: deterministic)
+#pragma unroll
+  for (int rt = 0; rt < RTS; ++rt)
+    merge_key_lanes<D, 1, strm::kWaves>(*reinterpret_cast<RowState<D>(*)[1]>(&rs[rt]), wk, mlds);
+  if (wk != 0) return;
 
-  const int slot = h + v;
+  const int slot = h + w;
 #pragma unroll
   for (int rt = 0; rt < RTS; ++rt) {
     const int m = rt * 16 + r16;
@@ -227,9 +244,10 @@ __device__ void system_piece(const StreamArgs& a, int h, int j0, int j1, int v, 
     store_row_tile(rs[rt], orow, lrow);
   }
   if (j0 == 0 && lane == 0) {
+    // the workgroup holding the stream's last step: the wave holding it, over four
     const long long p0 = (long long)h * a.sys_steps;
     a.sys_desc[2 * h] = slot;
-    a.sys_desc[2 * h + 1] = part_of64(p0 + a.sys_steps - 1, total, W) - v + 1;
+    a.sys_desc[2 * h + 1] = part_of64(p0 + a.sys_steps - 1, total, W) / strm::kWaves - w + 1;
   }
 }
 
@@ -292,11 +310,11 @@ struct CtxPiece {
   int i, h, rb, j0, c, qs, nq;
 };
 
-template <typename T, int D, int RTC>
+template <typename T, int D, int RTC, int OCC>
 __device__ void context_range(const StreamArgs& a, const ReqTables& t, long long y0, long long y1, long long Ts,
                               int v, long long total, int W) {
   constexpr int E = Elem<T>::kBytes;
-  constexpr int DEPTH = stream_depth_of<T, RTC>();
+  constexpr int DEPTH = stream_depth_of<T, RTC, OCC>();
   constexpr int RPB = 16 * RTC;  // rows per block
   const int lane = lane_id(), q4 = lane >> 4, r16 = lane & 15;
   const size_t page_stride = (size_t)a.num_kv_heads * kTile * D * E;
@@ -422,7 +440,20 @@ __device__ void context_range(const StreamArgs& a, const ReqTables& t, long long
 // ---- the kernel ---------------------------------------------------------------------------
 
 template <typename T, int D, int RTS, int RTC>
-__global__ __launch_bounds__(kWave* strm::kWaves, 1) void stream_attn_kernel(StreamArgs a) {
+constexpr int stream_occ() {
+  return stream_wgs_per_cu(Elem<T>::kBytes, D, RTS, RTC);
+}
+
+// LDS of one workgroup: the request tables (4 n + 1 ints), the scan scratch (one int per
+// thread), then, 16-byte aligned, the system pieces' merge area.
+__host__ __device__ constexpr size_t stream_tables_bytes(int n) {
+  return (sizeof(int) * ((size_t)4 * n + 1 + (size_t)kWave * kStreamWaves) + 15) / 16 * 16;
+}
+
+template <typename T, int D, int RTS, int RTC>
+__global__ __launch_bounds__(kWave* strm::kWaves, (stream_occ<T, D, RTS, RTC>())) void stream_attn_kernel(
+    StreamArgs a) {
+  constexpr int OCC = stream_occ<T, D, RTS, RTC>();
   extern __shared__ int lds_tab[];
   const int n = a.ctx_on ? a.n_req : 0;
   ReqTables t{lds_tab, lds_tab + n + 1, lds_tab + 2 * n + 1, lds_tab + 3 * n + 1};
@@ -435,36 +466,43 @@ __global__ __launch_bounds__(kWave* strm::kWaves, 1) void stream_attn_kernel(Str
   const long long total = Ts + Tc;
   // with fewer steps than waves only the first `total` waves take part (one step each),
   // so that every wave of the partition holds at least one step and the pieces of a
-  // stream sit on consecutive waves
+  // stream sit on consecutive waves (and workgroups)
   const int W = total < a.n_workers ? (int)total : a.n_workers;
-  const int v = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * strm::kWaves + threadIdx.x / kWave));
-  if (total == 0 || v >= W) return;
-  const long long x0 = (long long)v * total / W, x1 = (long long)(v + 1) * total / W;
+  const int w = blockIdx.x;
+  const int wk = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int v = w * strm::kWaves + wk;
+  if (total == 0 || w * strm::kWaves >= W) return;  // uniform over the workgroup
   if constexpr (RTS > 0) {
-    long long x = x0;
-    const long long xs1 = x1 < Ts ? x1 : Ts;
+    // the system steps of the workgroup's waves (all four take part, also a wave past W)
+    const int vl = min(w * strm::kWaves + strm::kWaves - 1, W - 1);
+    long long x = (long long)w * strm::kWaves * total / W;
+    const long long X1 = (long long)(vl + 1) * total / W;
+    const long long xs1 = X1 < Ts ? X1 : Ts;
+    float* mlds = reinterpret_cast<float*>(reinterpret_cast<char*>(lds_tab) + stream_tables_bytes(n));
     while (x < xs1) {
       const int h = (int)(x / a.sys_steps);
       const int j0 = (int)(x - (long long)h * a.sys_steps);
       const int j1 = (int)((long long)j0 + (xs1 - x) < a.sys_steps ? j0 + (xs1 - x) : a.sys_steps);
-      system_piece<T, D, RTS>(a, h, j0, j1, v, total, W);
+      system_piece<T, D, RTS, OCC>(a, h, j0, j1, w, wk, total, W, mlds);
       x += j1 - j0;
     }
   }
+  if (v >= W) return;
+  const long long x0 = (long long)v * total / W, x1 = (long long)(v + 1) * total / W;
   if (a.ctx_on && x1 > Ts) {
     const long long y0 = (x0 > Ts ? x0 : Ts) - Ts, y1 = x1 - Ts;
-    context_range<T, D, RTC>(a, t, y0, y1, Ts, v, total, W);
+    context_range<T, D, RTC, OCC>(a, t, y0, y1, Ts, v, total, W);
   }
 }
 
-size_t stream_lds_bytes(int n_req, int ctx_on) {
+size_t stream_lds_bytes(int n_req, int ctx_on, int sys_on, int head_dim) {
   const int n = ctx_on ? n_req : 0;
-  return sizeof(int) * ((size_t)4 * n + 1 + (size_t)kWave * strm::kWaves);
+  return stream_tables_bytes(n) + (sys_on ? (size_t)stream_merge_lds_bytes(head_dim) : 0);
 }
 
 template <typename T, int D, int RTS, int RTC>
 static hipError_t launch_stream_t(const StreamArgs& a, int grid, hipStream_t s) {
-  const size_t lds = stream_lds_bytes(a.n_req, a.ctx_on);
+  const size_t lds = stream_lds_bytes(a.n_req, a.ctx_on, RTS > 0, D);
   hipLaunchKernelGGL((stream_attn_kernel<T, D, RTS, RTC>), dim3(grid), dim3(kWave * strm::kWaves), lds, s, a);
   return hipGetLastError();
 }

@@ -108,7 +108,18 @@ def test_pointer_and_workspace_errors(lib):
 
 
 CUS = 256          # no GPU here: the library plans for 256 compute units
-WAVES = 4 * CUS    # one four-wave workgroup per compute unit
+
+
+def stream_grid(bf16, D, rts, rtc):
+    """Workgroups of a streaming launch: two per CU where the instantiation's registers
+    fit two waves per SIMD (the header's plan contract), else one."""
+    if bf16:
+        per_cu = 1 if (D == 128 and rts == 4) else 2
+    elif D == 128:
+        per_cu = 1 if (rts >= 2 or rtc == 2) else 2
+    else:
+        per_cu = 1 if rts == 4 else 2
+    return CUS * per_cu
 
 
 def a256(x):
@@ -117,21 +128,23 @@ def a256(x):
 
 def test_workspace_covers_the_plan(lib):
     """Workspace = the partial regions of the streaming launch, laid out as the header says:
-    system pieces (H_kv + waves slots of 16 * sys_row_tiles rows), their descriptors,
+    system pieces (H_kv + workgroups slots of 16 * sys_row_tiles rows), their descriptors,
     context pieces (B H_kv row_blocks + waves slots per request group) and row descriptors."""
     d = base_dims()               # B 4, H_q 8 / H_kv 2 -> M = 16 stacked rows per KV head
     plan = R.relay_get_plan(d, 1000)
     assert plan["sys_mode"] == 1 and plan["sys_row_tiles"] == 1
     assert plan["ctx_row_tiles"] == 1 and plan["ctx_row_blocks"] == 1
-    assert plan["stream_waves"] == WAVES and plan["stream_launches"] == 1 and plan["launches"] == 2
+    grid = stream_grid(True, 128, 1, 1)
+    assert plan["stream_waves"] == 4 * grid and plan["stream_launches"] == 1 and plan["launches"] == 2
     rows, D, H = 4 * 8, 128, 2
-    sys_slots, ctx_slots = H + WAVES, 4 * H * 1 + WAVES
+    sys_slots, ctx_slots = H + grid, 4 * H * 1 + 4 * grid
     expect = (a256(sys_slots * 16 * D * 4) + a256(sys_slots * 16 * 4) + a256(H * 2 * 4)
               + a256(ctx_slots * 16 * D * 4) + a256(ctx_slots * 16 * 4) + a256(rows * 16))
     assert R.relay_workspace_size(d, 1000) == expect
     p0 = R.relay_get_plan(d, 0)
     assert p0["sys_mode"] == 0 and p0["launches"] == 2
-    assert R.relay_workspace_size(d, 0) == expect - a256(sys_slots * 16 * D * 4) - a256(sys_slots * 16 * 4) - a256(H * 8)
+    ctx0 = 4 * H + 4 * stream_grid(True, 128, 0, 1)
+    assert R.relay_workspace_size(d, 0) == (a256(ctx0 * 16 * D * 4) + a256(ctx0 * 16 * 4) + a256(rows * 16))
 
 
 @pytest.mark.parametrize("cfg,sweep", [(1, 0), (2, 0), (3, 0), (3, 5), (4, 0), (5, 0)])
@@ -162,19 +175,21 @@ def test_plan_for_each_config(lib, cfg, sweep):
     R_ = int(s["q_lens"].max()) * spec.group      # query rows per (request, KV head)
     assert plan["ctx_row_tiles"] == (1 if R_ <= 16 else 2)
     assert plan["ctx_row_blocks"] == -(-R_ // (16 * plan["ctx_row_tiles"]))
-    assert plan["stream_waves"] == WAVES and plan["stream_launches"] == 1
+    rts = plan["sys_row_tiles"] if plan["sys_mode"] == 1 else 0
+    grid = stream_grid(spec.dtype == "bf16", spec.head_dim, rts, plan["ctx_row_tiles"])
+    assert plan["stream_waves"] == 4 * grid and plan["stream_launches"] == 1
     assert plan["stream_max_requests"] == spec.batch
 
 
 def test_requests_in_groups_of_one_streaming_launch(lib):
     """More requests than one launch's tables hold: the context streams run as several
-    launches over request groups (3968 requests each)."""
+    launches over request groups (2880 requests each)."""
     d = base_dims(batch=9000, total_q=9000, num_blocks=90000, max_ctx_len=100, max_blocks_per_seq=7)
     plan = R.relay_get_plan(d, 500)
-    assert plan["sys_mode"] == 2 and plan["stream_max_requests"] == 3968
-    assert plan["stream_launches"] == 3 and plan["launches"] == 5
+    assert plan["sys_mode"] == 2 and plan["stream_max_requests"] == 2880
+    assert plan["stream_launches"] == 4 and plan["launches"] == 6
     ws = R.relay_workspace_size(d, 500)
-    assert ws >= 3 * (3968 * 2 + WAVES) * 16 * 129 * 4
+    assert ws >= 4 * (2880 * 2 + 4 * stream_grid(True, 128, 0, 1)) * 16 * 129 * 4
 
 
 def test_key_tile_layout_matches_the_header_formula():

@@ -393,7 +393,7 @@ def test_steps_full_size_gqa():
 
 
 def test_many_requests_in_several_streaming_launches():
-    """More requests than one streaming launch takes (3968): the context streams run as
+    """More requests than one streaming launch takes (2880): the context streams run as
     several launches over request groups; every row against the oracle."""
     spec = W.config_spec(4).replace(name="c4-B4100", batch=4100, sys_len=100, ctx_median=20, ctx_cap=40)
     say(f"[parity] request groups {spec}")
