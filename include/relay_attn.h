@@ -199,6 +199,25 @@ int relay_attn_decode_timed(const relay_dims* dims, const void* q, const void* s
                             void* const* events);
 
 /*
+ * relay_attn_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): identical
+ * arguments and results, minus the workspace.  Its workspace is a static array of
+ * RELAY_NOALLOC_SCRATCH_BYTES per device, held by the loaded library until the process
+ * ends; nothing is allocated or freed, and no part of the array needs to start at
+ * zero.  Every call on one device shares that device's array, which keeps the last
+ * call's contents: calls that overlap on one device (other streams, other threads)
+ * race and must be serialised by the caller.  Returns RELAY_ERR_WORKSPACE when
+ * relay_workspace_size(dims, sys_len) exceeds RELAY_NOALLOC_SCRATCH_BYTES; errors
+ * otherwise as relay_attn_decode.
+ */
+#define RELAY_NOALLOC_SCRATCH_BYTES (128u << 20)
+int relay_attn_decode_noalloc(const relay_dims* dims, const void* q, const void* sys_k,
+                              const void* sys_v, int32_t sys_len, const void* ctx_k_pages,
+                              const void* ctx_v_pages, const int32_t* block_tables,
+                              const int32_t* ctx_lens, const int32_t* cu_q_lens, void* out,
+                              void* stream);
+
+/*
  * System-attention step alone (RelayAttention's first step): for every query row,
  * attention over the system keys only.  o_sys: float32 [T_q, H_q, d]; lse_sys:
  * float32 [T_q, H_q].  sys_len == 0 gives o_sys = 0 and lse_sys = -inf.  Enqueues

@@ -389,6 +389,41 @@ int check_q_layout(const relay_dims* d, const int32_t* cu) {
   return RELAY_OK;
 }
 
+// ---- the allocation-free decode's scratch --------------------------------------------
+//
+// The workspace of relay_attn_decode_noalloc: one array per device, part of the loaded
+// code object (each device the library runs on holds its own copy until the process
+// ends).  Host code never uses the array's name as an address: the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+static_assert(RELAY_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) char scratch[RELAY_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// This device's scratch address, or nullptr (and the error recorded) on failure.
+void* scratch_ptr() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    hip_fail(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(RELAY_ERR_UNSUPPORTED, "device %d: the allocation-free path serves devices 0..%d", dev, kMaxDevices - 1);
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    return nullptr;
+  }
+  // racing first calls on one device store the same address
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -485,6 +520,23 @@ int relay_attn_decode_timed(const relay_dims* dims, const void* q, const void* s
   if (!events) return fail(RELAY_ERR_INVALID, "events is NULL");
   return decode_impl(dims, q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens,
                      cu_q_lens, out, workspace, workspace_bytes, stream, events);
+}
+
+int relay_attn_decode_noalloc(const relay_dims* dims, const void* q, const void* sys_k, const void* sys_v,
+                              int32_t sys_len, const void* ctx_k_pages, const void* ctx_v_pages,
+                              const int32_t* block_tables, const int32_t* ctx_lens,
+                              const int32_t* cu_q_lens, void* out, void* stream) {
+  int rc = check_dims(dims, sys_len);
+  if (rc != RELAY_OK) return rc;
+  Plan p;
+  if ((rc = make_plan(dims, sys_len, &p)) != RELAY_OK) return rc;
+  if (p.ws_bytes > (size_t)RELAY_NOALLOC_SCRATCH_BYTES)
+    return fail(RELAY_ERR_WORKSPACE, "the call needs %zu bytes of workspace; the allocation-free path holds %zu",
+                p.ws_bytes, (size_t)RELAY_NOALLOC_SCRATCH_BYTES);
+  void* ws = scratch_ptr();
+  if (!ws) return RELAY_ERR_HIP;
+  return decode_impl(dims, q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens,
+                     out, ws, (size_t)RELAY_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int relay_sys_attn(const relay_dims* dims, const void* q, const void* sys_k, const void* sys_v,

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_PKG, "librelay_attn.so")
 
 RELAY_F32, RELAY_BF16 = 0, 1
 RELAY_OK = 0
+RELAY_ERR_WORKSPACE = -3
+NOALLOC_SCRATCH_BYTES = 128 << 20  # the header's RELAY_NOALLOC_SCRATCH_BYTES
 
 
 class relay_dims(ctypes.Structure):
@@ -55,7 +57,8 @@ class RelayError(RuntimeError):
 
 
 EXPORTS = ("relay_abi_version", "relay_strerror", "relay_last_error", "relay_workspace_size",
-           "relay_get_plan", "relay_attn_decode", "relay_attn_decode_timed", "relay_sys_attn",
+           "relay_get_plan", "relay_attn_decode", "relay_attn_decode_timed", "relay_attn_decode_noalloc",
+           "relay_sys_attn",
            "relay_ctx_attn", "relay_fuse", "relay_validate", "relay_rope_table", "relay_rope_append",
            "relay_rope_system", "relay_system_fill", "relay_prefill_workspace_size", "relay_prefill_attn")
 
@@ -80,6 +83,8 @@ def load_library(path: str = LIB_PATH):
     lib.relay_get_plan.restype = ctypes.c_int
     lib.relay_attn_decode.argtypes = [D, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.relay_attn_decode.restype = ctypes.c_int
+    lib.relay_attn_decode_noalloc.argtypes = [D, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.relay_attn_decode_noalloc.restype = ctypes.c_int
     lib.relay_attn_decode_timed.argtypes = [D, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                             ctypes.POINTER(vp)]
     lib.relay_attn_decode_timed.restype = ctypes.c_int
@@ -281,6 +286,25 @@ def relay_attn_decode(q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_
         ctypes.byref(dims), _ptr(q), _ptr(sys_k), _ptr(sys_v), int(sys_len), _ptr(ctx_k_pages),
         _ptr(ctx_v_pages), _ptr(block_tables), _ptr(ctx_lens), _ptr(cu_q_lens), _ptr(out), _ptr(ws),
         ws.numel(), _stream(stream)))
+    return out
+
+
+def relay_attn_decode_noalloc(q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens,
+                              cu_q_lens=None, out=None, *, scale: float, max_ctx_len: int,
+                              max_q_len: int = 1, out_dtype=torch.float32, stream=None) -> torch.Tensor:
+    """relay_attn_decode on the library's static per-device scratch (no workspace
+    argument, no device allocation inside the call; ``out`` is allocated here only when
+    it is not given).  Calls that overlap on one device race."""
+    _require_device(q, sys_k, sys_v, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens, out)
+    check_decode_args(q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables, ctx_lens, cu_q_lens,
+                      out, out_dtype)
+    dims = make_dims(q, ctx_k_pages, block_tables, scale=scale, max_ctx_len=max_ctx_len,
+                     max_q_len=max_q_len, out_dtype=out_dtype)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _check(load_library().relay_attn_decode_noalloc(
+        ctypes.byref(dims), _ptr(q), _ptr(sys_k), _ptr(sys_v), int(sys_len), _ptr(ctx_k_pages),
+        _ptr(ctx_v_pages), _ptr(block_tables), _ptr(ctx_lens), _ptr(cu_q_lens), _ptr(out), _stream(stream)))
     return out
 
 

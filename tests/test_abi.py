@@ -42,6 +42,11 @@ def test_library_exports_every_declared_symbol(lib):
         assert getattr(lib, name) is not None
 
 
+def test_noalloc_scratch_size_matches_the_header():
+    m = re.search(r"#define RELAY_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == R.NOALLOC_SCRATCH_BYTES
+
+
 def test_library_is_gfx950_only(lib):
     # the device code objects are embedded for gfx950 alone
     blob = open(R.LIB_PATH, "rb").read()
