@@ -33,7 +33,7 @@ namespace relay {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// A decode step adds P's bf16 rounding residual when some row's largest probability in
+// A decode 16-key block adds P's bf16 rounding residual when some row's largest probability in
 // it exceeds 1 / kSplitShare of the row's running sum.
 constexpr float kSplitShare = 32.f;
 
@@ -325,41 +325,48 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
       // rounding costs up to 2^-9 of each probability.  Where that could matter, the
       // rounding residual lo = P - bf16(P) (also bf16) goes in as a second product:
       //  * causal segments that some token sees little of (psplit, known per segment);
-      //  * decode steps in which some row's largest probability exceeds 1 / kSplitShare
-      //    of the row's running sum, i.e. a key that may hold a large share of the row's
-      //    weight.  Keys below that share round once: their errors are small and
-      //    independent.
+      //  * decode 16-key blocks in which some row's largest probability exceeds
+      //    1 / kSplitShare of the row's running sum, i.e. a key that may hold a large
+      //    share of the row's weight.  Keys below that share round once: their errors
+      //    are small and independent.
       const char* vt = buf + mf::kTileBytes;
       const int vsw = (hh ^ (r32 & 7)) << 4;  // V chunk 2 kb + hh of row d sits at (2 kb + hh) ^ (d % 8); d % 8 = r32 % 8
-      auto pv = [&](const float (&pp)[32], bool hi_part, bool lo_part) {
+      // the row's running sum (both lane halves): a 16-key block needs the residual
+      // product when one of its probabilities exceeds 1 / kSplitShare of it for some row
+      float row_sum;
+      {
+        float la, lb;
+        swap32(lsum, la, lb);
+        row_sum = la + lb;
+      }
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const float* p = pp + 8 * kb;
-          const u32x4 hi = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                                 pack_bf16x2(p[6], p[7])};
-          u32x4 lo = hi;
-          if (lo_part)
-            lo = u32x4{pack_bf16x2(p[0] - bf16_lo_as_float(hi[0]), p[1] - bf16_hi_as_float(hi[0])),
-                       pack_bf16x2(p[2] - bf16_lo_as_float(hi[1]), p[3] - bf16_hi_as_float(hi[1])),
-                       pack_bf16x2(p[4] - bf16_lo_as_float(hi[2]), p[5] - bf16_hi_as_float(hi[2])),
-                       pack_bf16x2(p[6] - bf16_lo_as_float(hi[3]), p[7] - bf16_hi_as_float(hi[3]))};
+      for (int kb = 0; kb < 4; ++kb) {
+        const float* p = sc + 8 * kb;
+        const u32x4 hi = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                               pack_bf16x2(p[6], p[7])};
+#pragma unroll
+        for (int db = 0; db < mf::D / 32; ++db) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(vt + (32 * db + r32) * 128 + (((2 * kb) << 4) ^ vsw));
+          o[db] = mfma32(v, hi, o[db]);
+        }
+        bool split;
+        if constexpr (CAUSAL) {
+          split = psplit;
+        } else {
+          float pm = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])), fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7])));
+          split = __builtin_amdgcn_ballot_w64(pm * kSplitShare > row_sum) != 0;
+        }
+        if (split) {
+          const u32x4 lo = u32x4{pack_bf16x2(p[0] - bf16_lo_as_float(hi[0]), p[1] - bf16_hi_as_float(hi[0])),
+                                 pack_bf16x2(p[2] - bf16_lo_as_float(hi[1]), p[3] - bf16_hi_as_float(hi[1])),
+                                 pack_bf16x2(p[4] - bf16_lo_as_float(hi[2]), p[5] - bf16_hi_as_float(hi[2])),
+                                 pack_bf16x2(p[6] - bf16_lo_as_float(hi[3]), p[7] - bf16_hi_as_float(hi[3]))};
 #pragma unroll
           for (int db = 0; db < mf::D / 32; ++db) {
             const u32x4 v = *reinterpret_cast<const u32x4*>(vt + (32 * db + r32) * 128 + (((2 * kb) << 4) ^ vsw));
-            if (hi_part) o[db] = mfma32(v, hi, o[db]);
-            if (lo_part) o[db] = mfma32(v, lo, o[db]);
+            o[db] = mfma32(v, lo, o[db]);
           }
         }
-      };
-      if constexpr (CAUSAL) {
-        if (psplit) pv(sc, true, true);
-        else pv(sc, true, false);
-      } else {
-        float la, lb;
-        swap32(lsum, la, lb);
-        const bool split = __builtin_amdgcn_ballot_w64(fast_exp2(mx - m_use) * kSplitShare > la + lb) != 0;
-        if (split) pv(sc, true, true);
-        else pv(sc, true, false);
       }
       if (more) __builtin_amdgcn_s_waitcnt(0);  // the next step's tiles have landed
       __syncthreads();  // (also: the buffers are free for the next segment)
