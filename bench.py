@@ -1,23 +1,34 @@
 #!/usr/bin/env python3
 """RelayAttention decode-attention benchmark on one MI355X.
 
-One step = one relay_attn_decode call (sys_attn + ctx_attn + relay_fuse) over one
-batch of the Llama2-7B-shaped decode-attention layer: batch 32, 32 MHA heads,
-head_dim 128, bf16 in / fp32 accumulation, system prompt 2048 tokens, per-request
-contexts uniform in [16, 512] (paged, block 16, shuffled block tables), synthetic
-seeded inputs.  Inputs are resident in HBM before timing starts.  Each real layer
-has its own KV cache, so the timed loop rotates over several copies of the inputs
-whose total exceeds the 256 MB Infinity Cache; a step therefore reads its K/V from
-HBM, not from the last-level cache.
+One step = one relay_attn_decode call (system attention, context attention and the
+relay merge) over one batch of the Llama2-7B-shaped decode-attention layer: batch 32,
+32 MHA heads, head_dim 128, bf16 in / fp32 accumulation, system prompt 2048 tokens,
+per-request contexts uniform in [16, 512] (paged, block 16, shuffled block tables),
+synthetic seeded inputs.  Inputs are resident in HBM before timing starts.  Each real
+layer has its own KV cache, so the timed loop rotates over several copies of the
+inputs whose total exceeds the 256 MB Infinity Cache; a step therefore reads its K/V
+from HBM, not from the last-level cache.
 
 Prints one JSON line:
   value          query-tokens/s/layer (T_q / step time)
-  roofline       dominant kernel: algorithmic bytes / HIP-event duration vs 8 TB/s
+  roofline       dominant kernel: algorithmic bytes (or flops) per launch over its
+                 kernel-execution time (HIP events the runtime stamps at the kernel's
+                 start and end), against the published peak and the measured ceiling
+                 (librelay_probes.so); with the committed rocprofv3 figure beside it
   cpu_baseline   the fp64 oracle on the host cores over a bounded sample
   sweep          query-tokens/s and HBM fraction vs system length (Llama-30B shape)
+  batch_sweep, context_dilution   relay against the prefix-shared baseline
+  oracle_single_thread   the oracle on one host thread, configs 1-3
+
+Other modes (one JSON line per case, for rocprofv3 runs): --sys-scaling,
+--batch-sweep, --copy-calibration; --summarize turns rocprofv3 CSV output into the
+text summaries under profiles/.
 """
 import argparse
+import csv
 import ctypes
+import glob
 import json
 import math
 import os
@@ -31,6 +42,14 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3
 MALL_BYTES = 256 * 2**20
+COPY_BYTES = 512 * 2**20
+READ_PROBE_BYTES = 2**30
+
+BATCH_POINTS = (1, 4, 16, 64, 256)       # Llama2-7B shape, relay against the baseline
+CTX_POINTS = (64, 256, 1024, 4096)       # every request's own context length, batch 32
+ORACLE_1T = ((1, 0), (2, 0), (3, 0), (3, 5))
+BATCH_SWEEP = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+SYS_SCALING = (("llama2_7b_mha", 2, (1, 4, 8, 16, 32)), ("llama3_8b_gqa", 4, (1, 4, 16, 64, 256)))
 
 
 def parse():
@@ -41,7 +60,7 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload config 1..5 (default 2)")
     ap.add_argument("--sweep-index", type=int, default=0, help="config-3 system-length index")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="only the main line (no sweeps, probes, extras)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the oracle sample in CPU-seconds (wall time x threads)")
     ap.add_argument("--no-graph", action="store_true",
@@ -50,98 +69,165 @@ def parse():
                     help="only run the system-attention step over batch sweeps of the Llama2-7B and "
                          "Llama-3-8B shapes (for counters: system-KV bytes read vs batch size)")
     ap.add_argument("--batch-sweep", action="store_true",
-                    help="only run relay vs the no-relay baseline (prefix-shared system pages) over "
-                         "batch sizes of the Llama2-7B shape, then over request context lengths at batch 32 "
-                         "(one JSON line per point)")
+                    help="only run relay vs the no-relay baseline over more batch sizes of the Llama2-7B "
+                         "shape, then over request context lengths at batch 32 (one JSON line per point)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run torch's device copy of COPY_BYTES, 10 times (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
+    ap.add_argument("--summarize", choices=("stats", "traffic", "mfma"),
+                    help="write a profiles/ summary from rocprofv3 --output-format csv directories")
+    ap.add_argument("--workload", default="", help="--summarize: workload name of the profiled run(s)")
+    ap.add_argument("--dirs", nargs="*", default=[],
+                    help="--summarize: rocprofv3 -d directories (stats: 1; traffic: fetch, write, copy "
+                         "fetch, copy write; mfma: one per workload, --workload lists them comma-separated)")
+    ap.add_argument("--commands", nargs="*", default=[], help="--summarize: the commands that made --dirs")
     return ap.parse_args()
 
 
-COPY_BYTES = 512 * 2**20
+# ---------------------------------------------------------------------------------------
+# kernels by short name, and the rocprofv3 summaries under profiles/
+
+KERNELS = (("stream_attn_kernel", "stream_attn"), ("sys_attn_mfma_kernel", "sys_attn_mfma"),
+           ("sys_attn_tiled_kernel", "sys_attn_tiled"), ("relay_merge_kernel", "relay_merge"),
+           ("relay_fuse_kernel", "relay_fuse"), ("rope_append_kernel", "rope_append"),
+           ("read_probe_kernel", "read_probe"), ("mfma_probe_kernel", "mfma_probe"))
 
 
-def copy_calibration(torch):
-    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(10):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": COPY_BYTES, "dispatches": 10}), flush=True)
+def short_name(full):
+    for k, s in KERNELS:
+        if k in full:
+            return s
+    return None
 
 
-BATCH_SWEEP = (1, 2, 4, 8, 16, 32, 64, 128, 256)
-CTX_SWEEP = (64, 256, 1024, 4096)  # every request's own context length, Llama2-7B shape, batch 32
-SYS_SCALING = (("llama2_7b_mha", 2, (1, 4, 8, 16, 32)), ("llama3_8b_gqa", 4, (1, 4, 16, 64, 256)))
-
-
-def sys_scaling(torch, relay, steps):
-    """relay_sys_attn alone (system kernel + chunk merge) for each batch size: 3
-    untimed calls then `steps` timed ones.  Prints one JSON line per case; under
-    rocprofv3 the system kernel's dispatches come in the same order, 3 + steps per
-    case."""
-    import workloads
-    for name, cfg, batches in SYS_SCALING:
-        for B in batches:
-            spec = workloads.config_spec(cfg, 0).replace(batch=B)
-            w = workloads.generate(spec)
-            t = relay.to_device(w, "cuda")
-            dims = relay.dims_of(t)
-            ws = relay.workspace(dims, t["sys_len"], "cuda")
-            call = lambda: relay.relay_sys_attn(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], dims,
-                                                workspace_buf=ws)
-            for _ in range(3):
-                call()
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(steps):
-                call()
-            e1.record()
-            torch.cuda.synchronize()
-            plan = relay.relay_get_plan(dims, t["sys_len"])
-            E = 2 if spec.dtype == "bf16" else 4
-            print(json.dumps({"shape": name, "batch": B, "sys_len": spec.sys_len,
-                              "rows_per_kv_head": w.total_q * spec.group,
-                              "kernel": ("sys_attn" if plan["sys_mode"] == 1 else
-                                         "sys_attn_mfma" if (spec.dtype == "bf16" and spec.head_dim == 128)
-                                         else "sys_attn_tiled"),
-                              "dispatches": 3 + steps,
-                              "sys_kv_bytes": 2 * spec.num_kv_heads * spec.head_dim * E * spec.sys_len,
-                              "us_per_call": round(1000 * e0.elapsed_time(e1) / steps, 2)}), flush=True)
-            del t, ws, w
-            torch.cuda.empty_cache()
-
-
-def stored_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3
-    counter summary, or None when there is none or the library's sources have
-    changed since it was taken."""
+def source_digest():
     from shared_prompt_kv_amd import build as B
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    with open(path) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
+    return B.source_digest()
+
+
+def _csv(d, suffix):
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    with open(files[0], newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _counters(d):
+    """{(short kernel, counter): [value per dispatch]} from a counter_collection.csv."""
+    per = {}
+    for row in _csv(d, "counter_collection.csv"):
+        k = short_name(row["Kernel_Name"]) or ("copy" if "copyBuffer" in row["Kernel_Name"] else None)
+        if k is None:
+            continue
+        key = (k, row["Counter_Name"], row["Dispatch_Id"])
+        per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (k, c, _), v in per.items():
+        out.setdefault((k, c), []).append(v)
+    return out
+
+
+def summarize(args):
+    """profiles/ text summary of rocprofv3 CSV output: kernel statistics, HBM traffic
+    per launch (FETCH_SIZE / WRITE_SIZE scaled by a device copy of known size), or
+    matrix-core utilisation."""
+    dig = source_digest()
+    head = [f"library_sources_sha256: {dig}"]
+    cmds = ["# commands:"] + [f"#   {c}" for c in args.commands]
+    if args.summarize == "stats":
+        rows = []
+        for r in _csv(args.dirs[0], "kernel_stats.csv"):
+            rows.append((short_name(r["Name"]) or "-", int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"]), r["Name"]))
+        named = [r for r in rows if r[0] != "-"]
+        dom = max(named, key=lambda r: r[1] * r[2])[0]
+        path = os.path.join(ROOT, "profiles", f"{dom}_{args.workload}_kernel_stats.txt")
+        lines = [f"# rocprofv3 kernel-trace statistics: {args.workload} (kernels timed by dispatch start/end)"]
+        lines += cmds + head
+        lines.append(f"{'kernel':16s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}  full name")
+        for s, c, a, mn, mx, pct, full in sorted(rows, key=lambda r: -r[5]):
+            lines.append(f"{s:16s} {c:6d} {a:9.3f} {mn:9.3f} {mx:9.3f} {pct:6.2f}  {full[:90]}")
+    elif args.summarize == "traffic":
+        fetch, write, cfetch, cwrite = (_counters(d) for d in args.dirs[:4])
+        cf = sum(cfetch[("copy", "FETCH_SIZE")]) / len(cfetch[("copy", "FETCH_SIZE")])
+        cw = sum(cwrite[("copy", "WRITE_SIZE")]) / len(cwrite[("copy", "WRITE_SIZE")])
+        fscale, wscale = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+        lines = [f"# HBM traffic per launch on {args.workload}: rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per "
+                 "dispatch), scaled by what the same counters read for torch's device copy of 512 MiB "
+                 "(one read + one write of 512 MiB)"]
+        lines += cmds + head
+        lines += [f"copy_bytes: {COPY_BYTES}", f"copy_fetch_kib_per_dispatch: {cf:.1f}",
+                  f"copy_write_kib_per_dispatch: {cw:.1f}", f"fetch_scale: {fscale:.4f}",
+                  f"write_scale: {wscale:.4f}"]
+        kernels = sorted({k for k, c in fetch if k not in ("copy",)})
+        best = None
+        for k in kernels:
+            f = fetch.get((k, "FETCH_SIZE"), [])
+            w = write.get((k, "WRITE_SIZE"), [])
+            if not f or not w:
+                continue
+            fk, wk = sum(f) / len(f), sum(w) / len(w)
+            t = int(round(fk * 1024 * fscale + wk * 1024 * wscale))
+            lines += [f"{k}.dispatches: {len(f)}", f"{k}.fetch_kib_per_dispatch: {fk:.1f}",
+                      f"{k}.write_kib_per_dispatch: {wk:.1f}", f"{k}.traffic_bytes_per_launch: {t}"]
+            if best is None or t > best[1]:
+                best = (k, t)
+        path = os.path.join(ROOT, "profiles", f"{best[0]}_{args.workload}_traffic.txt")
+    else:
+        lines = ["# Matrix-core utilisation: SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / "
+                 "(GRBM_GUI_ACTIVE per XCD * 1024 SIMDs); GRBM_GUI_ACTIVE is reported summed over "
+                 "the 8 XCDs, so per-XCD active cycles = value / 8"]
+        lines += cmds + head
+        lines.append(f"{'workload':26s} {'kernel':16s} {'dispatches':>10s} {'mfma_busy':>14s} "
+                     f"{'active/xcd':>12s} {'mfma_util':>9s}")
+        for wl, d in zip(args.workload.split(","), args.dirs):
+            cnt = _counters(d)
+            for k in sorted({k for k, c in cnt}):
+                busy = cnt.get((k, "SQ_VALU_MFMA_BUSY_CYCLES"))
+                act = cnt.get((k, "GRBM_GUI_ACTIVE"))
+                if not busy or not act:
+                    continue
+                b, a = sum(busy) / len(busy), sum(act) / len(act) / 8
+                lines.append(f"{wl:26s} {k:16s} {len(busy):10d} {b:14.0f} {a:12.0f} {b / (a * 1024):9.3f}")
+        path = os.path.join(ROOT, "profiles", "sys_attn_mfma_mfma_util.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
+def read_profile(kind, workload):
+    """A committed summary of this workload taken from the current library sources:
+    {kernel: avg_us} (kind "stats") or {kernel: traffic bytes per launch} ("traffic"),
+    with the file it came from; None when there is none or it is stale."""
+    pat = os.path.join(ROOT, "profiles", f"*_{workload}_{'kernel_stats' if kind == 'stats' else 'traffic'}.txt")
+    dig = source_digest()
+    for path in sorted(glob.glob(pat)):
+        with open(path) as f:
+            text = f.read().splitlines()
+        if f"library_sources_sha256: {dig}" not in text:
+            continue
+        out = {}
+        for line in text:
+            if line.startswith("#"):
+                continue
+            if kind == "stats":
+                parts = line.split()
+                if len(parts) >= 6 and parts[0] in dict((s, 1) for _, s in KERNELS):
+                    out[parts[0]] = float(parts[2])
+            elif ".traffic_bytes_per_launch:" in line:
                 k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
-    if kv.get("library_sources_sha256") != B.source_digest():
-        return None
-    try:
-        return int(kv["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+                out[k.split(".")[0]] = int(v)
+        if out:
+            return out, os.path.relpath(path, ROOT)
+    return None
 
 
 # ---------------------------------------------------------------------------------------
-# algorithmic work (what the method must move / compute, not implementation overhead)
+# algorithmic work (what the method must move / compute) and the partials' overhead
 
 
-def work_of(w):
+def work_of(w, plan=None):
     s = w.spec
     E = 2 if s.dtype == "bf16" else 4
     d, Hq, Hkv = s.head_dim, s.num_q_heads, s.num_kv_heads
@@ -152,22 +238,72 @@ def work_of(w):
     kv_sys = 2 * Hkv * d * E * s.sys_len
     kv_ctx = 2 * Hkv * d * E * sum_ctx
     q_bytes = rows * d * E
+    out_bytes = rows * d * 4
     part_row = rows * (d + 1) * 4          # one fp32 output row + LSE per query row
     tables = 4 * B * (mb + 2) + (4 * (B + 1) if int(w.q_lens.max()) > 1 else 0)
-    vis = 0
-    for b in range(B):
-        n, c = int(w.q_lens[b]), int(w.ctx_lens[b])
-        vis += sum(c - n + t + 1 for t in range(n))
-    return {
-        "step_bytes": kv_sys + kv_ctx + rows * d * (E + 4) + tables,
+    ql, cl = w.q_lens.astype(int), w.ctx_lens.astype(int)
+    vis = int((ql * cl - ql * (ql - 1) // 2).sum())      # visible context keys over all query tokens
+    sys_in_stream = plan is None or plan["sys_mode"] == 1
+    work = {
+        "step_bytes": kv_sys + kv_ctx + q_bytes + out_bytes + tables,
         "step_flops": 4 * Hq * d * (Tq * s.sys_len + vis),
-        "sys_attn": kv_sys + q_bytes,
-        # the streaming launch: context (and, at <= 64 stacked rows per KV head, system) K/V
-        "stream_attn": (kv_sys if w.total_q * s.group <= 64 else 0) + kv_ctx + q_bytes + tables,
-        "relay_merge": 2 * part_row + rows * d * 4,
         "sys_flops": 4 * Hq * d * Tq * s.sys_len,
         "ctx_flops": 4 * Hq * d * vis,
+        "sys_attn_mfma": kv_sys + q_bytes,
+        "sys_attn_tiled": kv_sys + q_bytes,
+        # the streaming launch: context (and, at <= 64 stacked rows per KV head, system) K/V
+        "stream_attn": (kv_sys if sys_in_stream else 0) + kv_ctx + q_bytes + tables,
+        # relay fusion as the method states it: two partials in, the output out
+        "relay_merge": 2 * part_row + out_bytes,
     }
+    if plan is not None:
+        work["overhead"] = partial_overhead(w, plan)
+    return work
+
+
+def partial_overhead(w, plan):
+    """Bytes of partial results beyond the method's two per row: what the kernels write
+    (each piece of a stream writes its rows' O and LSE) and what the merge reads back
+    beyond two partials per row.  Follows the streaming launch's static partition
+    (single request group); the system kernel writes every run slot of every row."""
+    import numpy as np
+    s = w.spec
+    d, g, Hkv = s.head_dim, s.group, s.num_kv_heads
+    row_b = (d + 1) * 4
+    rows = w.total_q * s.num_q_heads
+    if plan["stream_launches"] != 1:
+        return None
+    rtc, rbmax = plan["ctx_row_tiles"], plan["ctx_row_blocks"]
+    nq = w.q_lens.astype(np.int64)
+    c = np.minimum(w.ctx_lens.astype(np.int64), w.max_blocks_per_seq * 16)
+    steps = np.maximum(1, -(-c // 32))
+    rbs = np.minimum(-(-(nq * g) // (16 * rtc)), rbmax)
+    # streams in (request, head, row block) order
+    req = np.repeat(np.arange(len(c)), rbs * Hkv)
+    rb = np.concatenate([np.tile(np.arange(r), Hkv) for r in rbs]) if len(c) else np.zeros(0, np.int64)
+    st = steps[req]
+    rows_in = np.minimum(nq[req] * g - rb * 16 * rtc, 16 * rtc)
+    M = w.total_q * g
+    sys_mode = plan["sys_mode"]
+    S = -(-s.sys_len // 32) if sys_mode == 1 else 0
+    Ts = Hkv * S
+    T = Ts + int(st.sum())
+    W = min(plan["stream_waves"], T)
+    part_of = lambda x: ((x + 1) * W + T - 1) // T - 1
+    p0 = Ts + np.concatenate([[0], np.cumsum(st)[:-1]]) if len(st) else np.zeros(0, np.int64)
+    ctx_pieces = part_of(p0 + st - 1) - part_of(p0) + 1
+    written = int((ctx_pieces * rows_in).sum()) * row_b
+    if sys_mode == 1 and S > 0:
+        h = np.arange(Hkv)
+        sys_pieces = part_of(h * S + S - 1) // 4 - part_of(h * S) // 4 + 1
+        written_sys = int(sys_pieces.sum()) * M * row_b
+    elif sys_mode >= 2:
+        written_sys = plan["sys_runs"] * rows * row_b
+    else:
+        written_sys = 0
+    return {"stream_attn_partials_written": written + (written_sys if sys_mode == 1 else 0),
+            "sys_kernel_partials_written": written_sys if sys_mode >= 2 else 0,
+            "merge_extra_partial_reads": max(0, written + written_sys - 2 * rows * row_b)}
 
 
 # ---------------------------------------------------------------------------------------
@@ -182,7 +318,6 @@ class HipEvents:
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
 
     def create(self, n):
         out = []
@@ -210,27 +345,32 @@ def clone_set(torch, t):
     return {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
 
 
+def sys_kernel_name(plan):
+    return {2: "sys_attn_mfma", 3: "sys_attn_tiled"}.get(plan["sys_mode"])
+
+
 def measure(torch, relay, w, steps, warmup, per_kernel=True, graph=True, prep=None):
     """Times decode steps over rotating input copies.
 
-    graph: the steps captured in one HIP graph (a full rotation over the copies)
-    and replayed, as a served model replays its decode step; the timed region holds
-    `steps` steps.  eager: the same steps launched one by one through the prepared
-    C-ABI call.  Per-kernel durations come from HIP events recorded by the library
-    between its launches (eager).
+    graph: the steps captured in one HIP graph (a full rotation over the copies) and
+    replayed, as a served model replays its decode step; the timed region holds `steps`
+    steps.  eager: the same steps launched one by one through the prepared C-ABI call.
+    Per-kernel durations: the timed entry point's events, which the runtime stamps at
+    each kernel's own start and end (eager steps, `steps` of them).
     """
     t0 = relay.to_device(w, "cuda")
     if prep is not None:  # e.g. the no-relay baseline's inputs
         t0 = prep(t0)
-    work = work_of(w)
+    dims = relay.dims_of(t0)
+    plan = relay.relay_get_plan(dims, t0["sys_len"])
+    work = work_of(w, plan)
     n_sets = max(2, math.ceil(3 * MALL_BYTES / max(work["step_bytes"], 1)))
     n_sets = min(n_sets, 16)
     sets = [t0] + [clone_set(torch, t0) for _ in range(n_sets - 1)]
-    dims = relay.dims_of(t0)
     ws = relay.workspace(dims, t0["sys_len"], "cuda")
     outs = [torch.empty(t0["q"].shape, dtype=torch.float32, device="cuda") for _ in range(n_sets)]
     calls = [relay.DecodeCall(sets[i], outs[i], ws) for i in range(n_sets)]
-    res = {"n_sets": n_sets, "work": work, "plan": relay.relay_get_plan(dims, t0["sys_len"])}
+    res = {"n_sets": n_sets, "work": work, "plan": plan}
 
     for i in range(warmup):
         calls[i % n_sets]()
@@ -250,21 +390,19 @@ def measure(torch, relay, w, steps, warmup, per_kernel=True, graph=True, prep=No
 
     if per_kernel:
         he = HipEvents(torch)
-        evs = he.create(4 * steps)
+        evs = he.create(6 * steps)
         for i in range(steps):
-            calls[i % n_sets].timed(evs[4 * i:4 * i + 4])
+            calls[i % n_sets].timed(evs[6 * i:6 * i + 6])
         torch.cuda.synchronize()
-        # launch names: a separate (tiled) system launch, then the attention launch
-        # (both steps together when sys_mode == 1), then relay_fuse
-        mode = res["plan"]["sys_mode"]
-        names = ("sys_attn", "stream_attn", "relay_merge")
-        acc = dict.fromkeys(names, 0.0)
+        names = [sys_kernel_name(plan), "stream_attn", "relay_merge"]
+        acc = {}
         for i in range(steps):
-            e = evs[4 * i:4 * i + 4]
+            e = evs[6 * i:6 * i + 6]
             for j, k in enumerate(names):
-                acc[k] += he.elapsed_ms(e[j], e[j + 1])
+                if k is not None:
+                    acc[k] = acc.get(k, 0.0) + he.elapsed_ms(e[2 * j], e[2 * j + 1])
         he.destroy(evs)
-        res["kernel_us"] = {k: 1000.0 * v / steps for k, v in acc.items() if mode >= 2 or k != "sys_attn"}
+        res["kernel_us"] = {k: 1000.0 * v / steps for k, v in acc.items()}
     del calls, sets, outs, ws
     torch.cuda.empty_cache()
     return res
@@ -308,15 +446,32 @@ def _time_graph(torch, calls, n_sets, steps, res):
     del full, part
 
 
-def measured_hbm(torch):
-    """What plain torch kernels reach on this GPU: a 1 GiB read (sum of a bf16 tensor)
-    and a 512 MiB device copy (read + write), GB/s.  Context for the roofline fraction
-    (the 8 TB/s peak is a spec figure); not part of the decode step."""
-    x = torch.ones(2**29, dtype=torch.bfloat16, device="cuda")
-    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
+# ---------------------------------------------------------------------------------------
+# measured ceilings: librelay_probes.so
 
-    def rate(fn, nbytes, n=20):
+
+def probes_lib():
+    from shared_prompt_kv_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        raise RuntimeError(f"{B.PROBE_LIB} is not built: run `python -m shared_prompt_kv_amd.build`")
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    vp = ctypes.c_void_p
+    lib.relay_probe_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int32, vp]
+    lib.relay_probe_mfma.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp]
+    return lib
+
+
+def measured_ceilings(torch):
+    """What this GPU reaches at all: a hand-written streaming read of 1 GiB (best over
+    a few grid sizes) and bf16 matrix-core products on register operands (one
+    v_mfma_f32_32x32x16_bf16 stream per wave, two waves per SIMD)."""
+    lib = probes_lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    buf = torch.ones(READ_PROBE_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(16 * cus * 256, dtype=torch.float32, device="cuda")
+
+    def timed(fn, n=20):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -326,14 +481,40 @@ def measured_hbm(torch):
             fn()
         e1.record()
         torch.cuda.synchronize()
-        return round(nbytes / (e0.elapsed_time(e1) / n * 1e-3) / 1e9, 1)
+        return e0.elapsed_time(e1) / n * 1e-3
 
-    out = {"read_GBps": rate(lambda: x.sum(), x.numel() * 2),
-           "copy_GBps": rate(lambda: dst.copy_(src), 2 * COPY_BYTES),
-           "note": "torch sum over 1 GiB bf16 (read) and device copy of 512 MiB (read + write)"}
-    del x, src, dst
+    best = (0.0, 0)
+    for per_cu in (1, 2, 4, 8):
+        grid = per_cu * cus
+        t = timed(lambda: lib.relay_probe_read(ctypes.c_void_p(buf.data_ptr()), READ_PROBE_BYTES,
+                                               ctypes.c_void_p(sink.data_ptr()), grid, stream))
+        best = max(best, (READ_PROBE_BYTES / t / 1e9, grid))
+    iters, grid = 512, 2 * cus
+    flops = grid * 4 * iters * 4 * 32768
+    t = timed(lambda: lib.relay_probe_mfma(ctypes.c_void_p(sink.data_ptr()), iters, grid, stream), n=5)
+    out = {"read_GBps": round(best[0], 1), "read_grid": best[1],
+           "read_frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4),
+           "mfma_bf16_TFLOPs": round(flops / t / 1e12, 1),
+           "mfma_frac_of_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "note": "librelay_probes.so: relay_probe_read over 1 GiB (16-byte loads, 8 in flight per thread, "
+                   "one contiguous slab per workgroup, best grid), relay_probe_mfma (register operands, 4 "
+                   "independent accumulators per wave, 2 workgroups of 4 waves per CU)"}
+    del buf, sink
     torch.cuda.empty_cache()
     return out
+
+
+def copy_calibration(torch):
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "dispatches": 10}), flush=True)
+
+
+# ---------------------------------------------------------------------------------------
+# the oracle on the host
 
 
 def cpu_model():
@@ -347,16 +528,13 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(w, budget_cpu_s):
-    """The oracle (unchanged) on the host cores, request by request through the
-    workload (cycling), until about budget_cpu_s CPU-seconds have been spent."""
-    import oracle
+def _oracle_rate(w, budget_wall):
+    """Query tokens per second of the oracle (exact fp64 attention over all heads),
+    request by request through the workload (cycling) for about budget_wall seconds."""
     import numpy as np
-
+    import oracle
     P = oracle.Problem(w)
     Hq = w.spec.num_q_heads
-    cores = oracle.num_threads()
-    budget_wall = budget_cpu_s / max(cores, 1)
     tokens, elapsed, n = 0, 0.0, 0
     start = time.perf_counter()
     while elapsed < budget_wall:
@@ -366,18 +544,50 @@ def cpu_baseline(w, budget_cpu_s):
         tokens += hi - lo
         n += 1
         elapsed = time.perf_counter() - start
-    return {"value": round(tokens / elapsed, 3), "unit": "query-tokens/s/layer", "cores": cores,
+    return tokens / elapsed, n, tokens, elapsed
+
+
+def cpu_baseline(w, budget_cpu_s):
+    """The oracle (unchanged) on all host cores, until about budget_cpu_s CPU-seconds
+    have been spent."""
+    import oracle
+    cores = oracle.num_threads()
+    rate, n, tokens, elapsed = _oracle_rate(w, budget_cpu_s / max(cores, 1))
+    return {"value": round(rate, 3), "unit": "query-tokens/s/layer", "cores": cores,
             "kind": "oracle", "cpu": cpu_model(),
-            "sample": f"exact fp64 causal attention (all {Hq} heads) for {n} requests taken in order, "
-                      f"cycling over the {w.spec.batch} requests of the same workload: {tokens} query "
+            "sample": f"exact fp64 causal attention (all {w.spec.num_q_heads} heads) for {n} requests taken in "
+                      f"order, cycling over the {w.spec.batch} requests of the same workload: {tokens} query "
                       f"tokens in {elapsed:.2f} s wall on {cores} threads"}
 
 
-def point(torch, relay, spec, args, with_baseline=False):
+def oracle_single_thread(budget_s=1.5):
+    """The oracle on one host thread for configs 1-3 (config 3 at its shortest and
+    longest system prompt), about budget_s seconds each."""
+    import oracle
+    import workloads
+    before = oracle.num_threads()
+    oracle.set_num_threads(1)
+    out = []
+    try:
+        for cfg, sweep in ORACLE_1T:
+            w = workloads.generate(workloads.config_spec(cfg, sweep))
+            rate, n, tokens, elapsed = _oracle_rate(w, budget_s)
+            out.append({"workload": w.spec.name, "qtok_s": round(rate, 2), "requests": n, "query_tokens": tokens,
+                        "seconds": round(elapsed, 2)})
+    finally:
+        oracle.set_num_threads(before)
+    return {"unit": "query-tokens/s/layer", "threads": 1, "points": out}
+
+
+# ---------------------------------------------------------------------------------------
+# points, sweeps and the steps around the path
+
+
+def point(torch, relay, spec, args, with_baseline=False, steps=50):
     """One workload measured like the main line (fewer steps): throughput and
     roofline fractions; with_baseline adds the no-relay baseline's step time."""
     w = workloads_generate(spec)
-    rr = measure(torch, relay, w, min(args.steps, 50), min(args.warmup, 10))
+    rr = measure(torch, relay, w, min(args.steps, steps), min(args.warmup, 10))
     print(f"[bench] {spec.name}: {1000 * rr['ms_per_step']:.2f} us/step", file=sys.stderr, flush=True)
     m = rr["ms_per_step"]
     work = rr["work"]
@@ -388,26 +598,61 @@ def point(torch, relay, spec, args, with_baseline=False):
            "mfma_frac": round(work["step_flops"] / (m * 1e-3) / peak, 4),
            "kernel_us": {k: round(v, 2) for k, v in rr["kernel_us"].items()},
            "sys_mode": rr["plan"]["sys_mode"]}
+    ov = work.get("overhead")
+    if ov:
+        out["partial_bytes_frac"] = round((ov["stream_attn_partials_written"] + ov["sys_kernel_partials_written"])
+                                          / work["step_bytes"], 4)
+    sk = sys_kernel_name(rr["plan"])
+    if sk == "sys_attn_mfma" and sk in rr["kernel_us"]:
+        out["sys_attn_mfma_frac"] = round(work["sys_flops"] / (rr["kernel_us"][sk] * 1e-6) / peak, 4)
     if with_baseline:
         out.update(no_relay_baseline(torch, relay, w, args, m))
     return out
 
 
-def no_relay_baseline(torch, relay, w, args, relay_ms):
+def no_relay_baseline(torch, relay, w, args, relay_ms, steps=50):
     """The same decode step without relay: every request's block table starts with
     the shared system pages and the context step reads them once per request."""
     from shared_prompt_kv_amd import baseline
-    rb = measure(torch, relay, w, min(args.steps, 50), min(args.warmup, 10), per_kernel=False,
+    rb = measure(torch, relay, w, min(args.steps, steps), min(args.warmup, 10), per_kernel=False,
                  prep=baseline.prefix_shared)
     bm = rb["ms_per_step"]
     print(f"[bench] {w.spec.name} no-relay baseline: {1000 * bm:.2f} us/step", file=sys.stderr, flush=True)
     return {"no_relay_us_per_step": round(1000 * bm, 2), "relay_speedup": round(bm / relay_ms, 3)}
 
 
+def batch_points(torch, relay, args, batches, steps=30):
+    """Relay against the prefix-shared baseline over batch sizes of the Llama2-7B shape:
+    the gain grows with the batch and a single request gains nothing."""
+    import workloads
+    out = []
+    for B in batches:
+        r = point(torch, relay, workloads.config_spec(2, 0).replace(batch=B), args, with_baseline=True, steps=steps)
+        out.append({"batch": B, "relay_us": r["us_per_step"], "no_relay_us": r["no_relay_us_per_step"],
+                    "speedup": r["relay_speedup"], "qtok_s": r["qtok_s"]})
+    return out
+
+
+def ctx_points(torch, relay, args, lens, steps=30):
+    """Relay against the baseline at batch 32 when every request has its own context of
+    C tokens: long request contexts dilute the gain (the system share of the bytes
+    shrinks; kv_bytes_ratio = baseline K/V bytes over relay K/V bytes)."""
+    import workloads
+    out = []
+    for C in lens:
+        spec = workloads.config_spec(2, 0).replace(ctx_len_dist="fixed", ctx_lo=C, ctx_hi=C)
+        r = point(torch, relay, spec, args, with_baseline=True, steps=steps)
+        L, B = spec.sys_len, spec.batch
+        out.append({"ctx_len": C, "relay_us": r["us_per_step"], "no_relay_us": r["no_relay_us_per_step"],
+                    "speedup": r["relay_speedup"], "kv_bytes_ratio": round(B * (L + C) / (L + B * C), 3)})
+    return out
+
+
 def rope_append_time(torch, relay, w, args):
     """The step before the path on the same workload: position embedding of the new
     tokens' q and k at sys_len + context position and their K/V appended to the pages
-    (relay_rope_append), timed alone with HIP events over back-to-back calls."""
+    (relay_rope_append), through a pre-marshalled call, back to back, timed with HIP
+    events; also the same calls replayed from a HIP graph."""
     t = relay.to_device(w, "cuda")
     s = w.spec
     dt = t["q"].dtype
@@ -418,27 +663,43 @@ def rope_append_time(torch, relay, w, args):
     v_new = torch.randn((w.total_q, s.num_kv_heads, s.head_dim), generator=g, device="cuda").to(dt)
     q_out = torch.empty_like(q_new)
     dims = relay.dims_of(t)
-    call = lambda: relay.relay_rope_append(dims, s.sys_len, q_new, k_new, v_new, tab, t["block_tables"],
-                                           t["ctx_lens"], t["cu_q_lens"], t["ctx_k_pages"], t["ctx_v_pages"],
-                                           q_out=q_out)
+    call = relay.RopeAppendCall(dims, s.sys_len, q_new, k_new, v_new, tab, t["block_tables"], t["ctx_lens"],
+                                t["cu_q_lens"], t["ctx_k_pages"], t["ctx_v_pages"], q_out)
+    n = min(args.steps, 200)
+
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
     for _ in range(10):
         call()
-    torch.cuda.synchronize()
-    n = min(args.steps, 200)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(n):
+    us = 1000 * timed(call, n) / n
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
         call()
-    e1.record()
-    torch.cuda.synchronize()
-    us = 1000 * e0.elapsed_time(e1) / n
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(20):
+            call()
+    graph.replay()
+    reps = max(1, n // 20)
+    us_graph = 1000 * timed(graph.replay, reps) / (20 * reps)
     E = 2 if s.dtype == "bf16" else 4
     nbytes = (2 * w.total_q * s.num_q_heads * s.head_dim * E      # q in and out
               + 4 * w.total_q * s.num_kv_heads * s.head_dim * E   # k, v in; k, v pages out
               + w.total_q * s.head_dim * 4)                       # one table row per token
-    return {"us_per_call": round(us, 2), "bytes_alg": nbytes,
-            "hbm_frac": round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
-            "note": "back-to-back eager launches; a few MB per call, launch-latency bound"}
+    return {"us_per_call": round(us, 2), "us_per_call_graph": round(us_graph, 2), "bytes_alg": nbytes,
+            "hbm_frac": round(nbytes / (us_graph * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+            "note": "pre-marshalled calls back to back (eager), and 20 calls per HIP graph replay; a few MB "
+                    "per call, so launch-latency bound"}
 
 
 def prefill_time(torch, relay, spec, args):
@@ -487,16 +748,98 @@ def prefill_time(torch, relay, spec, args):
     return out
 
 
+def sys_scaling(torch, relay, steps):
+    """relay_sys_attn alone (system kernel + merge) for each batch size: 3 untimed
+    calls then `steps` timed ones.  Prints one JSON line per case; under rocprofv3 the
+    system kernel's dispatches come in the same order, 3 + steps per case."""
+    import workloads
+    for name, cfg, batches in SYS_SCALING:
+        for B in batches:
+            spec = workloads.config_spec(cfg, 0).replace(batch=B)
+            w = workloads.generate(spec)
+            t = relay.to_device(w, "cuda")
+            dims = relay.dims_of(t)
+            ws = relay.workspace(dims, t["sys_len"], "cuda")
+            call = lambda: relay.relay_sys_attn(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], dims,
+                                                workspace_buf=ws)
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            plan = relay.relay_get_plan(dims, t["sys_len"])
+            E = 2 if spec.dtype == "bf16" else 4
+            print(json.dumps({"shape": name, "batch": B, "sys_len": spec.sys_len,
+                              "rows_per_kv_head": w.total_q * spec.group,
+                              "kernel": sys_kernel_name(plan) or "stream_attn",
+                              "dispatches": 3 + steps,
+                              "sys_kv_bytes": 2 * spec.num_kv_heads * spec.head_dim * E * spec.sys_len,
+                              "us_per_call": round(1000 * e0.elapsed_time(e1) / steps, 2)}), flush=True)
+            del t, ws, w
+            torch.cuda.empty_cache()
+
+
 def workloads_generate(spec):
     import workloads
     return workloads.generate(spec)
 
 
+# ---------------------------------------------------------------------------------------
+
+
+def roofline(r, spec, ceilings):
+    """The dominant kernel's roofline: algorithmic work per launch over its
+    kernel-execution time (live HIP events), against the published peak and the
+    measured ceiling, with the committed rocprofv3 figure of the same workload (when it
+    was taken from the current library sources) beside it."""
+    kus, work, plan = r["kernel_us"], r["work"], r["plan"]
+    dom = max(kus, key=kus.get)
+    us = kus[dom]
+    mfma = dom == "sys_attn_mfma"
+    if mfma:
+        alg, unit, peak = work["sys_flops"], "TFLOP/s", BF16_PEAK_TFLOPS
+        achieved = alg / (us * 1e-6) / 1e12
+    else:
+        alg, unit, peak = work[dom], "GB/s", HBM_PEAK_GBS
+        achieved = alg / (us * 1e-6) / 1e9
+    out = {"kernel": dom, "bound": "mfma" if mfma else "hbm", "achieved": round(achieved, 1), "peak": peak,
+           "unit": unit, "frac": round(achieved / peak, 4), "traffic": None, "avg_us": round(us, 3),
+           "timing": "kernel start/end events (hipExtLaunchKernelGGL), eager steps"}
+    out["flops_alg_per_launch" if mfma else "bytes_alg_per_launch"] = alg
+    ov = work.get("overhead")
+    if ov:
+        out["overhead_bytes_per_launch"] = (ov["sys_kernel_partials_written"] if mfma
+                                            else ov["stream_attn_partials_written"] if dom == "stream_attn"
+                                            else ov["merge_extra_partial_reads"])
+    if ceilings:
+        c = ceilings["mfma_bf16_TFLOPs"] if mfma else ceilings["read_GBps"]
+        out["measured_ceiling"] = {"value": c, "unit": unit, "frac": round(achieved / c, 4),
+                                   "probe": "relay_probe_mfma" if mfma else "relay_probe_read"}
+    tr = read_profile("traffic", spec.name)
+    if tr and dom in tr[0]:
+        out["traffic"] = tr[0][dom]
+        out["traffic_source"] = tr[1]
+    st = read_profile("stats", spec.name)
+    if st and dom in st[0]:
+        ru = st[0][dom]
+        out["rocprof"] = {"avg_us": ru, "frac": round(alg / (ru * 1e-6) / (1e12 if mfma else 1e9) / peak, 4),
+                          "source": st[1]}
+    return out
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
-              "(the decode-attention path runs on a single MI355X; see DESIGN.md for how it would shard)",
+              "(the decode-attention path runs on a single MI355X; DESIGN.md says how it would shard)",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -507,44 +850,25 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
         return
+    relay.load_library()
     if args.sys_scaling:
-        relay.load_library()
         sys_scaling(torch, relay, min(args.steps, 20))
         return
     if args.batch_sweep:
-        relay.load_library()
-        for B in BATCH_SWEEP:
-            spec = workloads.config_spec(2, 0).replace(batch=B)
-            r = point(torch, relay, spec, args, with_baseline=True)
-            print(json.dumps({"shape": "llama2_7b_mha", "batch": B, "sys_len": spec.sys_len,
-                              "relay_us_per_step": r["us_per_step"], "qtok_s": r["qtok_s"],
-                              "no_relay_us_per_step": r["no_relay_us_per_step"],
-                              "relay_speedup": r["relay_speedup"]}), flush=True)
-        # long request contexts dilute the gain: the system share of the bytes shrinks
-        for C in CTX_SWEEP:
-            spec = workloads.config_spec(2, 0).replace(ctx_len_dist="fixed", ctx_lo=C, ctx_hi=C)
-            r = point(torch, relay, spec, args, with_baseline=True)
-            L, B = spec.sys_len, spec.batch
-            print(json.dumps({"shape": "llama2_7b_mha", "batch": B, "sys_len": L, "ctx_len": C,
-                              "relay_us_per_step": r["us_per_step"], "qtok_s": r["qtok_s"],
-                              "no_relay_us_per_step": r["no_relay_us_per_step"],
-                              "relay_speedup": r["relay_speedup"],
-                              "kv_bytes_ratio": round(B * (L + C) / (L + B * C), 3)}), flush=True)
+        for p in batch_points(torch, relay, args, BATCH_SWEEP):
+            print(json.dumps(dict(shape="llama2_7b_mha", **p)), flush=True)
+        for p in ctx_points(torch, relay, args, CTX_POINTS):
+            print(json.dumps(dict(shape="llama2_7b_mha", batch=32, **p)), flush=True)
         return
-    relay.load_library()
     spec = workloads.config_spec(args.config, args.sweep_index)
     w = workloads.generate(spec)
     r = measure(torch, relay, w, args.steps, args.warmup, graph=not args.no_graph)
     print(f"[bench] {spec.name}: {1000 * r['ms_per_step']:.2f} us/step", file=sys.stderr, flush=True)
+    ceilings = None if args.no_sweep else measured_ceilings(torch)
     work = r["work"]
     ms = r["ms_per_step"]
     value = w.total_q / (ms * 1e-3)
-    kus = r["kernel_us"]
-    dom = max(kus, key=kus.get)
-    achieved = work[dom] / (kus[dom] * 1e-6) / 1e9
-    step_hbm_frac = work["step_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)
     peak_flops = (BF16_PEAK_TFLOPS if spec.dtype == "bf16" else FP32_PEAK_TFLOPS) * 1e12
-    step_mfma_frac = work["step_flops"] / (ms * 1e-3) / peak_flops
     line = {
         "metric": "decode-attn query-tokens/s/layer + % HBM roofline vs system-prompt length",
         "value": round(value, 1),
@@ -565,15 +889,17 @@ def main():
                    "sys_len": spec.sys_len, "total_q": w.total_q, "sum_ctx_len": int(w.ctx_lens.sum()),
                    "ctx_len_range": [int(w.ctx_lens.min()), int(w.ctx_lens.max())],
                    "parallelism": "single-gpu", "input_copies_rotated": r["n_sets"]},
-        "step_hbm_roofline_frac": round(step_hbm_frac, 4),
-        "step_mfma_roofline_frac": round(step_mfma_frac, 5),
+        "step_hbm_roofline_frac": round(work["step_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+        "step_mfma_roofline_frac": round(work["step_flops"] / (ms * 1e-3) / peak_flops, 5),
         "step_bytes_alg": work["step_bytes"],
-        "kernel_us": {k: round(v, 3) for k, v in kus.items()},
+        "partial_overhead_bytes": work.get("overhead"),
+        "kernel_us": {k: round(v, 3) for k, v in r["kernel_us"].items()},
         "plan": r["plan"],
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "bytes_alg_per_launch": work[dom], "traffic": stored_traffic(dom, spec.name)},
+        "roofline": roofline(r, spec, ceilings),
     }
+    if ceilings:
+        line["step_hbm_frac_of_measured_read"] = round(work["step_bytes"] / (ms * 1e-3) / (ceilings["read_GBps"] * 1e9),
+                                                       4)
     if not args.no_sweep and args.config == 2:
         line["sweep"] = {"workload": "llama30b_mha (batch 32, 52 heads, ctx 128)",
                          "points": [dict(sys_len=Ls, **point(torch, relay, workloads.config_spec(3, i), args,
@@ -581,14 +907,19 @@ def main():
                                     for i, Ls in enumerate(workloads.CONFIG3_SYS_LENS)]}
         line["other_configs"] = [point(torch, relay, workloads.config_spec(c, 0), args, with_baseline=True)
                                  for c in (1, 4, 5)]
+        line["batch_sweep"] = {"workload": "llama2_7b_mha shape, system 2048, contexts U[16, 512]",
+                               "points": batch_points(torch, relay, args, BATCH_POINTS)}
+        line["context_dilution"] = {"workload": "llama2_7b_mha shape, batch 32, system 2048, every context C",
+                                    "points": ctx_points(torch, relay, args, CTX_POINTS)}
     if not args.no_sweep:
         line["no_relay_baseline"] = no_relay_baseline(torch, relay, w, args, ms)
         line["rope_append"] = rope_append_time(torch, relay, w, args)
         line["system_prefill"] = [prefill_time(torch, relay, workloads.config_spec(c, 0), args) for c in (2, 4)]
-    if not args.no_sweep:
-        line["hbm_measured"] = measured_hbm(torch)
+        line["hbm_measured"] = ceilings
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        if not args.no_sweep:
+            line["oracle_single_thread"] = oracle_single_thread()
     print(json.dumps(line), flush=True)
 
 

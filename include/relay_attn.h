@@ -96,8 +96,9 @@
 extern "C" {
 #endif
 
-#define RELAY_ATTN_ABI_VERSION 3  /* 3: keys in slot order inside each 16-byte chunk of a tile; plan
-                                     fields of the streaming launch */
+#define RELAY_ATTN_ABI_VERSION 4  /* 3: keys in slot order inside each 16-byte chunk of a tile; plan
+                                     fields of the streaming launch.  4: relay_attn_decode_timed
+                                     takes kernel start/end event pairs */
 
 /* element types */
 #define RELAY_F32 0  /* IEEE float32 */
@@ -185,11 +186,14 @@ int relay_attn_decode(const relay_dims* dims, const void* q, const void* sys_k,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * relay_attn_decode with per-kernel timing: identical work, plus events[0..3]
- * (hipEvent_t handles created by the caller; any entry may be NULL) recorded on
- * `stream`: [0] first, [1] after a separate system-attention launch (right after
- * [0] when the steps share one launch), [2] after the attention launch, [3] after
- * relay_fuse.  For benchmarks; events must not be NULL.
+ * relay_attn_decode with per-kernel timing: identical work, plus six events
+ * (hipEvent_t handles created by the caller; any entry may be NULL) that the runtime
+ * stamps with the start and the end of the kernels themselves (not with the time a
+ * launch is enqueued): [0], [1] the separate system-attention kernel, [2], [3] the
+ * streaming attention launch (the first one's start and the last one's end when the
+ * requests take several), [4], [5] the merge.  Events of a kernel the call does not
+ * launch (no separate system kernel when at most 64 query rows share a KV head; see
+ * relay_get_plan) are left untouched.  For benchmarks; events must not be NULL.
  */
 int relay_attn_decode_timed(const relay_dims* dims, const void* q, const void* sys_k,
                             const void* sys_v, int32_t sys_len, const void* ctx_k_pages,

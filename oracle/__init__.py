@@ -92,6 +92,8 @@ def _declare(lib):
     lib.oracle_merge.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -195,3 +197,8 @@ def merge(os_: Sequence[np.ndarray], lses: Sequence[np.ndarray], lib=None):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the following oracle calls (timing only: results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))

@@ -327,6 +327,15 @@ void oracle_merge(int k, long n_rows, int d, const double* o, const double* lse,
   }
 }
 
+/* Threads of the following calls (a timing knob: the arithmetic is the same at any count). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int oracle_num_threads(void) {
   int n = 1;
 #ifdef _OPENMP

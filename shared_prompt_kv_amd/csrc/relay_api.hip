@@ -245,7 +245,7 @@ int hip_fail(hipError_t e, const char* what) {
 
 // The system kernel (sys_mode 2 or 3): one launch writing per-row run partials.
 int launch_sys_kernel(const relay_dims* d, const Plan& p, const void* q, const void* sys_k, const void* sys_v,
-                      int32_t sys_len, char* ws, hipStream_t s) {
+                      int32_t sys_len, char* ws, hipStream_t s, const relay::LaunchTiming* tm = nullptr) {
   if (!grid_ok(p.sys_wgs)) return fail(RELAY_ERR_INVALID, "system grid too large");
   SysArgs a;
   a.q = q;
@@ -266,8 +266,8 @@ int launch_sys_kernel(const relay_dims* d, const Plan& p, const void* q, const v
   a.total_steps = p.sys_total_steps;
   a.parts = p.sys_parts;
   a.causal = p.causal;
-  hipError_t e = p.sys_mode == 2 ? relay::launch_sys_attn_mfma(a, p.sys_wgs, s)
-                                 : relay::launch_sys_attn_tiled(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s);
+  hipError_t e = p.sys_mode == 2 ? relay::launch_sys_attn_mfma(a, p.sys_wgs, s, tm)
+                                 : relay::launch_sys_attn_tiled(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s, tm);
   return e == hipSuccess ? RELAY_OK : hip_fail(e, "system attention launch");
 }
 
@@ -275,7 +275,8 @@ int launch_sys_kernel(const relay_dims* d, const Plan& p, const void* q, const v
 // streams (with_ctx) of every request group.
 int launch_streams(const relay_dims* d, const Plan& p, bool with_sys, bool with_ctx, const void* q,
                    const void* sys_k, const void* sys_v, int32_t sys_len, const void* ck, const void* cv,
-                   const int32_t* bt, const int32_t* cl, const int32_t* cu, char* ws, hipStream_t s) {
+                   const int32_t* bt, const int32_t* cl, const int32_t* cu, char* ws, hipStream_t s,
+                   const relay::LaunchTiming* tm = nullptr) {
   const bool sys = with_sys && p.sys_mode == 1;
   if (!sys && !with_ctx) return RELAY_OK;
   StreamArgs a{};
@@ -318,7 +319,9 @@ int launch_streams(const relay_dims* d, const Plan& p, bool with_sys, bool with_
     ac.slot_base = (long long)c * p.ctx_slots_per_chunk;
     if (c > 0) ac.sys_steps = 0;  // the system streams go with the first request group
     const int rts = ac.sys_steps > 0 ? p.rts : 0;
-    hipError_t e = relay::launch_stream_attn(ac, rts, p.rtc, d->in_dtype, d->head_dim, p.grid, s);
+    // timing: the first launch's start and the last one's end
+    const relay::LaunchTiming tc{tm && c == 0 ? tm->start : nullptr, tm && c == launches - 1 ? tm->stop : nullptr};
+    hipError_t e = relay::launch_stream_attn(ac, rts, p.rtc, d->in_dtype, d->head_dim, p.grid, s, &tc);
     if (e != hipSuccess) return hip_fail(e, "streaming attention launch");
   }
   return RELAY_OK;
@@ -326,7 +329,7 @@ int launch_streams(const relay_dims* d, const Plan& p, bool with_sys, bool with_
 
 // The merge: every row's output (and LSE when lse_out is given) from its parts.
 int launch_merge(const relay_dims* d, const Plan& p, bool with_sys, bool with_ctx, char* ws, void* out, int out_bf16,
-                 float* lse_out, hipStream_t s) {
+                 float* lse_out, hipStream_t s, const relay::LaunchTiming* tm = nullptr) {
   MergeArgs m{};
   m.n_rows = (long long)d->total_q * d->num_q_heads;
   m.num_q_heads = d->num_q_heads;
@@ -355,7 +358,7 @@ int launch_merge(const relay_dims* d, const Plan& p, bool with_sys, bool with_ct
   m.out = out;
   m.lse_out = lse_out;
   m.out_bf16 = out_bf16;
-  hipError_t e = relay::launch_relay_merge(m, d->head_dim, s);
+  hipError_t e = relay::launch_relay_merge(m, d->head_dim, s, tm);
   return e == hipSuccess ? RELAY_OK : hip_fail(e, "merge launch");
 }
 
@@ -376,11 +379,11 @@ int check_ws(const Plan& p, void* ws, size_t bytes) {
   return RELAY_OK;
 }
 
-// Records events[i] (a hipEvent_t, may be NULL) on the stream; no-op without events.
-int record(void* const* events, int i, hipStream_t s) {
-  if (!events || !events[i]) return RELAY_OK;
-  hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
-  return e == hipSuccess ? RELAY_OK : hip_fail(e, "hipEventRecord");
+// Launch timing from the caller's events: pair k is events[2 k] (kernel start) and
+// events[2 k + 1] (kernel end); none without events.
+relay::LaunchTiming timing_pair(void* const* events, int k) {
+  if (!events) return relay::LaunchTiming{nullptr, nullptr};
+  return relay::LaunchTiming{static_cast<hipEvent_t>(events[2 * k]), static_cast<hipEvent_t>(events[2 * k + 1])};
 }
 
 int check_q_layout(const relay_dims* d, const int32_t* cu) {
@@ -490,16 +493,14 @@ static int decode_impl(const relay_dims* dims, const void* q, const void* sys_k,
   if ((rc = check_ws(p, workspace, workspace_bytes)) != RELAY_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  if ((rc = record(events, 0, s)) != RELAY_OK) return rc;
-  if (p.sys_mode >= 2 && (rc = launch_sys_kernel(dims, p, q, sys_k, sys_v, sys_len, ws, s)) != RELAY_OK) return rc;
-  if ((rc = record(events, 1, s)) != RELAY_OK) return rc;
+  const relay::LaunchTiming t_sys = timing_pair(events, 0), t_stream = timing_pair(events, 1),
+                            t_merge = timing_pair(events, 2);
+  if (p.sys_mode >= 2 && (rc = launch_sys_kernel(dims, p, q, sys_k, sys_v, sys_len, ws, s, &t_sys)) != RELAY_OK)
+    return rc;
   if ((rc = launch_streams(dims, p, true, true, q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables,
-                           ctx_lens, cu_q_lens, ws, s)) != RELAY_OK)
+                           ctx_lens, cu_q_lens, ws, s, &t_stream)) != RELAY_OK)
     return rc;
-  if ((rc = record(events, 2, s)) != RELAY_OK) return rc;
-  if ((rc = launch_merge(dims, p, sys_len > 0, true, ws, out, dims->out_dtype == RELAY_BF16, nullptr, s)) != RELAY_OK)
-    return rc;
-  return record(events, 3, s);
+  return launch_merge(dims, p, sys_len > 0, true, ws, out, dims->out_dtype == RELAY_BF16, nullptr, s, &t_merge);
 }
 
 int relay_attn_decode(const relay_dims* dims, const void* q, const void* sys_k, const void* sys_v,

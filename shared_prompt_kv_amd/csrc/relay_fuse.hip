@@ -189,17 +189,17 @@ __global__ __launch_bounds__(THREADS) void relay_merge_kernel(MergeArgs a) {
   if (a.lse_out && c4 == 0) a.lse_out[row] = (z > 0.f) ? (mx + __builtin_amdgcn_logf(z)) * kLn2 : neg_inf();
 }
 
-hipError_t launch_relay_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {
+hipError_t launch_relay_merge(const MergeArgs& a, int head_dim, hipStream_t stream, const LaunchTiming* tm) {
   const int threads = merge_threads(head_dim, a.n_rows);
   const long long per = threads / (head_dim / 4);
   const long long nwg = (a.n_rows + per - 1) / per;
   if (nwg < 1 || nwg >= (1LL << 31)) return hipErrorInvalidValue;
   if (head_dim == 64) {
-    if (threads == 256) hipLaunchKernelGGL((relay_merge_kernel<64, 256>), dim3(nwg), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((relay_merge_kernel<64, 64>), dim3(nwg), dim3(64), 0, stream, a);
+    if (threads == 256) launch_kernel(relay_merge_kernel<64, 256>, dim3(nwg), dim3(256), 0, stream, tm, a);
+    else launch_kernel(relay_merge_kernel<64, 64>, dim3(nwg), dim3(64), 0, stream, tm, a);
   } else {
-    if (threads == 256) hipLaunchKernelGGL((relay_merge_kernel<128, 256>), dim3(nwg), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((relay_merge_kernel<128, 64>), dim3(nwg), dim3(64), 0, stream, a);
+    if (threads == 256) launch_kernel(relay_merge_kernel<128, 256>, dim3(nwg), dim3(256), 0, stream, tm, a);
+    else launch_kernel(relay_merge_kernel<128, 64>, dim3(nwg), dim3(64), 0, stream, tm, a);
   }
   return hipGetLastError();
 }

@@ -1,11 +1,28 @@
 // Internal interface between the C-ABI host code and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace relay {
+
+// Optional timing of one launch: events the runtime stamps with the kernel's own start
+// and end (hipExtLaunchKernelGGL), not with the time the launch is enqueued.
+struct LaunchTiming {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                          const LaunchTiming* tm, Args... args) {
+  if (tm && (tm->start || tm->stop))
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, tm->start, tm->stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
 
 // sys_attn_tiled (large M): one launch over (row block, chunk, KV head) workgroups.
 struct SysArgs {
@@ -115,7 +132,7 @@ inline int stream_grid(int cus, int elem_bytes, int head_dim, int rts, int rtc) 
 
 size_t stream_lds_bytes(int n_req, int ctx_on, int sys_on, int head_dim);
 hipError_t launch_stream_attn(const StreamArgs& a, int rts, int rtc, int in_dtype, int head_dim, int grid,
-                              hipStream_t stream);
+                              hipStream_t stream, const LaunchTiming* tm = nullptr);
 
 // Row tiles per context stream for up to R query rows per (request, KV head).
 inline int ctx_rt_for(int rows_per_request) { return rows_per_request <= 16 ? 1 : 2; }
@@ -146,7 +163,7 @@ struct MergeArgs {
   float* lse_out;      // may be NULL
   int out_bf16;
 };
-hipError_t launch_relay_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_relay_merge(const MergeArgs& a, int head_dim, hipStream_t stream, const LaunchTiming* tm = nullptr);
 inline int merge_threads(int head_dim, long long n_rows) {
   return n_rows >= 2LL * 256 * (256 / (head_dim / 4)) ? 256 : 64;
 }
@@ -192,7 +209,7 @@ hipError_t launch_rope_system(void* sys_k, const float* cos_sin, int sys_len, in
                               hipStream_t s);
 
 hipError_t launch_sys_attn_tiled(const SysArgs& a, const SysConfig& c, int in_dtype, int head_dim,
-                                 int nwg, hipStream_t stream);
+                                 int nwg, hipStream_t stream, const LaunchTiming* tm = nullptr);
 
 // sys_attn_mfma (bf16, head_dim 128): workgroups of kSysMfmaRows query rows; designed
 // for two workgroups per CU (kSysMfmaSlots resident at once).
@@ -210,7 +227,7 @@ constexpr int kSysCausalRunsPerSlot = 4;  // causal plans: runs per resident wor
 inline __host__ __device__ int lean_part_of(long long x, int total, int parts) {
   return (int)(((x + 1) * parts + total - 1) / total) - 1;
 }
-hipError_t launch_sys_attn_mfma(const SysArgs& a, int nwg, hipStream_t stream);
+hipError_t launch_sys_attn_mfma(const SysArgs& a, int nwg, hipStream_t stream, const LaunchTiming* tm = nullptr);
 // relay_fuse workgroup size: one wave, or four once there are enough rows for two
 // four-wave workgroups per CU (D/4 lanes per row).
 inline int fuse_threads(int head_dim, long long n_rows) {

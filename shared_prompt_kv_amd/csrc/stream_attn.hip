@@ -501,35 +501,36 @@ size_t stream_lds_bytes(int n_req, int ctx_on, int sys_on, int head_dim) {
 }
 
 template <typename T, int D, int RTS, int RTC>
-static hipError_t launch_stream_t(const StreamArgs& a, int grid, hipStream_t s) {
+static hipError_t launch_stream_t(const StreamArgs& a, int grid, hipStream_t s, const LaunchTiming* tm) {
   const size_t lds = stream_lds_bytes(a.n_req, a.ctx_on, RTS > 0, D);
-  hipLaunchKernelGGL((stream_attn_kernel<T, D, RTS, RTC>), dim3(grid), dim3(kWave * strm::kWaves), lds, s, a);
+  launch_kernel(stream_attn_kernel<T, D, RTS, RTC>, dim3(grid), dim3(kWave * strm::kWaves), (uint32_t)lds, s, tm, a);
   return hipGetLastError();
 }
 
 template <typename T, int D, int RTS>
-static hipError_t launch_stream_c(const StreamArgs& a, int rtc, int grid, hipStream_t s) {
-  return rtc == 1 ? launch_stream_t<T, D, RTS, 1>(a, grid, s) : launch_stream_t<T, D, RTS, 2>(a, grid, s);
+static hipError_t launch_stream_c(const StreamArgs& a, int rtc, int grid, hipStream_t s, const LaunchTiming* tm) {
+  return rtc == 1 ? launch_stream_t<T, D, RTS, 1>(a, grid, s, tm) : launch_stream_t<T, D, RTS, 2>(a, grid, s, tm);
 }
 
 template <typename T, int D>
-static hipError_t launch_stream_d(const StreamArgs& a, int rts, int rtc, int grid, hipStream_t s) {
+static hipError_t launch_stream_d(const StreamArgs& a, int rts, int rtc, int grid, hipStream_t s,
+                                  const LaunchTiming* tm) {
   switch (rts) {
-    case 0: return launch_stream_c<T, D, 0>(a, rtc, grid, s);
-    case 1: return launch_stream_c<T, D, 1>(a, rtc, grid, s);
-    case 2: return launch_stream_c<T, D, 2>(a, rtc, grid, s);
-    default: return launch_stream_c<T, D, 4>(a, rtc, grid, s);
+    case 0: return launch_stream_c<T, D, 0>(a, rtc, grid, s, tm);
+    case 1: return launch_stream_c<T, D, 1>(a, rtc, grid, s, tm);
+    case 2: return launch_stream_c<T, D, 2>(a, rtc, grid, s, tm);
+    default: return launch_stream_c<T, D, 4>(a, rtc, grid, s, tm);
   }
 }
 
 hipError_t launch_stream_attn(const StreamArgs& a, int rts, int rtc, int in_dtype, int head_dim, int grid,
-                              hipStream_t stream) {
+                              hipStream_t stream, const LaunchTiming* tm) {
   if ((rts != 0 && rts != 1 && rts != 2 && rts != 4) || (rtc != 1 && rtc != 2)) return hipErrorInvalidValue;
   if (in_dtype == 1)
-    return head_dim == 64 ? launch_stream_d<bf16_t, 64>(a, rts, rtc, grid, stream)
-                          : launch_stream_d<bf16_t, 128>(a, rts, rtc, grid, stream);
-  return head_dim == 64 ? launch_stream_d<float, 64>(a, rts, rtc, grid, stream)
-                        : launch_stream_d<float, 128>(a, rts, rtc, grid, stream);
+    return head_dim == 64 ? launch_stream_d<bf16_t, 64>(a, rts, rtc, grid, stream, tm)
+                          : launch_stream_d<bf16_t, 128>(a, rts, rtc, grid, stream, tm);
+  return head_dim == 64 ? launch_stream_d<float, 64>(a, rts, rtc, grid, stream, tm)
+                        : launch_stream_d<float, 128>(a, rts, rtc, grid, stream, tm);
 }
 
 }  // namespace relay

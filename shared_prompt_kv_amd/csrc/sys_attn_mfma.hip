@@ -405,11 +405,11 @@ __global__ __launch_bounds__(mf::kThreads, 2) void sys_attn_mfma_kernel(SysArgs 
   }
 }
 
-hipError_t launch_sys_attn_mfma(const SysArgs& a, int nwg, hipStream_t stream) {
+hipError_t launch_sys_attn_mfma(const SysArgs& a, int nwg, hipStream_t stream, const LaunchTiming* tm) {
   if (a.causal)
-    hipLaunchKernelGGL(sys_attn_mfma_kernel<true>, dim3(nwg), dim3(mf::kThreads), kSysMfmaLds, stream, a);
+    launch_kernel(sys_attn_mfma_kernel<true>, dim3(nwg), dim3(mf::kThreads), (uint32_t)kSysMfmaLds, stream, tm, a);
   else
-    hipLaunchKernelGGL(sys_attn_mfma_kernel<false>, dim3(nwg), dim3(mf::kThreads), kSysMfmaLds, stream, a);
+    launch_kernel(sys_attn_mfma_kernel<false>, dim3(nwg), dim3(mf::kThreads), (uint32_t)kSysMfmaLds, stream, tm, a);
   return hipGetLastError();
 }
 

@@ -177,11 +177,11 @@ __global__ __launch_bounds__(kWave* WK* WR) void sys_attn_tiled_kernel(SysArgs a
 }
 
 template <typename T, int D, int RT, int WK, int WR, bool PSPLIT>
-static hipError_t launch_sys_t(const SysArgs& a, int nwg, hipStream_t stream) {
+static hipError_t launch_sys_t(const SysArgs& a, int nwg, hipStream_t stream, const LaunchTiming* tm) {
   constexpr size_t lds = (WK > 1) ? sizeof(float) * (size_t)WR * (WK / 2) * kWave * RT * (2 + D / 4) : 0;
   static_assert(lds <= 64 * 1024, "LDS budget");
-  hipLaunchKernelGGL((sys_attn_tiled_kernel<T, D, RT, WK, WR, PSPLIT>), dim3(nwg), dim3(kWave * WK * WR), lds,
-                     stream, a);
+  launch_kernel(sys_attn_tiled_kernel<T, D, RT, WK, WR, PSPLIT>, dim3(nwg), dim3(kWave * WK * WR), (uint32_t)lds,
+                stream, tm, a);
   return hipGetLastError();
 }
 
@@ -191,19 +191,19 @@ static hipError_t launch_sys_t(const SysArgs& a, int nwg, hipStream_t stream) {
 // single rounding costs up to 2^-9 of a probability, too much where one key holds much
 // of a row's weight.
 template <typename T, int D>
-static hipError_t launch_sys_d(const SysArgs& a, const SysConfig& c, int nwg, hipStream_t s) {
+static hipError_t launch_sys_d(const SysArgs& a, const SysConfig& c, int nwg, hipStream_t s, const LaunchTiming* tm) {
   if (c.rt != 2 || c.wk != 1 || c.wr != 4) return hipErrorInvalidValue;
-  return launch_sys_t<T, D, 2, 1, 4, true>(a, nwg, s);
+  return launch_sys_t<T, D, 2, 1, 4, true>(a, nwg, s, tm);
 }
 
 hipError_t launch_sys_attn_tiled(const SysArgs& a, const SysConfig& c, int in_dtype, int head_dim,
-                           int nwg, hipStream_t stream) {
+                                 int nwg, hipStream_t stream, const LaunchTiming* tm) {
   if (in_dtype == 1) {
-    return head_dim == 64 ? launch_sys_d<bf16_t, 64>(a, c, nwg, stream)
-                          : launch_sys_d<bf16_t, 128>(a, c, nwg, stream);
+    return head_dim == 64 ? launch_sys_d<bf16_t, 64>(a, c, nwg, stream, tm)
+                          : launch_sys_d<bf16_t, 128>(a, c, nwg, stream, tm);
   }
-  return head_dim == 64 ? launch_sys_d<float, 64>(a, c, nwg, stream)
-                        : launch_sys_d<float, 128>(a, c, nwg, stream);
+  return head_dim == 64 ? launch_sys_d<float, 64>(a, c, nwg, stream, tm)
+                        : launch_sys_d<float, 128>(a, c, nwg, stream, tm);
 }
 
 }  // namespace relay

@@ -310,14 +310,15 @@ def relay_attn_decode_noalloc(q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages
 
 def relay_attn_decode_timed(t: dict, out, workspace_buf, events, out_dtype=torch.float32,
                             stream=None):
-    """relay_attn_decode on a ``to_device`` dict, recording 4 raw hipEvent_t handles
-    (ints) between the kernels."""
+    """relay_attn_decode on a ``to_device`` dict; ``events`` holds 6 raw hipEvent_t
+    handles (ints or None) stamped with the start and end of the system kernel, the
+    streaming launch and the merge."""
     _require_device(t["q"], t["sys_k"], t["sys_v"], t["ctx_k_pages"], t["ctx_v_pages"], t["block_tables"],
                     t["ctx_lens"], t["cu_q_lens"], out, workspace_buf)
     check_decode_args(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], t["ctx_k_pages"], t["ctx_v_pages"],
                       t["block_tables"], t["ctx_lens"], t["cu_q_lens"], out, out_dtype)
     dims = dims_of(t, out_dtype)
-    ev = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) if e else None for e in events])
+    ev = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e) if e else None for e in events])
     _check(load_library().relay_attn_decode_timed(
         ctypes.byref(dims), _ptr(t["q"]), _ptr(t["sys_k"]), _ptr(t["sys_v"]), int(t["sys_len"]),
         _ptr(t["ctx_k_pages"]), _ptr(t["ctx_v_pages"]), _ptr(t["block_tables"]), _ptr(t["ctx_lens"]),
@@ -455,6 +456,35 @@ def relay_rope_append(dims: relay_dims, sys_len: int, q_new, k_new, v_new, cos_s
     return q_out
 
 
+class RopeAppendCall:
+    """A relay_rope_append call with its arguments checked and marshalled once (as
+    ``DecodeCall`` for the decode step): calling it is one ctypes call, so a serving
+    loop, or a benchmark, sees the kernel rather than the argument handling."""
+
+    def __init__(self, dims: relay_dims, sys_len: int, q_new, k_new, v_new, cos_sin, block_tables, ctx_lens,
+                 cu_q_lens, ctx_k_pages, ctx_v_pages, q_out):
+        _require_device(q_new, k_new, v_new, cos_sin, block_tables, ctx_lens, cu_q_lens, ctx_k_pages, ctx_v_pages,
+                        q_out)
+        for x in (q_new, k_new, v_new, ctx_k_pages, ctx_v_pages, q_out):
+            if x.dtype != q_new.dtype or not x.is_contiguous():
+                raise ValueError("q/k/v/pages must be contiguous and of one dtype")
+        if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or cos_sin.shape[1] != q_new.shape[-1]:
+            raise ValueError("cos_sin must be float32 [max_pos, head_dim]")
+        self._keep = (dims, q_new, k_new, v_new, cos_sin, block_tables, ctx_lens, cu_q_lens, ctx_k_pages,
+                      ctx_v_pages, q_out)
+        self._fn = load_library().relay_rope_append
+        self._args = (ctypes.byref(dims), int(sys_len), _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(cos_sin),
+                      cos_sin.shape[0], _ptr(block_tables), _ptr(ctx_lens), _ptr(cu_q_lens), _ptr(q_out),
+                      _ptr(ctx_k_pages), _ptr(ctx_v_pages))
+        self.q_out = q_out
+
+    def __call__(self, stream=None):
+        rc = self._fn(*self._args, _stream(stream))
+        if rc != RELAY_OK:
+            _check(rc)
+        return self.q_out
+
+
 def key_tile_shape(lead: tuple, d: int, dtype: torch.dtype) -> tuple:
     """Shape of key tiles: lead + (d/G, 16, G), G the elements of 16 bytes."""
     g = 8 if dtype == torch.bfloat16 else 4
@@ -563,8 +593,9 @@ class DecodeCall:
         return self.out
 
     def timed(self, events, stream=None):
-        """The same call, recording 4 raw hipEvent_t handles between the kernels."""
-        ev = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) if e else None for e in events])
+        """The same call; ``events``: 6 raw hipEvent_t handles, start and end of the system
+        kernel, the streaming launch and the merge."""
+        ev = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e) if e else None for e in events])
         rc = self._timed(*self._args, _stream(stream), ev)
         if rc != RELAY_OK:
             _check(rc)

@@ -56,7 +56,7 @@ def test_library_is_gfx950_only(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert R.relay_abi_version() == 3
+    assert R.relay_abi_version() == 4
     assert lib.relay_strerror(0) == b"ok"
     assert lib.relay_strerror(-3) == b"workspace too small"
 
