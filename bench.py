@@ -74,12 +74,13 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run torch's device copy of COPY_BYTES, 10 times (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
-    ap.add_argument("--summarize", choices=("stats", "traffic", "mfma"),
+    ap.add_argument("--summarize", choices=("stats", "traffic", "mfma", "sysbytes"),
                     help="write a profiles/ summary from rocprofv3 --output-format csv directories")
     ap.add_argument("--workload", default="", help="--summarize: workload name of the profiled run(s)")
     ap.add_argument("--dirs", nargs="*", default=[],
                     help="--summarize: rocprofv3 -d directories (stats: 1; traffic: fetch, write, copy "
-                         "fetch, copy write; mfma: one per workload, --workload lists them comma-separated)")
+                         "fetch, copy write; mfma: one per workload, --workload lists them comma-separated; "
+                         "sysbytes: the --sys-scaling FETCH_SIZE run, its stdout, the copy-calibration fetch run)")
     ap.add_argument("--commands", nargs="*", default=[], help="--summarize: the commands that made --dirs")
     return ap.parse_args()
 
@@ -174,6 +175,37 @@ def summarize(args):
             if best is None or t > best[1]:
                 best = (k, t)
         path = os.path.join(ROOT, "profiles", f"{best[0]}_{args.workload}_traffic.txt")
+    elif args.summarize == "sysbytes":
+        # dispatches of the system step in order; the cases of the --sys-scaling run in
+        # the order of its JSON lines, `dispatches` each
+        rows = [r for r in _csv(args.dirs[0], "counter_collection.csv")
+                if r["Counter_Name"] == "FETCH_SIZE" and short_name(r["Kernel_Name"]) in
+                ("stream_attn", "sys_attn_mfma", "sys_attn_tiled")]
+        per = {}
+        for r in rows:
+            per[int(r["Dispatch_Id"])] = per.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+        fetch = [per[k] for k in sorted(per)]
+        cases = [json.loads(l) for l in open(args.dirs[1]) if l.startswith("{")]
+        cfetch = _counters(args.dirs[2])[("copy", "FETCH_SIZE")]
+        fscale = COPY_BYTES / (sum(cfetch) / len(cfetch) * 1024)
+        lines = ["# System-KV bytes read from HBM by the system step vs batch size (RelayAttention reads the",
+                 "# shared system K/V once per batch).  FETCH_SIZE (KiB per dispatch) of the system step's",
+                 f"# kernel, scaled by {fscale:.4f} (what FETCH_SIZE reads for torch's 512 MiB device copy);",
+                 "# per case: 3 untimed + the timed calls of relay_sys_attn, the merge launch excluded;",
+                 "# sys_kv_bytes = 2 * H_kv * d * 2 B * L_s."]
+        lines += cmds + head
+        lines.append(f"{'shape':16s} {'batch':>6s} {'rows/kvh':>8s} {'kernel':15s} {'sys_kv_MB':>9s} "
+                     f"{'fetch_MB':>9s} {'fetch/kv':>8s}")
+        i = 0
+        for c in cases:
+            n = c["dispatches"]
+            f = fetch[i:i + n]
+            i += n
+            mb = sum(f) / len(f) * 1024 * fscale / 1e6
+            kv = c["sys_kv_bytes"] / 1e6
+            lines.append(f"{c['shape']:16s} {c['batch']:6d} {c['rows_per_kv_head']:8d} {c['kernel']:15s} "
+                         f"{kv:9.2f} {mb:9.2f} {mb / kv:8.3f}")
+        path = os.path.join(ROOT, "profiles", "sys_attn_kv_bytes_vs_batch.txt")
     else:
         lines = ["# Matrix-core utilisation: SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / "
                  "(GRBM_GUI_ACTIVE per XCD * 1024 SIMDs); GRBM_GUI_ACTIVE is reported summed over "
