@@ -39,8 +39,12 @@
  *    stated maxima) are the caller's; relay_validate() checks them on host copies.
  *    Kernels clamp indices so that violating them cannot read or write out of
  *    bounds, but the numbers are then unspecified.
- *  - Thread safety: no global mutable state; concurrent calls on different
- *    streams with disjoint outputs and workspaces are safe.
+ *  - Thread safety: the library's only process-wide state is written once per
+ *    device and read atomically: the device's compute-unit count (it sizes the
+ *    launches) and, for relay_attn_decode_noalloc, the device address of its static
+ *    scratch.  No environment variable is read.  Concurrent calls on different
+ *    streams with disjoint outputs and workspaces are safe; concurrent
+ *    relay_attn_decode_noalloc calls on one device share its scratch and race.
  *
  * Notation: B requests; request b has n_b new query tokens (T_q = sum n_b) and a
  * context of c_b tokens that INCLUDES its n_b new tokens (their K/V are already in
@@ -158,9 +162,10 @@ const char* relay_last_error(void);
 
 /*
  * Bytes of device workspace that relay_attn_decode, relay_sys_attn and
- * relay_ctx_attn need for these dimensions and system length (the partial
- * outputs and log-sum-exps of system chunks and context splits).  Returns 0 on
- * invalid dims (see relay_last_error()).
+ * relay_ctx_attn need for these dimensions and system length: the partial outputs
+ * and log-sum-exps of the streaming launch's pieces and of the system kernel's
+ * runs, and descriptors of where each row's pieces are.  Returns 0 on invalid dims
+ * (see relay_last_error()).
  */
 size_t relay_workspace_size(const relay_dims* dims, int32_t sys_len);
 
@@ -168,16 +173,20 @@ size_t relay_workspace_size(const relay_dims* dims, int32_t sys_len);
 int relay_get_plan(const relay_dims* dims, int32_t sys_len, relay_plan* plan);
 
 /*
- * The whole RelayAttention decode step: system attention (skipped when
- * sys_len == 0), context attention and relay fusion, written to out.
- * Equals exact causal attention of each query row over its visible
- * [system; context] keys.  Enqueued on `stream`: when at most 64 query rows
- * share a KV head, one launch that runs the system and context steps together,
- * then relay_fuse (2 launches); otherwise the matrix-core system kernel, the
- * context step and relay_fuse (3 launches).  relay_get_plan() says which.
- * workspace must hold
- * relay_workspace_size(dims, sys_len) bytes (256-byte aligned); its contents on
- * entry are irrelevant and on return unspecified.
+ * The whole RelayAttention decode step (RelayAttention paper page, Abstract: the
+ * system KV read once per batch, then combined with each request's own attention;
+ * atyun.com article, section "RelayAttention": the three steps and their exact
+ * equivalence to attention over the concatenated cache): system attention (skipped
+ * when sys_len == 0), context attention and relay fusion, written to out.  Equals
+ * exact causal attention of each query row over its visible [system; context] keys.
+ * Enqueued on `stream`: when at most 64 query rows share a KV head, one streaming
+ * launch that runs the system and context steps together (per group of at most
+ * relay_plan.stream_max_requests requests), then the merge (2 launches for up to
+ * that many requests); otherwise the matrix-core system kernel first (3 launches).
+ * relay_get_plan() says which.  workspace must hold relay_workspace_size(dims,
+ * sys_len) bytes (256-byte aligned): the partial results and where they are; its
+ * contents on entry are irrelevant (nothing in it needs to start at zero) and on
+ * return unspecified.
  */
 int relay_attn_decode(const relay_dims* dims, const void* q, const void* sys_k,
                       const void* sys_v, int32_t sys_len, const void* ctx_k_pages,
@@ -222,10 +231,14 @@ int relay_attn_decode_noalloc(const relay_dims* dims, const void* q, const void*
                               void* stream);
 
 /*
- * System-attention step alone (RelayAttention's first step): for every query row,
- * attention over the system keys only.  o_sys: float32 [T_q, H_q, d]; lse_sys:
- * float32 [T_q, H_q].  sys_len == 0 gives o_sys = 0 and lse_sys = -inf.  Enqueues
- * sys_attn and a relay_fuse that merges the chunk partials.
+ * System-attention step alone (atyun.com article, section "RelayAttention", first
+ * step: every request's query rows against the shared system keys, the per-request
+ * matrix-vector products grouped into matrix-matrix products; linnk.ai summary,
+ * section "Deeper Inquiries"): for every query row, attention over the system keys
+ * only.  o_sys: float32 [T_q, H_q, d]; lse_sys: float32 [T_q, H_q].  sys_len == 0
+ * gives o_sys = 0 and lse_sys = -inf.  Enqueues the system step (the streaming
+ * launch's system streams at <= 64 rows per KV head, else the matrix-core system
+ * kernel) and the merge of its partials.
  */
 int relay_sys_attn(const relay_dims* dims, const void* q, const void* sys_k, const void* sys_v,
                    int32_t sys_len, float* o_sys, float* lse_sys, void* workspace,
@@ -258,10 +271,12 @@ int relay_prefill_attn(const relay_dims* dims, const void* q, const void* sys_k,
                        size_t workspace_bytes, void* stream);
 
 /*
- * Context-attention step alone (RelayAttention's second step): for every query
- * row, causal attention over its request's visible context keys only.
- * o_ctx / lse_ctx as for relay_sys_attn.  Enqueues ctx_attn and a relay_fuse
- * that merges the split partials.
+ * Context-attention step alone (atyun.com article, section "RelayAttention",
+ * second step: each request against its own keys in the paged cache, as
+ * PagedAttention does; linnk.ai summary, section "Abstract"): for every query row,
+ * causal attention over its request's visible context keys only.  o_ctx / lse_ctx
+ * as for relay_sys_attn.  Enqueues the streaming launch's context streams and the
+ * merge of their pieces.
  */
 int relay_ctx_attn(const relay_dims* dims, const void* q, const void* ctx_k_pages,
                    const void* ctx_v_pages, const int32_t* block_tables,
@@ -269,8 +284,11 @@ int relay_ctx_attn(const relay_dims* dims, const void* q, const void* ctx_k_page
                    float* lse_ctx, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Relay fusion alone (RelayAttention's third step) over n_rows rows of head_dim
- * values: out = alpha_sys * o_sys + alpha_ctx * o_ctx with the LSE weights above.
+ * Relay fusion alone (atyun.com article, section "RelayAttention", third step: the
+ * two intermediate outputs averaged with weights from their log-sum-exp normalisers;
+ * linnk.ai summary, section "Abstract": a convex combination) over n_rows rows of
+ * head_dim values: out = alpha_sys * o_sys + alpha_ctx * o_ctx with the LSE weights
+ * above.
  * o_*: float32 [n_rows, head_dim]; lse_*: float32 [n_rows]; a part with LSE = -inf
  * has weight 0.  out: [n_rows, head_dim] of out_dtype.  lse_out (may be NULL):
  * float32 [n_rows], ln(e^lse_sys + e^lse_ctx).  head_dim: 64 or 128.
