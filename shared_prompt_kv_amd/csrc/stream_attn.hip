@@ -107,21 +107,30 @@ __device__ void build_tables(const StreamArgs& a, const ReqTables& t, int* scrat
     t.pre[i] = w;  // the weight, turned into the prefix below
     sum += w;
   }
-  scratch[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan of the thread sums
-    const int x = tid >= off ? scratch[tid - off] : 0;
-    __syncthreads();
-    scratch[tid] += x;
-    __syncthreads();
+  // inclusive scan of the thread sums: inside each wave by shuffles, then over the
+  // wave totals (one barrier)
+  const int lane = lane_id(), wave = tid / kWave;
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
   }
-  int run = tid ? scratch[tid - 1] : 0;
+  if (lane == kWave - 1) scratch[wave] = incl;
+  __syncthreads();
+  int base = 0, all = 0;
+#pragma unroll
+  for (int k = 0; k < strm::kWaves; ++k) {
+    base += k < wave ? scratch[k] : 0;
+    all += scratch[k];
+  }
+  int run = base + incl - sum;  // exclusive prefix of this thread's first request
   for (int i = i0; i < i1; ++i) {
     const int w = t.pre[i];
     t.pre[i] = run;
     run += w;
   }
-  if (tid == kThreads - 1) t.pre[n] = scratch[kThreads - 1];
+  if (tid == kThreads - 1) t.pre[n] = all;
   __syncthreads();
 }
 
