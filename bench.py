@@ -275,7 +275,9 @@ def work_of(w, plan=None):
     tables = 4 * B * (mb + 2) + (4 * (B + 1) if int(w.q_lens.max()) > 1 else 0)
     ql, cl = w.q_lens.astype(int), w.ctx_lens.astype(int)
     vis = int((ql * cl - ql * (ql - 1) // 2).sum())      # visible context keys over all query tokens
-    sys_in_stream = plan is None or plan["sys_mode"] == 1
+    # the system K/V are read by the streaming launch (system streams, or the matrix-core
+    # system workgroups inside it)
+    sys_in_stream = plan is None or plan["sys_mode"] in (1, 4)
     work = {
         "step_bytes": kv_sys + kv_ctx + q_bytes + out_bytes + tables,
         "step_flops": 4 * Hq * d * (Tq * s.sys_len + vis),
@@ -333,8 +335,9 @@ def partial_overhead(w, plan):
         written_sys = plan["sys_runs"] * rows * row_b
     else:
         written_sys = 0
-    return {"stream_attn_partials_written": written + (written_sys if sys_mode == 1 else 0),
-            "sys_kernel_partials_written": written_sys if sys_mode >= 2 else 0,
+    in_stream = sys_mode in (1, 4)
+    return {"stream_attn_partials_written": written + (written_sys if in_stream else 0),
+            "sys_kernel_partials_written": 0 if in_stream else written_sys,
             "merge_extra_partial_reads": max(0, written + written_sys - 2 * rows * row_b)}
 
 
@@ -637,6 +640,10 @@ def point(torch, relay, spec, args, with_baseline=False, steps=50):
     sk = sys_kernel_name(rr["plan"])
     if sk == "sys_attn_mfma" and sk in rr["kernel_us"]:
         out["sys_attn_mfma_frac"] = round(work["sys_flops"] / (rr["kernel_us"][sk] * 1e-6) / peak, 4)
+    if rr["plan"]["sys_mode"] == 4:  # system flops over the launch that holds them
+        out["stream_attn_mfma_frac"] = round(work["sys_flops"] / (rr["kernel_us"]["stream_attn"] * 1e-6) / peak, 4)
+        out["stream_attn_hbm_frac"] = round(work["stream_attn"] / (rr["kernel_us"]["stream_attn"] * 1e-6)
+                                            / (HBM_PEAK_GBS * 1e9), 4)
     if with_baseline:
         out.update(no_relay_baseline(torch, relay, w, args, m))
     return out
@@ -833,6 +840,10 @@ def roofline(r, spec, ceilings):
     dom = max(kus, key=kus.get)
     us = kus[dom]
     mfma = dom == "sys_attn_mfma"
+    if dom == "stream_attn" and plan["sys_mode"] == 4:
+        # the matrix-core system workgroups and the context streams in one launch: the
+        # roofline is whichever of the two bounds takes longer
+        mfma = work["sys_flops"] / (BF16_PEAK_TFLOPS * 1e12) > work["stream_attn"] / (HBM_PEAK_GBS * 1e9)
     if mfma:
         alg, unit, peak = work["sys_flops"], "TFLOP/s", BF16_PEAK_TFLOPS
         achieved = alg / (us * 1e-6) / 1e12

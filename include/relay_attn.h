@@ -137,11 +137,14 @@ typedef struct {
 typedef struct {
   int32_t sys_mode;            /* 0: no system step; 1: system streams inside the streaming launch
                                   (at most 64 stacked query rows per KV head); 2: the matrix-core
-                                  system kernel runs first (bf16, head_dim 128); 3: the tiled system
-                                  kernel runs first (fp32 or head_dim 64) */
+                                  system kernel runs first (bf16, head_dim 128; the system step
+                                  alone); 3: the tiled system kernel runs first (fp32 or head_dim
+                                  64); 4: the matrix-core system workgroups inside the first
+                                  streaming launch, beside the context workgroups (the decode step,
+                                  bf16, head_dim 128, more than 64 rows per KV head) */
   int32_t sys_row_tiles;       /* sys_mode 1: 16-row tiles of one system stream */
-  int32_t sys_runs;            /* sys_mode 2, 3: partial slots per row written by the system kernel */
-  int32_t sys_wgs;             /* sys_mode 2, 3: workgroups of the system kernel */
+  int32_t sys_runs;            /* sys_mode 2, 3, 4: partial slots per row written by the system kernel */
+  int32_t sys_wgs;             /* sys_mode 2, 3, 4: workgroups of the system kernel */
   int32_t ctx_row_tiles;       /* 16-row tiles of one context stream */
   int32_t ctx_row_blocks;      /* context streams per (request, KV head) */
   int32_t stream_waves;        /* waves of one streaming launch; each streams an equal share of the steps */
@@ -179,11 +182,12 @@ int relay_get_plan(const relay_dims* dims, int32_t sys_len, relay_plan* plan);
  * equivalence to attention over the concatenated cache): system attention (skipped
  * when sys_len == 0), context attention and relay fusion, written to out.  Equals
  * exact causal attention of each query row over its visible [system; context] keys.
- * Enqueued on `stream`: when at most 64 query rows share a KV head, one streaming
- * launch that runs the system and context steps together (per group of at most
- * relay_plan.stream_max_requests requests), then the merge (2 launches for up to
- * that many requests); otherwise the matrix-core system kernel first (3 launches).
- * relay_get_plan() says which.  workspace must hold relay_workspace_size(dims,
+ * Enqueued on `stream`: one streaming launch that runs the system and context steps
+ * together (per group of at most relay_plan.stream_max_requests requests), then the
+ * merge (2 launches for up to that many requests).  At most 64 query rows per KV head
+ * take the system step as streams of the launch; more rows take it as matrix-core
+ * workgroups of the launch's first group (bf16, head_dim 128), or as a system kernel
+ * before it (3 launches: fp32 or head_dim 64).  relay_get_plan() says which.  workspace must hold relay_workspace_size(dims,
  * sys_len) bytes (256-byte aligned): the partial results and where they are; its
  * contents on entry are irrelevant (nothing in it needs to start at zero) and on
  * return unspecified.

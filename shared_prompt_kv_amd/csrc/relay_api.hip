@@ -115,7 +115,8 @@ int check_dims(const relay_dims* d, int32_t sys_len) {
 int clamp_int(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // The system kernel's plan (M > 64 stacked rows per KV head).
-void plan_system_kernel(const relay_dims* d, int32_t sys_len, int M, Plan* p) {
+// slots: workgroups of the system kernel resident at once (the launch is cut to fill them).
+void plan_system_kernel(const relay_dims* d, int32_t sys_len, int M, Plan* p, long long slots = relay::kSysMfmaSlots) {
   if (d->in_dtype == RELAY_BF16 && d->head_dim == 128) {
     p->sys_mode = 2;
     p->sys_row_blocks = ceil_div(M, relay::kSysMfmaRows);
@@ -124,7 +125,7 @@ void plan_system_kernel(const relay_dims* d, int32_t sys_len, int M, Plan* p) {
     p->sys_steps_per_head = ceil_div(sys_len, relay::kSysMfmaStep);
     const long long S = (long long)p->sys_steps_per_head * d->num_kv_heads;
     p->sys_total_steps = (int)S;
-    long long parts = relay::kSysMfmaSlots / p->sys_row_blocks;
+    long long parts = slots / p->sys_row_blocks;
     // causal: a row block's work grows with its tokens, so the runs are cut finer
     // and the workgroups of early row blocks, which finish first, free their slots
     if (p->causal) parts *= relay::kSysCausalRunsPerSlot;
@@ -159,6 +160,19 @@ void plan_system_kernel(const relay_dims* d, int32_t sys_len, int M, Plan* p) {
   }
 }
 
+// Whether the decode step's matrix-core system workgroups should share the CUs with the
+// context streams (one of each per CU) rather than run first at two per CU: yes unless
+// the system step's matrix-core time exceeds twice the context step's memory time
+// (then the co-run's halved matrix-core occupancy costs more than the overlap saves).
+// The context bytes are estimated from max_ctx_len (the lengths are device data): half
+// of it per request.
+bool corun_pays(const relay_dims* d, int32_t sys_len) {
+  const double sys_flops = 4.0 * d->num_q_heads * d->head_dim * (double)d->total_q * sys_len;
+  const double ctx_bytes = 4.0 * d->num_kv_heads * d->head_dim * (double)d->batch * (d->max_ctx_len / 2.0 + 16.0);
+  const double t_sys = sys_flops / relay::kSysMfmaFlopsPerS, t_ctx = ctx_bytes / relay::kStreamBytesPerS;
+  return t_ctx > 0.5 * t_sys;
+}
+
 // Fills *p for dims and sys_len (need: what the call computes).  Returns RELAY_OK or
 // an error for sizes one streaming launch cannot index.
 int make_plan(const relay_dims* d, int32_t sys_len, Plan* p, Need need = kDecode) {
@@ -185,6 +199,11 @@ int make_plan(const relay_dims* d, int32_t sys_len, Plan* p, Need need = kDecode
       const int tiles = ceil_div(M, 16);
       p->rts = tiles <= 2 ? tiles : 4;
       p->sys_steps = ceil_div(sys_len, 32);
+    } else if (need == kDecode && d->in_dtype == RELAY_BF16 && D == 128 && corun_pays(d, sys_len)) {
+      // the matrix-core system workgroups inside the streaming launch, one per CU beside
+      // one context workgroup per CU
+      plan_system_kernel(d, sys_len, M, p, device_cus());
+      p->sys_mode = 4;
     } else {
       plan_system_kernel(d, sys_len, M, p);
     }
@@ -194,8 +213,10 @@ int make_plan(const relay_dims* d, int32_t sys_len, Plan* p, Need need = kDecode
   const long long R = (long long)d->max_q_len * g;
   p->rtc = relay::ctx_rt_for((int)R);
   p->ctx_rb = ceil_div(R, 16 * p->rtc);
-  // one or two workgroups per CU (what the launch's instantiation is built for)
-  p->grid = relay::stream_grid(device_cus(), d->in_dtype == RELAY_BF16 ? 2 : 4, D, p->rts, p->rtc);
+  // one or two workgroups per CU (what the launch's instantiation is built for); one
+  // per CU beside the system workgroups
+  p->grid = p->sys_mode == 4 ? device_cus()
+                             : relay::stream_grid(device_cus(), d->in_dtype == RELAY_BF16 ? 2 : 4, D, p->rts, p->rtc);
   p->workers = p->grid * relay::kStreamWaves;
   if (p->sys_mode == 1) p->sys_slots = (long long)d->num_kv_heads + p->grid;
   const int cap = d->max_ctx_len < d->max_blocks_per_seq * 16 ? d->max_ctx_len : d->max_blocks_per_seq * 16;
@@ -212,7 +233,7 @@ int make_plan(const relay_dims* d, int32_t sys_len, Plan* p, Need need = kDecode
   p->ctx_slots = p->ctx_slots_per_chunk * p->n_chunks;
   // ---- merge
   p->merge_wgs = ceil_div(rows, relay::merge_threads(D, rows) / (D / 4));
-  p->launches = (p->sys_mode >= 2 ? 1 : 0) + p->n_chunks + 1;
+  p->launches = (p->sys_mode == 2 || p->sys_mode == 3 ? 1 : 0) + p->n_chunks + 1;
   // ---- workspace (fp32 partials, 256-byte aligned regions)
   if (p->sys_mode == 1) {
     p->off_sys_o = off;
@@ -244,9 +265,8 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 // The system kernel (sys_mode 2 or 3): one launch writing per-row run partials.
-int launch_sys_kernel(const relay_dims* d, const Plan& p, const void* q, const void* sys_k, const void* sys_v,
-                      int32_t sys_len, char* ws, hipStream_t s, const relay::LaunchTiming* tm = nullptr) {
-  if (!grid_ok(p.sys_wgs)) return fail(RELAY_ERR_INVALID, "system grid too large");
+SysArgs system_args(const relay_dims* d, const Plan& p, const void* q, const void* sys_k, const void* sys_v,
+                    int32_t sys_len, char* ws) {
   SysArgs a;
   a.q = q;
   a.sys_k = sys_k;
@@ -266,17 +286,27 @@ int launch_sys_kernel(const relay_dims* d, const Plan& p, const void* q, const v
   a.total_steps = p.sys_total_steps;
   a.parts = p.sys_parts;
   a.causal = p.causal;
-  hipError_t e = p.sys_mode == 2 ? relay::launch_sys_attn_mfma(a, p.sys_wgs, s, tm)
-                                 : relay::launch_sys_attn_tiled(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s, tm);
+  return a;
+}
+
+// The system kernel as a launch of its own (sys_mode 2, 3; sys_mode 4's workgroups when
+// the system step runs alone).
+int launch_sys_kernel(const relay_dims* d, const Plan& p, const void* q, const void* sys_k, const void* sys_v,
+                      int32_t sys_len, char* ws, hipStream_t s, const relay::LaunchTiming* tm = nullptr) {
+  if (!grid_ok(p.sys_wgs)) return fail(RELAY_ERR_INVALID, "system grid too large");
+  const SysArgs a = system_args(d, p, q, sys_k, sys_v, sys_len, ws);
+  hipError_t e = p.sys_mode == 3 ? relay::launch_sys_attn_tiled(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s, tm)
+                                 : relay::launch_sys_attn_mfma(a, p.sys_wgs, s, tm);
   return e == hipSuccess ? RELAY_OK : hip_fail(e, "system attention launch");
 }
 
 // The streaming launches: the system streams (sys_mode 1, with_sys) and the context
-// streams (with_ctx) of every request group.
+// streams (with_ctx) of every request group; co_sys (sys_mode 4): the system kernel's
+// workgroups go with the first request group's launch.
 int launch_streams(const relay_dims* d, const Plan& p, bool with_sys, bool with_ctx, const void* q,
                    const void* sys_k, const void* sys_v, int32_t sys_len, const void* ck, const void* cv,
                    const int32_t* bt, const int32_t* cl, const int32_t* cu, char* ws, hipStream_t s,
-                   const relay::LaunchTiming* tm = nullptr) {
+                   const relay::LaunchTiming* tm = nullptr, const SysArgs* co_sys = nullptr) {
   const bool sys = with_sys && p.sys_mode == 1;
   if (!sys && !with_ctx) return RELAY_OK;
   StreamArgs a{};
@@ -321,7 +351,17 @@ int launch_streams(const relay_dims* d, const Plan& p, bool with_sys, bool with_
     const int rts = ac.sys_steps > 0 ? p.rts : 0;
     // timing: the first launch's start and the last one's end
     const relay::LaunchTiming tc{tm && c == 0 ? tm->start : nullptr, tm && c == launches - 1 ? tm->stop : nullptr};
-    hipError_t e = relay::launch_stream_attn(ac, rts, p.rtc, d->in_dtype, d->head_dim, p.grid, s, &tc);
+    hipError_t e;
+    if (co_sys && c == 0) {
+      if (!grid_ok((long long)p.sys_wgs + p.grid)) return fail(RELAY_ERR_INVALID, "grid too large");
+      relay::CoArgs co;
+      co.sys = *co_sys;
+      co.str = ac;
+      co.n_sys = p.sys_wgs;
+      e = relay::launch_stream_sys(co, p.rtc, p.sys_wgs + p.grid, s, &tc);
+    } else {
+      e = relay::launch_stream_attn(ac, rts, p.rtc, d->in_dtype, d->head_dim, p.grid, s, &tc);
+    }
     if (e != hipSuccess) return hip_fail(e, "streaming attention launch");
   }
   return RELAY_OK;
@@ -449,9 +489,11 @@ const char* relay_last_error(void) { return g_err; }
 
 size_t relay_workspace_size(const relay_dims* dims, int32_t sys_len) {
   if (check_dims(dims, sys_len) != RELAY_OK) return 0;
-  Plan p;
+  Plan p, pc;
   if (make_plan(dims, sys_len, &p) != RELAY_OK) return 0;
-  return p.ws_bytes;
+  // relay_ctx_attn plans the context streams alone (two workgroups per CU)
+  if (make_plan(dims, 0, &pc) != RELAY_OK) return 0;
+  return p.ws_bytes > pc.ws_bytes ? p.ws_bytes : pc.ws_bytes;
 }
 
 int relay_get_plan(const relay_dims* dims, int32_t sys_len, relay_plan* out) {
@@ -495,10 +537,12 @@ static int decode_impl(const relay_dims* dims, const void* q, const void* sys_k,
   char* ws = static_cast<char*>(workspace);
   const relay::LaunchTiming t_sys = timing_pair(events, 0), t_stream = timing_pair(events, 1),
                             t_merge = timing_pair(events, 2);
-  if (p.sys_mode >= 2 && (rc = launch_sys_kernel(dims, p, q, sys_k, sys_v, sys_len, ws, s, &t_sys)) != RELAY_OK)
+  if ((p.sys_mode == 2 || p.sys_mode == 3) &&
+      (rc = launch_sys_kernel(dims, p, q, sys_k, sys_v, sys_len, ws, s, &t_sys)) != RELAY_OK)
     return rc;
+  const SysArgs co = p.sys_mode == 4 ? system_args(dims, p, q, sys_k, sys_v, sys_len, ws) : SysArgs{};
   if ((rc = launch_streams(dims, p, true, true, q, sys_k, sys_v, sys_len, ctx_k_pages, ctx_v_pages, block_tables,
-                           ctx_lens, cu_q_lens, ws, s, &t_stream)) != RELAY_OK)
+                           ctx_lens, cu_q_lens, ws, s, &t_stream, p.sys_mode == 4 ? &co : nullptr)) != RELAY_OK)
     return rc;
   return launch_merge(dims, p, sys_len > 0, true, ws, out, dims->out_dtype == RELAY_BF16, nullptr, s, &t_merge);
 }

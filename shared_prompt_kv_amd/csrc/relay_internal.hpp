@@ -125,6 +125,15 @@ struct StreamArgs {
   int n_workers;       // waves of the launch (grid * kStreamWaves)
 };
 
+// The decode step's launch of matrix-core system workgroups (the first n_sys) beside the
+// context streams' workgroups (stream_attn.hip).
+struct CoArgs {
+  SysArgs sys;
+  StreamArgs str;
+  int n_sys;
+};
+hipError_t launch_stream_sys(const CoArgs& a, int rtc, int grid, hipStream_t stream, const LaunchTiming* tm = nullptr);
+
 // Workgroups of one streaming launch for this instantiation on a device with `cus` CUs.
 inline int stream_grid(int cus, int elem_bytes, int head_dim, int rts, int rtc) {
   return cus * stream_wgs_per_cu(elem_bytes, head_dim, rts, rtc);
@@ -216,6 +225,11 @@ hipError_t launch_sys_attn_tiled(const SysArgs& a, const SysConfig& c, int in_dt
 constexpr int kSysMfmaRows = 128;
 constexpr int kSysMfmaSlots = 512;
 constexpr int kSysMfmaStep = 64;
+// Rates the decode plan weighs the system step's matrix-core time against the context
+// step's memory time with (measured on MI355X: the system kernel at two workgroups per CU
+// runs at about 0.9 PFLOP/s, the streaming launch at about 4.5 TB/s).
+constexpr double kSysMfmaFlopsPerS = 0.9e15;
+constexpr double kStreamBytesPerS = 4.5e12;
 // Partials in which some row sees fewer than this many keys compute P.V with P split
 // into bf16 hi + lo (two products): there single probabilities can be large and bf16
 // rounding of P alone would cost up to 2^-9 of the output.  Where every row sees many

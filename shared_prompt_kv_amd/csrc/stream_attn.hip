@@ -35,6 +35,7 @@
 // of a row with the same log-sum-exp identity that relay fusion uses.
 #include "relay_device.hpp"
 #include "relay_internal.hpp"
+#include "sys_attn_mfma.hpp"
 
 namespace relay {
 
@@ -459,11 +460,10 @@ __host__ __device__ constexpr size_t stream_tables_bytes(int n) {
   return (sizeof(int) * ((size_t)4 * n + 1 + (size_t)kWave * kStreamWaves) + 15) / 16 * 16;
 }
 
+// Streaming workgroup w of the launch's streaming workgroups (lds_tab: its LDS).
 template <typename T, int D, int RTS, int RTC>
-__global__ __launch_bounds__(kWave* strm::kWaves, (stream_occ<T, D, RTS, RTC>())) void stream_attn_kernel(
-    StreamArgs a) {
+__device__ __forceinline__ void stream_workgroup(const StreamArgs& a, int w, int* lds_tab) {
   constexpr int OCC = stream_occ<T, D, RTS, RTC>();
-  extern __shared__ int lds_tab[];
   const int n = a.ctx_on ? a.n_req : 0;
   ReqTables t{lds_tab, lds_tab + n + 1, lds_tab + 2 * n + 1, lds_tab + 3 * n + 1};
   long long Tc = 0;
@@ -477,7 +477,6 @@ __global__ __launch_bounds__(kWave* strm::kWaves, (stream_occ<T, D, RTS, RTC>())
   // so that every wave of the partition holds at least one step and the pieces of a
   // stream sit on consecutive waves (and workgroups)
   const int W = total < a.n_workers ? (int)total : a.n_workers;
-  const int w = blockIdx.x;
   const int wk = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int v = w * strm::kWaves + wk;
   if (total == 0 || w * strm::kWaves >= W) return;  // uniform over the workgroup
@@ -502,6 +501,37 @@ __global__ __launch_bounds__(kWave* strm::kWaves, (stream_occ<T, D, RTS, RTC>())
     const long long y0 = (x0 > Ts ? x0 : Ts) - Ts, y1 = x1 - Ts;
     context_range<T, D, RTC, OCC>(a, t, y0, y1, Ts, v, total, W);
   }
+}
+
+template <typename T, int D, int RTS, int RTC>
+__global__ __launch_bounds__(kWave* strm::kWaves, (stream_occ<T, D, RTS, RTC>())) void stream_attn_kernel(
+    StreamArgs a) {
+  extern __shared__ int lds_tab[];
+  stream_workgroup<T, D, RTS, RTC>(a, blockIdx.x, lds_tab);
+}
+
+// The decode step with more than 64 stacked rows per KV head (bf16, head_dim 128): the
+// matrix-core system workgroups (the first a.n_sys of the launch, compute-bound) and the
+// context streams' workgroups (memory-bound) in one launch, one of each per CU, so
+// each CU's matrix cores and its memory stream work at the same time.
+template <int RTC>
+__global__ __launch_bounds__(kWave* strm::kWaves, 2) void stream_sys_kernel(CoArgs a) {
+  extern __shared__ __attribute__((aligned(16))) int lds_tab[];
+  if ((int)blockIdx.x < a.n_sys)
+    sys_mfma_workgroup<false>(a.sys, blockIdx.x, a.n_sys, reinterpret_cast<char*>(lds_tab));
+  else
+    stream_workgroup<bf16_t, 128, 0, RTC>(a.str, blockIdx.x - a.n_sys, lds_tab);
+}
+
+hipError_t launch_stream_sys(const CoArgs& a, int rtc, int grid, hipStream_t s, const LaunchTiming* tm) {
+  static_assert(stream_wgs_per_cu(2, 128, 0, 1) == 2 && stream_wgs_per_cu(2, 128, 0, 2) == 2,
+                "the context workgroups are built for two per CU");
+  if (rtc != 1 && rtc != 2) return hipErrorInvalidValue;
+  const size_t lds = stream_lds_bytes(a.str.n_req, a.str.ctx_on, 0, 128);
+  const uint32_t bytes = (uint32_t)(lds > kSysMfmaLds ? lds : kSysMfmaLds);
+  if (rtc == 1) launch_kernel(stream_sys_kernel<1>, dim3(grid), dim3(kWave * strm::kWaves), bytes, s, tm, a);
+  else launch_kernel(stream_sys_kernel<2>, dim3(grid), dim3(kWave * strm::kWaves), bytes, s, tm, a);
+  return hipGetLastError();
 }
 
 size_t stream_lds_bytes(int n_req, int ctx_on, int sys_on, int head_dim) {

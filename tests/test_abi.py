@@ -115,6 +115,16 @@ def test_pointer_and_workspace_errors(lib):
 CUS = 256          # no GPU here: the library plans for 256 compute units
 
 
+def corun(d, sys_len):
+    """The plan's choice for the decode step's matrix-core system workgroups (bf16, d = 128,
+    > 64 rows per KV head): inside the streaming launch unless the system step's
+    matrix-core time (at 0.9 PFLOP/s) exceeds twice the context step's memory time (at
+    4.5 TB/s, half of max_ctx_len per request)."""
+    t_sys = 4.0 * d.num_q_heads * d.head_dim * d.total_q * sys_len / 0.9e15
+    t_ctx = 4.0 * d.num_kv_heads * d.head_dim * d.batch * (d.max_ctx_len / 2.0 + 16.0) / 4.5e12
+    return t_ctx > 0.5 * t_sys
+
+
 def stream_grid(bf16, D, rts, rtc):
     """Workgroups of a streaming launch: two per CU where the instantiation's registers
     fit two waves per SIMD (the header's plan contract), else one."""
@@ -166,11 +176,15 @@ def test_plan_for_each_config(lib, cfg, sweep):
         tiles = -(-M // 16)
         assert plan["sys_row_tiles"] == (tiles if tiles <= 2 else 4)
         assert plan["sys_runs"] == 0 and plan["sys_wgs"] == 0
-    else:         # matrix-core system kernel: (row block, run of 64-key steps) workgroups
-        assert plan["sys_mode"] == 2 and plan["launches"] == 3
+    else:         # matrix-core system workgroups, (row block, run of 64-key steps)
+        co = corun(d, spec.sys_len)
+        if co:    # inside the streaming launch, one per CU
+            assert plan["sys_mode"] == 4 and plan["launches"] == 2
+        else:     # a launch of their own first, two per CU
+            assert plan["sys_mode"] == 2 and plan["launches"] == 3
         row_blocks = -(-M // 128)
         steps = spec.num_kv_heads * -(-spec.sys_len // 64)
-        parts = min(max(512 // row_blocks, 1), steps)
+        parts = min(max((CUS if co else 2 * CUS) // row_blocks, 1), steps)
         assert plan["sys_wgs"] == -(-row_blocks * parts // 8) * 8
         # slots: the most runs one head's steps fall into
         part_of = lambda x: ((x + 1) * parts + steps - 1) // steps - 1
@@ -181,7 +195,9 @@ def test_plan_for_each_config(lib, cfg, sweep):
     assert plan["ctx_row_tiles"] == (1 if R_ <= 16 else 2)
     assert plan["ctx_row_blocks"] == -(-R_ // (16 * plan["ctx_row_tiles"]))
     rts = plan["sys_row_tiles"] if plan["sys_mode"] == 1 else 0
-    grid = stream_grid(spec.dtype == "bf16", spec.head_dim, rts, plan["ctx_row_tiles"])
+    # beside the system workgroups: one context workgroup per CU
+    grid = CUS if plan["sys_mode"] == 4 else stream_grid(spec.dtype == "bf16", spec.head_dim, rts,
+                                                         plan["ctx_row_tiles"])
     assert plan["stream_waves"] == 4 * grid and plan["stream_launches"] == 1
     assert plan["stream_max_requests"] == spec.batch
 
@@ -191,8 +207,8 @@ def test_requests_in_groups_of_one_streaming_launch(lib):
     launches over request groups (2880 requests each)."""
     d = base_dims(batch=9000, total_q=9000, num_blocks=90000, max_ctx_len=100, max_blocks_per_seq=7)
     plan = R.relay_get_plan(d, 500)
-    assert plan["sys_mode"] == 2 and plan["stream_max_requests"] == 2880
-    assert plan["stream_launches"] == 4 and plan["launches"] == 6
+    assert corun(d, 500) and plan["sys_mode"] == 4 and plan["stream_max_requests"] == 2880
+    assert plan["stream_launches"] == 4 and plan["launches"] == 5   # system workgroups in the first
     ws = R.relay_workspace_size(d, 500)
     assert ws >= 4 * (2880 * 2 + 4 * stream_grid(True, 128, 0, 1)) * 16 * 129 * 4
 

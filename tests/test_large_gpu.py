@@ -42,7 +42,7 @@ def test_system_cache_past_4_gib(batch):
     assert sys_k.numel() * 2 > 2**32 and sys_v.numel() * 2 > 2**32
     t.update(sys_k=sys_k, sys_v=sys_v, sys_len=L_SYS)
     plan = R.relay_get_plan(R.dims_of(t), L_SYS)
-    assert plan["sys_mode"] == (1 if batch * H_Q // H_KV <= 64 else 2)
+    assert plan["sys_mode"] in ((1,) if batch * H_Q // H_KV <= 64 else (2, 4))
     out = R.decode_workload(t).cpu().numpy()
     torch.cuda.synchronize()
 

@@ -335,15 +335,18 @@ def test_multi_split_shapes(spec):
 
 # shapes whose matrix-core system runs cross KV-head boundaries: (batch, sys_len); 1 query
 # token per request, 32 / 8 heads, so M = 4 B stacked rows per KV head in ceil(M / 128) row
-# blocks and 512 // row_blocks runs over the 8 heads' 64-key steps
+# blocks and slots // row_blocks runs over the 8 heads' 64-key steps (slots: one system
+# workgroup per CU inside the streaming launch, two in a launch of their own)
 CROSSING = [(75, 1920), (150, 2560), (200, 1000)]
 
 
-def _runs_cross_heads(batch, sys_len, hkv=8, g=4):
+def _runs_cross_heads(batch, sys_len, sys_mode, hkv=8, g=4):
+    # one system workgroup per CU inside the streaming launch (sys_mode 4), else two
+    cus = torch.cuda.get_device_properties(0).multi_processor_count * (1 if sys_mode == 4 else 2)
     rb = -(-batch * g // 128)
     sph = -(-sys_len // 64)
     S = hkv * sph
-    parts = min(max(512 // rb, 1), S)
+    parts = min(max(cus // rb, 1), S)
     return any((p * S // parts) % sph for p in range(1, parts))
 
 
@@ -351,13 +354,13 @@ def _runs_cross_heads(batch, sys_len, hkv=8, g=4):
 def test_system_runs_across_heads(batch, sys_len):
     """Matrix-core system step whose key runs cross KV-head boundaries (each run one
     partial per head it touches, unused slots empty), step alone and whole decode."""
-    assert _runs_cross_heads(batch, sys_len)
     spec = W.config_spec(4).replace(batch=batch, sys_len=sys_len, ctx_median=60, ctx_cap=300)
     say(f"[parity] system runs across heads {spec}")
     w = workload(spec)
     t = upload(w)
     plan = R.relay_get_plan(R.dims_of(t), t["sys_len"])
-    assert plan["sys_mode"] == 2 and plan["sys_runs"] >= 2
+    assert plan["sys_mode"] in (2, 4) and plan["sys_runs"] >= 2
+    assert _runs_cross_heads(batch, sys_len, plan["sys_mode"])
     o, lse = R.relay_sys_attn(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], R.dims_of(t))
     out = R.decode_workload(t)
     torch.cuda.synchronize()
