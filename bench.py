@@ -82,13 +82,18 @@ def parse():
                          "fetch, copy write; mfma: one per workload, --workload lists them comma-separated; "
                          "sysbytes: the --sys-scaling FETCH_SIZE run, its stdout, the copy-calibration fetch run)")
     ap.add_argument("--commands", nargs="*", default=[], help="--summarize: the commands that made --dirs")
+    ap.add_argument("--timed-steps", type=int, default=0,
+                    help="--summarize stats: also report the mean of each kernel's last N dispatches")
     return ap.parse_args()
 
 
 # ---------------------------------------------------------------------------------------
 # kernels by short name, and the rocprofv3 summaries under profiles/
 
-KERNELS = (("stream_attn_kernel", "stream_attn"), ("sys_attn_mfma_kernel", "sys_attn_mfma"),
+# stream_sys_kernel is the streaming launch that also holds the matrix-core system
+# workgroups (sys_mode 4): it is the step's streaming launch, named like the other one
+KERNELS = (("stream_attn_kernel", "stream_attn"), ("stream_sys_kernel", "stream_attn"),
+           ("sys_attn_mfma_kernel", "sys_attn_mfma"),
            ("sys_attn_tiled_kernel", "sys_attn_tiled"), ("relay_merge_kernel", "relay_merge"),
            ("relay_fuse_kernel", "relay_fuse"), ("rope_append_kernel", "rope_append"),
            ("read_probe_kernel", "read_probe"), ("mfma_probe_kernel", "mfma_probe"))
@@ -143,12 +148,28 @@ def summarize(args):
                          float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"]), r["Name"]))
         named = [r for r in rows if r[0] != "-"]
         dom = max(named, key=lambda r: r[1] * r[2])[0]
+        # the mean over each kernel's last --timed-steps dispatches: the eager pass whose
+        # kernels bench.py times with start/end events (the graph replays before it can
+        # run at another clock)
+        last = {}
+        if args.timed_steps > 0:
+            per = {}
+            for r in _csv(args.dirs[0], "kernel_trace.csv"):
+                per.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+            for k, v in per.items():
+                v = [d for _, d in sorted(v)][-args.timed_steps:]
+                last[k] = sum(v) / len(v) / 1e3
         path = os.path.join(ROOT, "profiles", f"{dom}_{args.workload}_kernel_stats.txt")
-        lines = [f"# rocprofv3 kernel-trace statistics: {args.workload} (kernels timed by dispatch start/end)"]
+        lines = [f"# rocprofv3 kernel-trace statistics: {args.workload} (kernels timed by dispatch start/end);",
+                 f"# timed_avg_us: mean of each kernel's last {args.timed_steps} dispatches (the eager pass "
+                 "that bench.py times with kernel start/end events)"]
         lines += cmds + head
-        lines.append(f"{'kernel':16s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}  full name")
+        lines.append(f"{'kernel':16s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} "
+                     f"{'timed_avg_us':>12s} {'pct':>6s}  full name")
         for s, c, a, mn, mx, pct, full in sorted(rows, key=lambda r: -r[5]):
-            lines.append(f"{s:16s} {c:6d} {a:9.3f} {mn:9.3f} {mx:9.3f} {pct:6.2f}  {full[:90]}")
+            ta = f"{last[full]:12.3f}" if full in last else f"{'-':>12s}"
+            lines.append(f"{s:16s} {c:6d} {a:9.3f} {mn:9.3f} {mx:9.3f} {ta} {pct:6.2f}  {full[:90]}")
     elif args.summarize == "traffic":
         fetch, write, cfetch, cwrite = (_counters(d) for d in args.dirs[:4])
         cf = sum(cfetch[("copy", "FETCH_SIZE")]) / len(cfetch[("copy", "FETCH_SIZE")])
@@ -230,7 +251,8 @@ def summarize(args):
 
 def read_profile(kind, workload):
     """A committed summary of this workload taken from the current library sources:
-    {kernel: avg_us} (kind "stats") or {kernel: traffic bytes per launch} ("traffic"),
+    {kernel: (avg_us, timed_avg_us or None)} (kind "stats") or {kernel: traffic bytes per
+    launch} ("traffic"),
     with the file it came from; None when there is none or it is stale."""
     pat = os.path.join(ROOT, "profiles", f"*_{workload}_{'kernel_stats' if kind == 'stats' else 'traffic'}.txt")
     dig = source_digest()
@@ -245,8 +267,8 @@ def read_profile(kind, workload):
                 continue
             if kind == "stats":
                 parts = line.split()
-                if len(parts) >= 6 and parts[0] in dict((s, 1) for _, s in KERNELS):
-                    out[parts[0]] = float(parts[2])
+                if len(parts) >= 7 and parts[0] in dict((s, 1) for _, s in KERNELS):
+                    out[parts[0]] = (float(parts[2]), None if parts[5] == "-" else float(parts[5]))
             elif ".traffic_bytes_per_launch:" in line:
                 k, v = line.split(":", 1)
                 out[k.split(".")[0]] = int(v)
@@ -869,8 +891,10 @@ def roofline(r, spec, ceilings):
         out["traffic_source"] = tr[1]
     st = read_profile("stats", spec.name)
     if st and dom in st[0]:
-        ru = st[0][dom]
-        out["rocprof"] = {"avg_us": ru, "frac": round(alg / (ru * 1e-6) / (1e12 if mfma else 1e9) / peak, 4),
+        avg, timed = st[0][dom]
+        ru = timed if timed is not None else avg
+        out["rocprof"] = {"avg_us": avg, "timed_avg_us": timed,
+                          "frac": round(alg / (ru * 1e-6) / (1e12 if mfma else 1e9) / peak, 4),
                           "source": st[1]}
     return out
 
