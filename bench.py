@@ -91,9 +91,10 @@ def parse():
 # kernels by short name, and the rocprofv3 summaries under profiles/
 
 # stream_sys_kernel is the streaming launch that also holds the matrix-core system
-# workgroups (sys_mode 4): it is the step's streaming launch, named like the other one
+# workgroups (sys_mode 4): it is the step's streaming launch, named like the other one;
+# sys_attn_mfma_pp_kernel is the eight-wave form of the matrix-core system kernel
 KERNELS = (("stream_attn_kernel", "stream_attn"), ("stream_sys_kernel", "stream_attn"),
-           ("sys_attn_mfma_kernel", "sys_attn_mfma"),
+           ("sys_attn_mfma_kernel", "sys_attn_mfma"), ("sys_attn_mfma_pp_kernel", "sys_attn_mfma"),
            ("sys_attn_tiled_kernel", "sys_attn_tiled"), ("relay_merge_kernel", "relay_merge"),
            ("relay_fuse_kernel", "relay_fuse"), ("rope_append_kernel", "rope_append"),
            ("read_probe_kernel", "read_probe"), ("mfma_probe_kernel", "mfma_probe"))

@@ -100,9 +100,9 @@
 extern "C" {
 #endif
 
-#define RELAY_ATTN_ABI_VERSION 4  /* 3: keys in slot order inside each 16-byte chunk of a tile; plan
+#define RELAY_ATTN_ABI_VERSION 5  /* 3: keys in slot order inside each 16-byte chunk of a tile; plan
                                      fields of the streaming launch.  4: relay_attn_decode_timed
-                                     takes kernel start/end event pairs */
+                                     takes kernel start/end event pairs.  5: relay_plan.sys_rows_per_wg */
 
 /* element types */
 #define RELAY_F32 0  /* IEEE float32 */
@@ -152,6 +152,9 @@ typedef struct {
   int32_t stream_max_requests; /* requests per streaming launch */
   int32_t merge_wgs;           /* workgroups of the merge launch */
   int32_t launches;            /* kernel launches of one relay_attn_decode call */
+  int32_t sys_rows_per_wg;     /* sys_mode 2, 4: stacked query rows per matrix-core system workgroup
+                                  (128; 256 for the eight-wave kernel that sys_mode 2 uses when its
+                                  row blocks fill) */
 } relay_plan;
 
 /* ABI version compiled into the library (RELAY_ATTN_ABI_VERSION). */

@@ -72,6 +72,7 @@ struct Plan {
   SysConfig sc{};
   int sys_chunks = 0, sys_chunk_len = 0, sys_row_blocks = 0, sys_wgs = 0, xcd_remap = 0;
   int sys_steps_per_head = 0, sys_total_steps = 0, sys_parts = 0;
+  int sys_pp = 0;  // sys_mode 2: the two-group kernel (kSysPPRows rows, one workgroup per CU)
   // streaming launches
   int rtc = 1, ctx_rb = 1, grid = 0, workers = 0, chunk_req = 0, n_chunks = 0;
   long long sys_slots = 0, ctx_slots_per_chunk = 0, ctx_slots = 0;
@@ -116,10 +117,12 @@ int clamp_int(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // The system kernel's plan (M > 64 stacked rows per KV head).
 // slots: workgroups of the system kernel resident at once (the launch is cut to fill them).
-void plan_system_kernel(const relay_dims* d, int32_t sys_len, int M, Plan* p, long long slots = relay::kSysMfmaSlots) {
+void plan_system_kernel(const relay_dims* d, int32_t sys_len, int M, Plan* p, long long slots = relay::kSysMfmaSlots,
+                        bool pp = false) {
   if (d->in_dtype == RELAY_BF16 && d->head_dim == 128) {
     p->sys_mode = 2;
-    p->sys_row_blocks = ceil_div(M, relay::kSysMfmaRows);
+    p->sys_pp = pp && !p->causal ? 1 : 0;
+    p->sys_row_blocks = ceil_div(M, p->sys_pp ? relay::kSysPPRows : relay::kSysMfmaRows);
     // the 64-key steps of all heads, cut into `parts` equal runs so the row blocks
     // times the parts fill the resident workgroup slots once
     p->sys_steps_per_head = ceil_div(sys_len, relay::kSysMfmaStep);
@@ -158,6 +161,16 @@ void plan_system_kernel(const relay_dims* d, int32_t sys_len, int M, Plan* p, lo
     p->sys_wgs = p->sys_row_blocks * p->sys_chunks * d->num_kv_heads;
     p->xcd_remap = (p->sys_row_blocks > 1 && p->sys_wgs % 8 == 0) ? 1 : 0;
   }
+}
+
+// Whether the system step as a launch of its own takes the two-group kernel (256 rows
+// per workgroup, one per CU, about 10 % faster per row at config-5 sizes) rather than
+// the four-wave one (128 rows, two per CU): yes unless the 256-row blocks would hold more
+// than 10 % more padding rows than the 128-row ones.
+bool pp_fills(int M) {
+  const long long pp = (long long)relay::kSysPPRows * ceil_div(M, relay::kSysPPRows);
+  const long long mf = (long long)relay::kSysMfmaRows * ceil_div(M, relay::kSysMfmaRows);
+  return 10 * pp <= 11 * mf;
 }
 
 // Whether the decode step's matrix-core system workgroups should share the CUs with the
@@ -204,6 +217,9 @@ int make_plan(const relay_dims* d, int32_t sys_len, Plan* p, Need need = kDecode
       // one context workgroup per CU
       plan_system_kernel(d, sys_len, M, p, device_cus());
       p->sys_mode = 4;
+    } else if (need != kPrefill && d->in_dtype == RELAY_BF16 && D == 128 && pp_fills(M)) {
+      // a launch of its own: the two-group kernel, one workgroup per CU
+      plan_system_kernel(d, sys_len, M, p, device_cus(), true);
     } else {
       plan_system_kernel(d, sys_len, M, p);
     }
@@ -296,6 +312,7 @@ int launch_sys_kernel(const relay_dims* d, const Plan& p, const void* q, const v
   if (!grid_ok(p.sys_wgs)) return fail(RELAY_ERR_INVALID, "system grid too large");
   const SysArgs a = system_args(d, p, q, sys_k, sys_v, sys_len, ws);
   hipError_t e = p.sys_mode == 3 ? relay::launch_sys_attn_tiled(a, p.sc, d->in_dtype, d->head_dim, p.sys_wgs, s, tm)
+                 : p.sys_pp      ? relay::launch_sys_attn_pp(a, p.sys_wgs, s, tm)
                                  : relay::launch_sys_attn_mfma(a, p.sys_wgs, s, tm);
   return e == hipSuccess ? RELAY_OK : hip_fail(e, "system attention launch");
 }
@@ -489,11 +506,14 @@ const char* relay_last_error(void) { return g_err; }
 
 size_t relay_workspace_size(const relay_dims* dims, int32_t sys_len) {
   if (check_dims(dims, sys_len) != RELAY_OK) return 0;
-  Plan p, pc;
+  Plan p, pc, ps;
   if (make_plan(dims, sys_len, &p) != RELAY_OK) return 0;
-  // relay_ctx_attn plans the context streams alone (two workgroups per CU)
+  // relay_ctx_attn plans the context streams alone (two workgroups per CU), and
+  // relay_sys_attn the system step alone
   if (make_plan(dims, 0, &pc) != RELAY_OK) return 0;
-  return p.ws_bytes > pc.ws_bytes ? p.ws_bytes : pc.ws_bytes;
+  if (make_plan(dims, sys_len, &ps, kSysOnly) != RELAY_OK) return 0;
+  size_t b = p.ws_bytes > pc.ws_bytes ? p.ws_bytes : pc.ws_bytes;
+  return b > ps.ws_bytes ? b : ps.ws_bytes;
 }
 
 int relay_get_plan(const relay_dims* dims, int32_t sys_len, relay_plan* out) {
@@ -513,6 +533,7 @@ int relay_get_plan(const relay_dims* dims, int32_t sys_len, relay_plan* out) {
   out->stream_max_requests = p.chunk_req;
   out->merge_wgs = p.merge_wgs;
   out->launches = p.launches;
+  out->sys_rows_per_wg = p.sys_mode == 2 || p.sys_mode == 4 ? (p.sys_pp ? relay::kSysPPRows : relay::kSysMfmaRows) : 0;
   return RELAY_OK;
 }
 
@@ -594,7 +615,7 @@ int relay_sys_attn(const relay_dims* dims, const void* q, const void* sys_k, con
   if (!aligned16(q) || !aligned16(sys_k) || !aligned16(sys_v) || !aligned16(o_sys))
     return fail(RELAY_ERR_INVALID, "arrays must be 16-byte aligned");
   Plan p;
-  if ((rc = make_plan(dims, sys_len, &p)) != RELAY_OK) return rc;
+  if ((rc = make_plan(dims, sys_len, &p, kSysOnly)) != RELAY_OK) return rc;
   if ((rc = check_ws(p, workspace, workspace_bytes)) != RELAY_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);

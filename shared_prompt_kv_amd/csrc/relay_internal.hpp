@@ -223,6 +223,9 @@ hipError_t launch_sys_attn_tiled(const SysArgs& a, const SysConfig& c, int in_dt
 // sys_attn_mfma (bf16, head_dim 128): workgroups of kSysMfmaRows query rows; designed
 // for two workgroups per CU (kSysMfmaSlots resident at once).
 constexpr int kSysMfmaRows = 128;
+// The decode system step as a launch of its own: one workgroup of kSysPPRows rows (eight
+// waves in two groups half a step apart) per CU.
+constexpr int kSysPPRows = 256;
 constexpr int kSysMfmaSlots = 512;
 constexpr int kSysMfmaStep = 64;
 // Rates the decode plan weighs the system step's matrix-core time against the context
@@ -242,6 +245,7 @@ inline __host__ __device__ int lean_part_of(long long x, int total, int parts) {
   return (int)(((x + 1) * parts + total - 1) / total) - 1;
 }
 hipError_t launch_sys_attn_mfma(const SysArgs& a, int nwg, hipStream_t stream, const LaunchTiming* tm = nullptr);
+hipError_t launch_sys_attn_pp(const SysArgs& a, int nwg, hipStream_t stream, const LaunchTiming* tm = nullptr);
 // relay_fuse workgroup size: one wave, or four once there are enough rows for two
 // four-wave workgroups per CU (D/4 lanes per row).
 inline int fuse_threads(int head_dim, long long n_rows) {

@@ -56,7 +56,7 @@ def test_library_is_gfx950_only(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert R.relay_abi_version() == 4
+    assert R.relay_abi_version() == 5
     assert lib.relay_strerror(0) == b"ok"
     assert lib.relay_strerror(-3) == b"workspace too small"
 
@@ -180,11 +180,14 @@ def test_plan_for_each_config(lib, cfg, sweep):
         co = corun(d, spec.sys_len)
         if co:    # inside the streaming launch, one per CU
             assert plan["sys_mode"] == 4 and plan["launches"] == 2
-        else:     # a launch of their own first, two per CU
+        else:     # a launch of their own first, one workgroup per CU: 256 rows where the
+            # 256-row blocks pad at most 10 % more rows than 128-row ones, else 128
             assert plan["sys_mode"] == 2 and plan["launches"] == 3
-        row_blocks = -(-M // 128)
+        pp = not co and 10 * 256 * -(-M // 256) <= 11 * 128 * -(-M // 128)
+        assert plan["sys_rows_per_wg"] == (256 if pp else 128)
+        row_blocks = -(-M // plan["sys_rows_per_wg"])
         steps = spec.num_kv_heads * -(-spec.sys_len // 64)
-        parts = min(max((CUS if co else 2 * CUS) // row_blocks, 1), steps)
+        parts = min(max((CUS if co or pp else 2 * CUS) // row_blocks, 1), steps)
         assert plan["sys_wgs"] == -(-row_blocks * parts // 8) * 8
         # slots: the most runs one head's steps fall into
         part_of = lambda x: ((x + 1) * parts + steps - 1) // steps - 1

@@ -334,16 +334,18 @@ def test_multi_split_shapes(spec):
 
 
 # shapes whose matrix-core system runs cross KV-head boundaries: (batch, sys_len); 1 query
-# token per request, 32 / 8 heads, so M = 4 B stacked rows per KV head in ceil(M / 128) row
-# blocks and slots // row_blocks runs over the 8 heads' 64-key steps (slots: one system
-# workgroup per CU inside the streaming launch, two in a launch of their own)
+# token per request, 32 / 8 heads, so M = 4 B stacked rows per KV head in row blocks of
+# the plan's rows per workgroup and slots // row_blocks runs over the 8 heads' 64-key
+# steps (slots: one workgroup per CU, or two for 128-row blocks in a launch of their own)
 CROSSING = [(75, 1920), (150, 2560), (200, 1000)]
 
 
-def _runs_cross_heads(batch, sys_len, sys_mode, hkv=8, g=4):
-    # one system workgroup per CU inside the streaming launch (sys_mode 4), else two
-    cus = torch.cuda.get_device_properties(0).multi_processor_count * (1 if sys_mode == 4 else 2)
-    rb = -(-batch * g // 128)
+def _runs_cross_heads(batch, sys_len, plan, hkv=8, g=4):
+    rows = plan["sys_rows_per_wg"]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if plan["sys_mode"] == 2 and rows == 128:
+        cus *= 2
+    rb = -(-batch * g // rows)
     sph = -(-sys_len // 64)
     S = hkv * sph
     parts = min(max(cus // rb, 1), S)
@@ -360,7 +362,7 @@ def test_system_runs_across_heads(batch, sys_len):
     t = upload(w)
     plan = R.relay_get_plan(R.dims_of(t), t["sys_len"])
     assert plan["sys_mode"] in (2, 4) and plan["sys_runs"] >= 2
-    assert _runs_cross_heads(batch, sys_len, plan["sys_mode"])
+    assert _runs_cross_heads(batch, sys_len, plan)
     o, lse = R.relay_sys_attn(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], R.dims_of(t))
     out = R.decode_workload(t)
     torch.cuda.synchronize()
@@ -370,6 +372,34 @@ def test_system_runs_across_heads(batch, sys_len):
     check(lse.cpu().numpy(), rl, spec.dtype, "lse_sys")
     ref, _ = P.attention()
     check(out.cpu().numpy(), ref, spec.dtype, "out")
+
+
+# the system step alone on the eight-wave two-group kernel (256 rows per workgroup, one
+# workgroup per CU): (batch, sys_len, sign of the scale).  M = 4 B stacked rows per KV
+# head; B = 120 leaves the last row block partly padded; sys_len 3000 and 1000 end inside
+# a 64-key step and inside a 16-key tile; the runs of 64-key steps cross KV heads
+TWO_GROUP = [(64, 3000, 1), (120, 1000, 1), (64, 1000, -1)]
+
+
+@pytest.mark.parametrize("batch,sys_len,sign", TWO_GROUP,
+                         ids=[f"B{b}-L{l}-{'neg' if g < 0 else 'pos'}" for b, l, g in TWO_GROUP])
+def test_system_two_group_kernel(batch, sys_len, sign):
+    """relay_sys_attn on the two-group matrix-core kernel: every row's system-part output
+    and log-sum-exp against the oracle (a negative scale included: its sign is folded
+    into the query)."""
+    spec = W.config_spec(4).replace(batch=batch, sys_len=sys_len, ctx_median=60, ctx_cap=300)
+    say(f"[parity] two-group system kernel {spec} sign {sign}")
+    w = workload(spec)
+    t = upload(w)
+    t["scale"] = sign * spec.scale
+    d = R.dims_of(t)
+    M = batch * spec.group
+    assert 10 * 256 * -(-M // 256) <= 11 * 128 * -(-M // 128)  # the plan's rule for 256 rows
+    o, lse = R.relay_sys_attn(t["q"], t["sys_k"], t["sys_v"], t["sys_len"], d)
+    torch.cuda.synchronize()
+    ro, rl = oracle.Problem(w, scale=sign * spec.scale).system_part()
+    check(o.cpu().numpy(), ro, spec.dtype, "o_sys")
+    check(lse.cpu().numpy(), rl, spec.dtype, "lse_sys")
 
 
 def test_steps_full_size_gqa():
