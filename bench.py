@@ -838,7 +838,10 @@ def sys_scaling(torch, relay, steps):
             E = 2 if spec.dtype == "bf16" else 4
             print(json.dumps({"shape": name, "batch": B, "sys_len": spec.sys_len,
                               "rows_per_kv_head": w.total_q * spec.group,
-                              "kernel": sys_kernel_name(plan) or "stream_attn",
+                              # relay_sys_attn: the system streams at <= 64 rows per KV
+                              # head, else the system kernel as a launch of its own
+                              "kernel": {1: "stream_attn", 3: "sys_attn_tiled"}.get(plan["sys_mode"],
+                                                                                    "sys_attn_mfma"),
                               "dispatches": 3 + steps,
                               "sys_kv_bytes": 2 * spec.num_kv_heads * spec.head_dim * E * spec.sys_len,
                               "us_per_call": round(1000 * e0.elapsed_time(e1) / steps, 2)}), flush=True)
