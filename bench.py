@@ -321,8 +321,10 @@ def work_of(w, plan=None):
 def partial_overhead(w, plan):
     """Bytes of partial results beyond the method's two per row: what the kernels write
     (each piece of a stream writes its rows' O and LSE) and what the merge reads back
-    beyond two partials per row.  Follows the streaming launch's static partition
-    (single request group); the system kernel writes every run slot of every row."""
+    beyond two partials per row (every place fixed in advance, sys_row_slots per KV head
+    and ctx_row_slots per row, whether a piece went there or not, and the pieces past
+    them).  Follows the streaming launch's static partition (single request group); the
+    system kernel writes every run slot of every row."""
     import numpy as np
     s = w.spec
     d, g, Hkv = s.head_dim, s.group, s.num_kv_heads
@@ -350,18 +352,22 @@ def partial_overhead(w, plan):
     p0 = Ts + np.concatenate([[0], np.cumsum(st)[:-1]]) if len(st) else np.zeros(0, np.int64)
     ctx_pieces = part_of(p0 + st - 1) - part_of(p0) + 1
     written = int((ctx_pieces * rows_in).sum()) * row_b
+    ks, kc = plan.get("sys_row_slots", 0), plan.get("ctx_row_slots", 0)
+    read = int((np.maximum(ctx_pieces, kc) * rows_in).sum()) * row_b
     if sys_mode == 1 and S > 0:
         h = np.arange(Hkv)
         sys_pieces = part_of(h * S + S - 1) // 4 - part_of(h * S) // 4 + 1
         written_sys = int(sys_pieces.sum()) * M * row_b
+        read += int(np.maximum(sys_pieces, ks).sum()) * M * row_b
     elif sys_mode >= 2:
         written_sys = plan["sys_runs"] * rows * row_b
+        read += written_sys
     else:
         written_sys = 0
     in_stream = sys_mode in (1, 4)
     return {"stream_attn_partials_written": written + (written_sys if in_stream else 0),
             "sys_kernel_partials_written": 0 if in_stream else written_sys,
-            "merge_extra_partial_reads": max(0, written + written_sys - 2 * rows * row_b)}
+            "merge_extra_partial_reads": max(0, read - 2 * rows * row_b)}
 
 
 # ---------------------------------------------------------------------------------------

@@ -100,9 +100,10 @@
 extern "C" {
 #endif
 
-#define RELAY_ATTN_ABI_VERSION 5  /* 3: keys in slot order inside each 16-byte chunk of a tile; plan
+#define RELAY_ATTN_ABI_VERSION 6  /* 3: keys in slot order inside each 16-byte chunk of a tile; plan
                                      fields of the streaming launch.  4: relay_attn_decode_timed
-                                     takes kernel start/end event pairs.  5: relay_plan.sys_rows_per_wg */
+                                     takes kernel start/end event pairs.  5: relay_plan.sys_rows_per_wg.
+                                     6: relay_plan.sys_row_slots, ctx_row_slots */
 
 /* element types */
 #define RELAY_F32 0  /* IEEE float32 */
@@ -155,6 +156,12 @@ typedef struct {
   int32_t sys_rows_per_wg;     /* sys_mode 2, 4: stacked query rows per matrix-core system workgroup
                                   (128; 256 for the eight-wave kernel that sys_mode 2 uses when its
                                   row blocks fill) */
+  int32_t sys_row_slots;       /* sys_mode 1: pieces of a KV head's system stream written to workspace
+                                  slots fixed in advance (the merge reads those with the
+                                  descriptors, in one memory round trip; later pieces cost it a
+                                  second); from an estimate of the launch's steps (the context
+                                  lengths are device data); 0 above 4096 output rows */
+  int32_t ctx_row_slots;       /* the same for the pieces of a context stream (each row's own slots) */
 } relay_plan;
 
 /* ABI version compiled into the library (RELAY_ATTN_ABI_VERSION). */
@@ -169,9 +176,10 @@ const char* relay_last_error(void);
 /*
  * Bytes of device workspace that relay_attn_decode, relay_sys_attn and
  * relay_ctx_attn need for these dimensions and system length: the partial outputs
- * and log-sum-exps of the streaming launch's pieces and of the system kernel's
- * runs, and descriptors of where each row's pieces are.  Returns 0 on invalid dims
- * (see relay_last_error()).
+ * and log-sum-exps of the streaming launch's pieces (the first relay_plan.sys_row_slots
+ * of each system stream and ctx_row_slots of each context stream at places fixed in
+ * advance) and of the system kernel's runs, and descriptors of where each row's other
+ * pieces are.  Returns 0 on invalid dims (see relay_last_error()).
  */
 size_t relay_workspace_size(const relay_dims* dims, int32_t sys_len);
 

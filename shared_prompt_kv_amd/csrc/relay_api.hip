@@ -77,7 +77,9 @@ struct Plan {
   int rtc = 1, ctx_rb = 1, grid = 0, workers = 0, chunk_req = 0, n_chunks = 0;
   long long sys_slots = 0, ctx_slots_per_chunk = 0, ctx_slots = 0;
   int merge_wgs = 0, launches = 0;
+  int ks = 0, kc = 0;  // the rows' own slots for system and context pieces
   size_t off_sys_o = 0, off_sys_lse = 0, off_sys_desc = 0, off_ctx_o = 0, off_ctx_lse = 0, off_rowdesc = 0;
+  size_t off_row_o = 0, off_row_lse = 0;
   size_t ws_bytes = 0;
 };
 
@@ -234,7 +236,7 @@ int make_plan(const relay_dims* d, int32_t sys_len, Plan* p, Need need = kDecode
   p->grid = p->sys_mode == 4 ? device_cus()
                              : relay::stream_grid(device_cus(), d->in_dtype == RELAY_BF16 ? 2 : 4, D, p->rts, p->rtc);
   p->workers = p->grid * relay::kStreamWaves;
-  if (p->sys_mode == 1) p->sys_slots = (long long)d->num_kv_heads + p->grid;
+
   const int cap = d->max_ctx_len < d->max_blocks_per_seq * 16 ? d->max_ctx_len : d->max_blocks_per_seq * 16;
   const long long per_req = (long long)ceil_div(cap, 32) * d->num_kv_heads * p->ctx_rb;
   long long chunk = relay::kStreamMaxRequests;
@@ -247,6 +249,42 @@ int make_plan(const relay_dims* d, int32_t sys_len, Plan* p, Need need = kDecode
   p->n_chunks = ceil_div(d->batch, chunk);
   p->ctx_slots_per_chunk = chunk * d->num_kv_heads * p->ctx_rb + p->workers;
   p->ctx_slots = p->ctx_slots_per_chunk * p->n_chunks;
+  // ---- the rows' own piece slots, which the merge reads without looking up where they
+  // are: for up to kRowSlotRows rows (the system streams' shapes), where the merge waits
+  // on memory latency, not bandwidth (with more rows, slots read in vain cost more than
+  // the round trip they save).  Context: the most waves the longest stream can fall
+  // into, with at least (system steps + one step per stream) / waves steps per wave, at
+  // most four.  System streams: the most workgroups one KV head's steps fall into, for a
+  // step count estimated from half the longest context per stream (the lengths are
+  // device data), plus one; exact when the launch holds no context streams.  Pieces past
+  // a row's own slots take the stream slots, and the merge a second round trip for them.
+  const long long max_steps = ceil_div(cap, 32) > 1 ? ceil_div(cap, 32) : 1;
+  const long long Ts = p->sys_mode == 1 ? (long long)d->num_kv_heads * p->sys_steps : 0;
+  const bool row_slots = p->sys_mode <= 1 && rows <= relay::kRowSlotRows;
+  if (row_slots && need != kSysOnly) {
+    long long per_wave = (Ts + chunk * d->num_kv_heads) / p->workers;
+    if (per_wave < 1) per_wave = 1;
+    long long kc = (max_steps - 1 + per_wave - 1) / per_wave + 1;
+    if (kc > max_steps) kc = max_steps;
+    p->kc = (int)(kc < 4 ? kc : 4);
+  }
+  if (row_slots && p->sys_mode == 1) {
+    const long long ss = p->sys_steps;
+    long long T = Ts;
+    if (need != kSysOnly) T += chunk * d->num_kv_heads * p->ctx_rb * ((max_steps + 1) / 2);
+    const long long W = T < p->workers ? T : p->workers;
+    auto part = [&](long long x) { return ((x + 1) * W + T - 1) / T - 1; };
+    long long most = 1;
+    for (int h = 0; h < d->num_kv_heads; ++h) {
+      const long long n = part(h * ss + ss - 1) / relay::kStreamWaves - part(h * ss) / relay::kStreamWaves + 1;
+      if (n > most) most = n;
+    }
+    if (need != kSysOnly) ++most;
+    p->ks = (int)(most < relay::kMaxRowSlots - p->kc ? most : relay::kMaxRowSlots - p->kc);
+  }
+  // system stream slots: the fixed ones (KV head h's piece k < ks at h ks + k), then one
+  // per (KV head, workgroup) pair a later piece can fall on (h + w)
+  if (p->sys_mode == 1) p->sys_slots = (long long)d->num_kv_heads * (p->ks + 1) + p->grid;
   // ---- merge
   p->merge_wgs = ceil_div(rows, relay::merge_threads(D, rows) / (D / 4));
   p->launches = (p->sys_mode == 2 || p->sys_mode == 3 ? 1 : 0) + p->n_chunks + 1;
@@ -270,6 +308,10 @@ int make_plan(const relay_dims* d, int32_t sys_len, Plan* p, Need need = kDecode
   off += align256((size_t)p->ctx_slots * 16 * p->rtc * sizeof(float));
   p->off_rowdesc = off;
   off += align256((size_t)rows * 4 * sizeof(int));
+  p->off_row_o = off;
+  off += align256((size_t)rows * p->kc * D * sizeof(float));
+  p->off_row_lse = off;
+  off += align256((size_t)rows * p->kc * sizeof(float));
   p->ws_bytes = off;
   return RELAY_OK;
 }
@@ -358,6 +400,10 @@ int launch_streams(const relay_dims* d, const Plan& p, bool with_sys, bool with_
   a.ctx_o = reinterpret_cast<float*>(ws + p.off_ctx_o);
   a.ctx_lse = reinterpret_cast<float*>(ws + p.off_ctx_lse);
   a.ctx_rowdesc = reinterpret_cast<int*>(ws + p.off_rowdesc);
+  a.row_o = reinterpret_cast<float*>(ws + p.off_row_o);
+  a.row_lse = reinterpret_cast<float*>(ws + p.off_row_lse);
+  a.ks = p.ks;
+  a.kc = p.kc;
   const int launches = with_ctx ? p.n_chunks : 1;
   for (int c = 0; c < launches; ++c) {
     StreamArgs ac = a;
@@ -412,6 +458,14 @@ int launch_merge(const relay_dims* d, const Plan& p, bool with_sys, bool with_ct
     m.ctx_rows = 16 * p.rtc;
     m.ctx_slots = p.ctx_slots;
   }
+  // the kernel reads both descriptor arrays unconditionally: unused ones point at the
+  // row descriptors (always part of the workspace)
+  m.ctx_rowdesc = reinterpret_cast<const int*>(ws + p.off_rowdesc);
+  if (m.sys_src != 1) m.sys_desc = m.ctx_rowdesc;
+  m.row_o = reinterpret_cast<const float*>(ws + p.off_row_o);
+  m.row_lse = reinterpret_cast<const float*>(ws + p.off_row_lse);
+  m.ks = p.ks;
+  m.kc = p.kc;
   m.out = out;
   m.lse_out = lse_out;
   m.out_bf16 = out_bf16;
@@ -534,6 +588,8 @@ int relay_get_plan(const relay_dims* dims, int32_t sys_len, relay_plan* out) {
   out->merge_wgs = p.merge_wgs;
   out->launches = p.launches;
   out->sys_rows_per_wg = p.sys_mode == 2 || p.sys_mode == 4 ? (p.sys_pp ? relay::kSysPPRows : relay::kSysMfmaRows) : 0;
+  out->sys_row_slots = p.ks;
+  out->ctx_row_slots = p.kc;
   return RELAY_OK;
 }
 

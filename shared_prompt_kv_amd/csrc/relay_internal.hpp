@@ -101,7 +101,7 @@ struct StreamArgs {
   int sys_len;
   int sys_steps;       // ceil(L_s / 32)
   int M;               // stacked rows per KV head (T_q * g)
-  float* sys_o;        // [H_kv + workgroups slots][16 RTS rows][d]
+  float* sys_o;        // [H_kv ks + H_kv + workgroups slots][16 RTS rows][d]
   float* sys_lse;      // [slots][16 RTS]
   int* sys_desc;       // [H_kv][2]: first slot, number of pieces
   // context streams (request, KV head, row block) of requests [b_begin, b_begin + n_req)
@@ -122,6 +122,13 @@ struct StreamArgs {
   float* ctx_o;        // [slots][16 RTC][d]
   float* ctx_lse;      // [slots][16 RTC]
   int* ctx_rowdesc;    // [T_q * H_q][4]: first slot, number of pieces, row in the piece
+  // pieces at places fixed in advance, where the merge finds them without looking up
+  // where they are: piece k < ks of KV head h's system stream in system slot h ks + k
+  // (later ones in slot H_kv ks + h + w), piece j < kc of a context stream in slot j of
+  // each of its rows, row_o[(r kc + j) d] (later ones in the stream slots above)
+  float* row_o;
+  float* row_lse;      // [T_q * H_q][kc]
+  int ks, kc;
   int n_workers;       // waves of the launch (grid * kStreamWaves)
 };
 
@@ -168,11 +175,20 @@ struct MergeArgs {
   const int* ctx_rowdesc;
   int ctx_rows;        // rows per context slot (16 RTC)
   long long ctx_slots; // context slots (clamp)
+  // pieces at fixed places (StreamArgs::row_o): the first ks system pieces of every KV
+  // head, the first kc context pieces of every row
+  const float* row_o;
+  const float* row_lse;
+  int ks, kc;
   void* out;
   float* lse_out;      // may be NULL
   int out_bf16;
 };
 hipError_t launch_relay_merge(const MergeArgs& a, int head_dim, hipStream_t stream, const LaunchTiming* tm = nullptr);
+// Most pieces at fixed places per row (system and context together), which the merge
+// reads with the descriptors; the most output rows a plan gives such places.
+constexpr int kMaxRowSlots = 16;
+constexpr long long kRowSlotRows = 4096;
 inline int merge_threads(int head_dim, long long n_rows) {
   return n_rows >= 2LL * 256 * (256 / (head_dim / 4)) ? 256 : 64;
 }

@@ -26,13 +26,16 @@
 //
 // The part of a context stream that one wave processes is a piece, and so is the part
 // of a system stream that one workgroup processes; each piece writes one partial (O
-// normalised by its own sum, and its log-sum-exp) for the stream's rows, into slot
-// (stream id + v) of the context partials (v the wave) or slot (h + w) of the system
-// partials (w the workgroup).  Pieces are ordered like their streams, so these slots
-// are distinct.  The holder of a stream's first step also writes where the stream's
-// pieces are (first slot and count), per KV head for system streams and per output row
-// for context streams; the merge (relay_fuse.hip) reads those and combines the pieces
-// of a row with the same log-sum-exp identity that relay fusion uses.
+// normalised by its own sum, and its log-sum-exp) for the stream's rows.  The first
+// pieces of a stream go to places fixed in advance: piece k < ks of KV head h's system
+// stream to system slot h ks + k, piece j < kc of a context stream to slot j of each of
+// its rows; later ones to slot (H_kv ks + h + w) of the system partials (w the
+// workgroup) or slot (stream id + v) of the context partials (v the wave).  Pieces are
+// ordered like their streams, so these slots are distinct.  The holder of a stream's
+// first step also writes where the stream's pieces are (first slot and count), per KV
+// head for system streams and per output row for context streams; the merge
+// (relay_fuse.hip) reads those together with the fixed places and combines the pieces of
+// a row with the same log-sum-exp identity that relay fusion uses.
 #include "relay_device.hpp"
 #include "relay_internal.hpp"
 #include "sys_attn_mfma.hpp"
@@ -196,8 +199,8 @@ __device__ __forceinline__ void run_steps(int nsteps, const u32x4 (&qf)[RT][Step
 // and merged through LDS (mlds: stream_merge_lds_bytes of this workgroup).  Every wave
 // of the workgroup calls it with the same arguments (it holds barriers).
 template <typename T, int D, int RTS, int OCC>
-__device__ void system_piece(const StreamArgs& a, int h, int j0, int j1, int w, int wk, long long total, int W,
-                             float* mlds) {
+__device__ void system_piece(const StreamArgs& a, int h, int j0, int j1, int w, int wk, int k, long long total,
+                             int W, float* mlds) {
   constexpr int E = Elem<T>::kBytes;
   const int lane = lane_id(), r16 = lane & 15;
   u32x4 qf[RTS][StepK<T, D>::NCH];
@@ -240,14 +243,17 @@ __device__ void system_piece(const StreamArgs& a, int h, int j0, int j1, int w, 
     merge_key_lanes<D, 1, strm::kWaves>(*reinterpret_cast<RowState<D>(*)[1]>(&rs[rt]), wk, mlds);
   if (wk != 0) return;
 
-  const int slot = h + w;
+  // piece k of the stream (k = w - the first piece's workgroup): fixed slot h ks + k while
+  // k < ks, else slot H_kv ks + h + w
+  const int slot = a.num_kv_heads * a.ks + h + w;
+  const size_t base = k < a.ks ? (size_t)h * a.ks + k : (size_t)slot;
 #pragma unroll
   for (int rt = 0; rt < RTS; ++rt) {
     const int m = rt * 16 + r16;
     float* orow = nullptr;
     float* lrow = nullptr;
     if (m < a.M) {
-      const size_t r = (size_t)slot * (16 * RTS) + m;
+      const size_t r = base * (16 * RTS) + m;
       orow = a.sys_o + r * D;
       lrow = a.sys_lse + r;
     }
@@ -320,7 +326,9 @@ struct CtxPiece {
   int i, h, rb, j0, c, qs, nq;
 };
 
-template <typename T, int D, int RTC, int OCC>
+// OWN: the launch may place context pieces in the rows' own slots (a.kc > 0); the
+// launch beside the matrix-core system workgroups never does.
+template <typename T, int D, int RTC, int OCC, bool OWN>
 __device__ void context_range(const StreamArgs& a, const ReqTables& t, long long y0, long long y1, long long Ts,
                               int v, long long total, int W) {
   constexpr int E = Elem<T>::kBytes;
@@ -330,6 +338,10 @@ __device__ void context_range(const StreamArgs& a, const ReqTables& t, long long
   const size_t page_stride = (size_t)a.num_kv_heads * kTile * D * E;
 
   CtxWin wc = ctx_window<RTC>(a, t, y0, y1);
+  // only the wave's first piece can start inside its stream: its index among the
+  // stream's pieces (that stream's first step is launch step Ts + y0 - j, j the stream
+  // step at y0)
+  const int j_first = OWN ? v - part_of64(Ts + y0 - __builtin_amdgcn_readfirstlane(wc.j), total, W) : 0;
   CtxWin wn = (y0 + strm::kWin < y1) ? ctx_window<RTC>(a, t, y0 + strm::kWin, y1) : wc;
 
   auto issue = [&](CtxSlot<T, D, RTC>& s, long long y) {
@@ -359,7 +371,9 @@ __device__ void context_range(const StreamArgs& a, const ReqTables& t, long long
   int last[RTC];
   CtxPiece cur{-1, 0, 0, 0, 0, 0, 0};
 
-  // the finished piece's partial (and, for a stream's first piece, where its pieces are)
+  // the finished piece's partial (and, for a stream's first piece, where its pieces are):
+  // piece j of the stream goes to slot j of each of its rows while j < kc, else to stream
+  // slot s_id + v
   auto finish = [&]() {
     const int i = cur.i;
     const long long s_id = ((long long)i * a.num_kv_heads + cur.h) * a.ctx_rb + cur.rb;
@@ -368,6 +382,7 @@ __device__ void context_range(const StreamArgs& a, const ReqTables& t, long long
     const int rbs = request_row_blocks(a, cur.nq, RPB);
     const long long p0 = Ts + t.pre[i] + (long long)(cur.h * rbs + cur.rb) * steps;
     const int pieces = part_of64(p0 + steps - 1, total, W) - v + 1;
+    const int j = cur.j0 > 0 ? j_first : 0;
 #pragma unroll
     for (int rt = 0; rt < RTC; ++rt) {
       const int rr = rt * 16 + r16;
@@ -376,9 +391,12 @@ __device__ void context_range(const StreamArgs& a, const ReqTables& t, long long
       float* orow = nullptr;
       float* lrow = nullptr;
       if (ok) {
-        const size_t r = (size_t)slot * RPB + rr;
-        orow = a.ctx_o + r * D;
-        lrow = a.ctx_lse + r;
+        const bool own = OWN && j < a.kc;
+        const int tl0 = rl / a.group, gi0 = rl - tl0 * a.group;
+        const size_t oi0 = (size_t)(cur.qs + tl0) * a.num_q_heads + (size_t)cur.h * a.group + gi0;
+        const size_t r = own ? oi0 * a.kc + j : (size_t)slot * RPB + rr;
+        orow = (own ? a.row_o : a.ctx_o) + r * D;
+        lrow = (own ? a.row_lse : a.ctx_lse) + r;
       }
       store_row_tile(rs[rt], orow, lrow);
       if (ok && cur.j0 == 0 && q4 == 0) {
@@ -461,7 +479,7 @@ __host__ __device__ constexpr size_t stream_tables_bytes(int n) {
 }
 
 // Streaming workgroup w of the launch's streaming workgroups (lds_tab: its LDS).
-template <typename T, int D, int RTS, int RTC>
+template <typename T, int D, int RTS, int RTC, bool OWN>
 __device__ __forceinline__ void stream_workgroup(const StreamArgs& a, int w, int* lds_tab) {
   constexpr int OCC = stream_occ<T, D, RTS, RTC>();
   const int n = a.ctx_on ? a.n_req : 0;
@@ -491,7 +509,9 @@ __device__ __forceinline__ void stream_workgroup(const StreamArgs& a, int w, int
       const int h = (int)(x / a.sys_steps);
       const int j0 = (int)(x - (long long)h * a.sys_steps);
       const int j1 = (int)((long long)j0 + (xs1 - x) < a.sys_steps ? j0 + (xs1 - x) : a.sys_steps);
-      system_piece<T, D, RTS, OCC>(a, h, j0, j1, w, wk, total, W, mlds);
+      // only the workgroup's first piece can start inside a stream (k > 0)
+      const int k = j0 > 0 ? w - part_of64((long long)h * a.sys_steps, total, W) / strm::kWaves : 0;
+      system_piece<T, D, RTS, OCC>(a, h, j0, j1, w, wk, k, total, W, mlds);
       x += j1 - j0;
     }
   }
@@ -499,7 +519,7 @@ __device__ __forceinline__ void stream_workgroup(const StreamArgs& a, int w, int
   const long long x0 = (long long)v * total / W, x1 = (long long)(v + 1) * total / W;
   if (a.ctx_on && x1 > Ts) {
     const long long y0 = (x0 > Ts ? x0 : Ts) - Ts, y1 = x1 - Ts;
-    context_range<T, D, RTC, OCC>(a, t, y0, y1, Ts, v, total, W);
+    context_range<T, D, RTC, OCC, OWN>(a, t, y0, y1, Ts, v, total, W);
   }
 }
 
@@ -507,7 +527,7 @@ template <typename T, int D, int RTS, int RTC>
 __global__ __launch_bounds__(kWave* strm::kWaves, (stream_occ<T, D, RTS, RTC>())) void stream_attn_kernel(
     StreamArgs a) {
   extern __shared__ int lds_tab[];
-  stream_workgroup<T, D, RTS, RTC>(a, blockIdx.x, lds_tab);
+  stream_workgroup<T, D, RTS, RTC, true>(a, blockIdx.x, lds_tab);
 }
 
 // The decode step with more than 64 stacked rows per KV head (bf16, head_dim 128): the
@@ -520,7 +540,7 @@ __global__ __launch_bounds__(kWave* strm::kWaves, 2) void stream_sys_kernel(CoAr
   if ((int)blockIdx.x < a.n_sys)
     sys_mfma_workgroup<false>(a.sys, blockIdx.x, a.n_sys, reinterpret_cast<char*>(lds_tab));
   else
-    stream_workgroup<bf16_t, 128, 0, RTC>(a.str, blockIdx.x - a.n_sys, lds_tab);
+    stream_workgroup<bf16_t, 128, 0, RTC, false>(a.str, blockIdx.x - a.n_sys, lds_tab);
 }
 
 hipError_t launch_stream_sys(const CoArgs& a, int rtc, int grid, hipStream_t s, const LaunchTiming* tm) {

@@ -44,7 +44,8 @@ class relay_dims(ctypes.Structure):
 class relay_plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "sys_mode", "sys_row_tiles", "sys_runs", "sys_wgs", "ctx_row_tiles", "ctx_row_blocks",
-        "stream_waves", "stream_launches", "stream_max_requests", "merge_wgs", "launches", "sys_rows_per_wg")]
+        "stream_waves", "stream_launches", "stream_max_requests", "merge_wgs", "launches", "sys_rows_per_wg",
+        "sys_row_slots", "ctx_row_slots")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -56,7 +56,7 @@ def test_library_is_gfx950_only(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert R.relay_abi_version() == 5
+    assert R.relay_abi_version() == 6
     assert lib.relay_strerror(0) == b"ok"
     assert lib.relay_strerror(-3) == b"workspace too small"
 
@@ -141,10 +141,40 @@ def a256(x):
     return -(-x // 256) * 256
 
 
+def row_slots(d, sys_len, sys_mode, waves, ctx=True):
+    """The rows' own piece slots the plan reserves (the header's relay_plan contract):
+    context, the most waves the longest stream (S 32-key steps) falls into when each wave
+    holds at least (system steps + one per stream) // waves steps, at most min(4, S);
+    system streams, the most workgroups of four waves one KV head's steps fall into when
+    the launch holds the system steps plus, per context stream, half the longest
+    context's steps (all W waves share the steps equally), plus one when the launch also
+    holds context streams; capped so that both fit 16.  None with the system kernel's runs
+    or more than 4096 output rows."""
+    if sys_mode > 1 or d.total_q * d.num_q_heads > 4096:
+        return 0, 0
+    cap = min(d.max_ctx_len, d.max_blocks_per_seq * 16)
+    max_steps = max(1, -(-cap // 32))
+    ss = -(-sys_len // 32) if sys_mode == 1 else 0
+    Ts = d.num_kv_heads * ss
+    kc = 0
+    if ctx:
+        per_wave = max(1, (Ts + d.batch * d.num_kv_heads) // waves)
+        kc = min(4, max_steps, -(-(max_steps - 1) // per_wave) + 1)
+    ks = 0
+    if sys_mode == 1:
+        T = Ts + (d.batch * d.num_kv_heads * ((max_steps + 1) // 2) if ctx else 0)
+        W = min(T, waves)
+        part = lambda x: ((x + 1) * W + T - 1) // T - 1
+        most = max(part(h * ss + ss - 1) // 4 - part(h * ss) // 4 + 1 for h in range(d.num_kv_heads))
+        ks = min(most + (1 if ctx else 0), 16 - kc)
+    return ks, kc
+
+
 def test_workspace_covers_the_plan(lib):
     """Workspace = the partial regions of the streaming launch, laid out as the header says:
-    system pieces (H_kv + workgroups slots of 16 * sys_row_tiles rows), their descriptors,
-    context pieces (B H_kv row_blocks + waves slots per request group) and row descriptors."""
+    system pieces (H_kv (sys_row_slots + 1) + workgroups slots of 16 * sys_row_tiles rows),
+    their descriptors, context pieces (B H_kv row_blocks + waves slots per request group),
+    row descriptors and every row's ctx_row_slots own slots."""
     d = base_dims()               # B 4, H_q 8 / H_kv 2 -> M = 16 stacked rows per KV head
     plan = R.relay_get_plan(d, 1000)
     assert plan["sys_mode"] == 1 and plan["sys_row_tiles"] == 1
@@ -152,14 +182,19 @@ def test_workspace_covers_the_plan(lib):
     grid = stream_grid(True, 128, 1, 1)
     assert plan["stream_waves"] == 4 * grid and plan["stream_launches"] == 1 and plan["launches"] == 2
     rows, D, H = 4 * 8, 128, 2
-    sys_slots, ctx_slots = H + grid, 4 * H * 1 + 4 * grid
+    ks, kc = row_slots(d, 1000, 1, 4 * grid)
+    assert (plan["sys_row_slots"], plan["ctx_row_slots"]) == (ks, kc) and ks >= 1 and kc == 4
+    sys_slots, ctx_slots = H * (ks + 1) + grid, 4 * H * 1 + 4 * grid
     expect = (a256(sys_slots * 16 * D * 4) + a256(sys_slots * 16 * 4) + a256(H * 2 * 4)
-              + a256(ctx_slots * 16 * D * 4) + a256(ctx_slots * 16 * 4) + a256(rows * 16))
+              + a256(ctx_slots * 16 * D * 4) + a256(ctx_slots * 16 * 4) + a256(rows * 16)
+              + a256(rows * kc * D * 4) + a256(rows * kc * 4))
     assert R.relay_workspace_size(d, 1000) == expect
     p0 = R.relay_get_plan(d, 0)
     assert p0["sys_mode"] == 0 and p0["launches"] == 2
+    assert (p0["sys_row_slots"], p0["ctx_row_slots"]) == (0, 4)
     ctx0 = 4 * H + 4 * stream_grid(True, 128, 0, 1)
-    assert R.relay_workspace_size(d, 0) == (a256(ctx0 * 16 * D * 4) + a256(ctx0 * 16 * 4) + a256(rows * 16))
+    assert R.relay_workspace_size(d, 0) == (a256(ctx0 * 16 * D * 4) + a256(ctx0 * 16 * 4) + a256(rows * 16)
+                                            + a256(rows * 4 * D * 4) + a256(rows * 4 * 4))
 
 
 @pytest.mark.parametrize("cfg,sweep", [(1, 0), (2, 0), (3, 0), (3, 5), (4, 0), (5, 0)])
@@ -203,6 +238,8 @@ def test_plan_for_each_config(lib, cfg, sweep):
                                                          plan["ctx_row_tiles"])
     assert plan["stream_waves"] == 4 * grid and plan["stream_launches"] == 1
     assert plan["stream_max_requests"] == spec.batch
+    assert (plan["sys_row_slots"], plan["ctx_row_slots"]) == row_slots(d, spec.sys_len, plan["sys_mode"],
+                                                                       plan["stream_waves"])
 
 
 def test_requests_in_groups_of_one_streaming_launch(lib):

@@ -440,6 +440,65 @@ def test_many_requests_in_several_streaming_launches():
     check(out.cpu().numpy(), ref, spec.dtype, "out")
 
 
+# ------------------------------------------------------------------------------------------
+# pieces past the places fixed in advance: the plan sizes the fixed places from an
+# estimate (the context lengths are device data); pieces past them take the stream slots
+
+def _piece_counts(w, plan):
+    """Most pieces of one KV head's system stream and of one context stream, from the
+    equal split of the launch's 32-key steps over its waves (the partition the header
+    documents for relay_plan.stream_waves), for one query token per request."""
+    spec = w.spec
+    H, ss = spec.num_kv_heads, -(-spec.sys_len // 32)
+    steps = [max(1, -(-int(c) // 32)) for c in w.ctx_lens]
+    T = H * ss + H * sum(steps)
+    Wv = min(T, plan["stream_waves"])
+    part = lambda x: ((x + 1) * Wv + T - 1) // T - 1
+    n_sys = max(part(h * ss + ss - 1) // 4 - part(h * ss) // 4 + 1 for h in range(H)) if ss else 0
+    n_ctx, p0 = 0, H * ss
+    for s in steps:
+        for _ in range(H):
+            n_ctx = max(n_ctx, part(p0 + s - 1) - part(p0) + 1)
+            p0 += s
+    return n_sys, n_ctx
+
+
+OVERFLOW = [
+    # contexts far shorter than the declared longest one: the step estimate is too high,
+    # so system streams fall into more workgroups than their fixed slots
+    ("sys", W.config_spec(2).replace(name="c2-short-ctx", batch=24, sys_len=3000, ctx_lo=8, ctx_hi=40), 4096),
+    ("sys", W.config_spec(1).replace(name="c1-short-ctx", batch=16, num_q_heads=4, num_kv_heads=4,
+                                      sys_len=900, ctx_lo=1, ctx_hi=20), 8192),
+    # one long context over many waves: more context pieces than the row's own slots
+    ("ctx", W.config_spec(2).replace(name="c2-long-ctx", batch=2, num_q_heads=4, num_kv_heads=4,
+                                      sys_len=64, ctx_lo=2500, ctx_hi=3000), None),
+]
+
+
+@pytest.mark.parametrize("kind,spec,declared", OVERFLOW, ids=[s.name for _, s, _ in OVERFLOW])
+def test_pieces_past_the_fixed_places(kind, spec, declared):
+    say(f"[parity] pieces past the fixed places ({kind}) {spec} declared max_ctx_len {declared}")
+    w = workload(spec)
+    t = upload(w)
+    if declared:
+        # a larger declared bound, with block tables wide enough for it (padding entries
+        # are never read)
+        cols = -(-declared // 16)
+        bt = t["block_tables"]
+        t = dict(t, max_ctx_len=declared,
+                 block_tables=torch.nn.functional.pad(bt, (0, cols - bt.shape[1])).contiguous())
+    plan = R.relay_get_plan(R.dims_of(t), t["sys_len"])
+    n_sys, n_ctx = _piece_counts(w, plan)
+    if kind == "sys":
+        assert plan["sys_mode"] == 1 and n_sys > plan["sys_row_slots"] >= 1, (plan, n_sys)
+    else:
+        assert n_ctx > plan["ctx_row_slots"] >= 1, (plan, n_ctx)
+    out = R.decode_workload(t)
+    torch.cuda.synchronize()
+    ref, _ = oracle.Problem(w).attention()
+    check(out.cpu().numpy(), ref, spec.dtype, f"pieces past the fixed places ({kind})")
+
+
 def test_garbage_workspace():
     """Whatever the workspace held (here random bytes), a call gives the same bits."""
     spec = SCHED_SPECS[0]
