@@ -6,15 +6,16 @@
 // fused elementwise kernel in the linnk.ai summary, section "Abstract").  With
 // LSE_i = ln sum_{j in part i} e^{s_j}, the weights e^{LSE_i} / sum_k e^{LSE_k} are
 // non-negative, sum to one, and make the result equal attention over the union of
-// the parts.  The same identity merges any number of parts, so the per-chunk
-// partials of sys_attn and the per-split partials of ctx_attn are merged here in one
+// the parts.  The same identity merges any number of parts, so the pieces of the
+// system and context streams (or the system kernel's runs) are merged here in one
 // pass: one read of every partial row, one write of the output.
 //
 // Layout: D/4 lanes per row, each owning four consecutive dimensions (one 16-byte
 // load per partial); one wave per workgroup when there are few rows, so a few hundred
-// rows still spread over the CUs, four when there are many.  HBM-bound.  One pass: the LSEs and outputs of a batch of partials are
-// loaded together (one memory latency per batch) and folded into a running
-// (max, weight sum, weighted sum) that is rescaled when the max grows.
+// rows still spread over the CUs, four when there are many.  One pass: the LSEs and
+// outputs of a batch of partials are loaded together (one memory latency per batch)
+// and folded into a running (max, weight sum, weighted sum) that is rescaled when the
+// max grows.  Few rows: bound by memory latency; many: by HBM bandwidth.
 #include "relay_device.hpp"
 #include "relay_internal.hpp"
 
